@@ -1,0 +1,260 @@
+"""Plain CPU oracle for paged decode attention (fp64, NumPy).
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module. The HIP
+product path never imports it, and this module imports nothing from the
+product package: the two share no code.
+
+Sources (page titles as they appear on the pages):
+  * "DCU page832 attention" (luanjiahao.me, 2026-07-17):
+      §1  a token's logical page is ``token // BLOCK_SIZE``, its page offset is
+          ``token % BLOCK_SIZE``, and the block table maps the logical page to a
+          physical page; K/V stride, KV head and head dim complete the address.
+      §4  the cache shape ``[num_physical_pages, BLOCK_SIZE, Hkv, D]`` per
+          component (``unbind(1)`` of ``[num_physical_pages, 2, ...]``).
+      §5  per key tile: gather K/V through the table, ``score = dot(Q, K) * scale``,
+          then an online-softmax update with V; the causal range is kept.
+      §7  q=1 decode reads every logical page of the sequence and skips none.
+  * "vLLM 下双卡 Radeon 上的混合 SSM 解码速率" (cadamcat.github.io), the
+    paragraph on the upstream split-KV patch: the KV range of one
+    (sequence, KV head) is cut among several workgroups and the pieces are
+    reduced afterwards.
+  * "Qwen3.8 auf MI350P betreiben", Lektion 3: several verify rows share one
+    K/V walk, each row keeps its own causal mask, and partial softmax
+    statistics are merged.
+
+What is computed (the plain definition; split-KV is an exact re-association of
+it, so the oracle evaluates the definition directly):
+    for sequence b, query row i, query head h:
+        g   = h // G                        (G = Hq / Hkv, consecutive groups)
+        pos = L_b - q_len + i               (bottom-right causal alignment)
+        s_j = sigma * sum_d q[b,i,h,d] * K_j[d]     for j in [0, pos]
+        out = sum_j exp(s_j - max s) V_j / sum_j exp(s_j - max s)
+with K_j, V_j read through the block table, bf16 widened exactly to fp64, and
+sigma = float64(float32(scale)), the value the kernel receives.
+
+Readings where the pages are silent (each also listed in the design notes):
+GQA head h uses KV head h // G; a sequence with L = 0 yields zeros; the
+multi-row causal window is bottom-right aligned (row i sees j <= L - q_len + i).
+
+Parity pins: every function here is checked by ``tests/test_oracle_pins.py``
+against brute force, closed forms, invariants, a library routine, and the
+worked integers the pages print.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits_to_f64", "page_of", "token_offsets_ref", "gather_token_rows",
+    "paged_attention_ref", "partial_stats_ref", "merge_partials_ref",
+    "split_attention_ref", "split_plan_ref", "split_ranges_ref", "kv_bytes_ref",
+]
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (uint16) to float64."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Address translation ("DCU page832 attention", §1 and §5).
+# ---------------------------------------------------------------------------
+
+def page_of(token: int, block_size: int) -> tuple[int, int]:
+    """(logical page, offset in page) of a logical token index."""
+    return token // block_size, token % block_size
+
+
+def token_offsets_ref(block_table, seq_lens, block_size: int, stride_page: int,
+                      stride_tok: int, stride_head: int, kv_head: int) -> list:
+    """Element offset of every live token's row start, per sequence.
+
+    offset(b, j) = block_table[b, j // B] * stride_page + (j % B) * stride_tok
+                   + kv_head * stride_head          (Python integers, no overflow)
+    """
+    out = []
+    for b, L in enumerate(np.asarray(seq_lens).tolist()):
+        row = []
+        for j in range(int(L)):
+            p, o = page_of(j, block_size)
+            phys = int(block_table[b][p])
+            row.append(phys * stride_page + o * stride_tok + kv_head * stride_head)
+        out.append(np.asarray(row, dtype=np.int64))
+    return out
+
+
+def gather_token_rows(cache, table_row, n_tokens: int, block_size: int, kv_head: int) -> np.ndarray:
+    """Rows cache[block_table[j // B], j % B, kv_head, :] for j < n_tokens, as fp64."""
+    j = np.arange(n_tokens, dtype=np.int64)
+    logical_page = j // block_size
+    page_offset = j % block_size
+    physical_page = np.asarray(table_row, dtype=np.int64)[logical_page]
+    return bf16_bits_to_f64(np.asarray(cache)[physical_page, page_offset, kv_head, :])
+
+
+# ---------------------------------------------------------------------------
+# Attention by definition.
+# ---------------------------------------------------------------------------
+
+def _softmax_weighted_sum(scores: np.ndarray, values: np.ndarray) -> np.ndarray:
+    """sum_j exp(s_j - max s) v_j / sum_j exp(s_j - max s) for one row of scores."""
+    if scores.size == 0:
+        return np.zeros(values.shape[1], dtype=np.float64)
+    e = np.exp(scores - scores.max())
+    return (e @ values) / e.sum()
+
+
+def paged_attention_ref(q, k_cache, v_cache, block_table, seq_lens, block_size: int,
+                        scale: float) -> np.ndarray:
+    """fp64 paged attention for all sequences, query rows and query heads.
+
+    q: uint16 bf16 bits [num_seqs, q_len, Hq, D]; k_cache / v_cache: uint16
+    [num_pages, B, Hkv, D] (any strides); block_table: int [num_seqs, max_pages];
+    seq_lens: [num_seqs]. Returns float64 [num_seqs, q_len, Hq, D].
+    """
+    q = np.asarray(q)
+    ns, q_len, hq, d = q.shape
+    hkv = np.asarray(k_cache).shape[2]
+    assert hq % hkv == 0
+    G = hq // hkv
+    sigma = float(np.float32(scale))
+    out = np.zeros((ns, q_len, hq, d), dtype=np.float64)
+    for b in range(ns):
+        L = int(seq_lens[b])
+        if L == 0:
+            continue
+        assert L >= q_len, "a sequence must hold at least its q_len new tokens"
+        for g in range(hkv):
+            K = gather_token_rows(k_cache, block_table[b], L, block_size, g)
+            V = gather_token_rows(v_cache, block_table[b], L, block_size, g)
+            for i in range(q_len):
+                pos = L - q_len + i                   # last visible token of row i
+                for h in range(g * G, (g + 1) * G):
+                    qv = bf16_bits_to_f64(q[b, i, h])
+                    s = sigma * (K[: pos + 1] @ qv)
+                    out[b, i, h] = _softmax_weighted_sum(s, V[: pos + 1])
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Split mode: partial softmax statistics and their merge (split-KV paragraph of
+# the dual-Radeon page; Lektion 3 of the MI350P page).
+# ---------------------------------------------------------------------------
+
+def partial_stats_ref(scores: np.ndarray, values: np.ndarray):
+    """(m, Z, A) of one split: m = max s, Z = sum exp(s - m), A = sum exp(s - m) v.
+
+    An empty split returns (-inf, 0, 0).
+    """
+    if scores.size == 0:
+        return -math.inf, 0.0, np.zeros(values.shape[1], dtype=np.float64)
+    m = float(scores.max())
+    e = np.exp(scores - m)
+    return m, float(e.sum()), e @ values
+
+
+def merge_partials_ref(parts) -> np.ndarray:
+    """Merge [(m_s, Z_s, A_s)]: M = max over non-empty splits,
+    out = sum e^(m_s - M) A_s / sum e^(m_s - M) Z_s. All-empty gives zeros."""
+    live = [(m, z, a) for (m, z, a) in parts if z > 0.0]
+    if not live:
+        return np.zeros_like(parts[0][2])
+    M = max(m for m, _, _ in live)
+    num = sum(math.exp(m - M) * a for m, _, a in live)
+    den = sum(math.exp(m - M) * z for m, z, _ in live)
+    return num / den
+
+
+def split_attention_ref(q, k_cache, v_cache, block_table, seq_lens, block_size: int,
+                        scale: float, ranges) -> np.ndarray:
+    """Same result as paged_attention_ref, evaluated split by split and merged.
+
+    ranges[b] is a list of [begin, end) token ranges that partition [0, L_b).
+    """
+    q = np.asarray(q)
+    ns, q_len, hq, d = q.shape
+    hkv = np.asarray(k_cache).shape[2]
+    G = hq // hkv
+    sigma = float(np.float32(scale))
+    out = np.zeros((ns, q_len, hq, d), dtype=np.float64)
+    for b in range(ns):
+        L = int(seq_lens[b])
+        if L == 0:
+            continue
+        for g in range(hkv):
+            K = gather_token_rows(k_cache, block_table[b], L, block_size, g)
+            V = gather_token_rows(v_cache, block_table[b], L, block_size, g)
+            for i in range(q_len):
+                pos = L - q_len + i
+                for h in range(g * G, (g + 1) * G):
+                    qv = bf16_bits_to_f64(q[b, i, h])
+                    parts = []
+                    for (lo, hi) in ranges[b]:
+                        hi_vis = min(hi, pos + 1)
+                        if hi_vis <= lo:
+                            parts.append(partial_stats_ref(np.zeros(0), V[:0]))
+                            continue
+                        s = sigma * (K[lo:hi_vis] @ qv)
+                        parts.append(partial_stats_ref(s, V[lo:hi_vis]))
+                    out[b, i, h] = merge_partials_ref(parts)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Split plan. The pages do not give the upstream split heuristic; this is the
+# plan this library defines, restated here in plain integers so the library's
+# planner can be checked against it exactly.
+#
+#   T          tile of logical tokens; split boundaries are multiples of T
+#   n_tiles    = ceil(max_seq_len / T)
+#   work       = total_tokens if given, else num_seqs * max_seq_len
+#   c (tiles)  = ceil(Hkv * work / (cu_count * wg_per_cu * T)), at least min_tiles,
+#                at most n_tiles, and at most floor((tbl_cap - 2) * B / T) (>= 1)
+#                so a split's block-table entries fit the kernel's table cache;
+#                a forced split count S_f instead gives c = ceil(n_tiles / S_f)
+#                (then the same two upper bounds)
+#   S          = ceil(n_tiles / c);   chunk = c * T tokens
+#   sequence b uses S_b = ceil(L_b / chunk) splits; split s covers
+#   [s * chunk, min((s + 1) * chunk, L_b)).
+# ---------------------------------------------------------------------------
+
+def _cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def split_plan_ref(num_seqs: int, num_kv_heads: int, max_seq_len: int, block_size: int,
+                   cu_count: int, *, total_tokens: int = 0, forced_splits: int = 0,
+                   tile: int = 64, wg_per_cu: int = 1, min_tiles: int = 2,
+                   tbl_cap: int = 2048) -> tuple[int, int]:
+    """Return (S, chunk_tokens)."""
+    n_tiles = max(1, _cdiv(max_seq_len, tile))
+    cap = max(1, ((tbl_cap - 2) * block_size) // tile)
+    if forced_splits > 0:
+        c = _cdiv(n_tiles, forced_splits)
+    else:
+        work = total_tokens if total_tokens > 0 else num_seqs * max_seq_len
+        target = max(1, cu_count * wg_per_cu)
+        c = max(min_tiles, _cdiv(num_kv_heads * work, target * tile))
+    c = max(1, min(c, n_tiles, cap))
+    return _cdiv(n_tiles, c), c * tile
+
+
+def split_ranges_ref(seq_lens, num_splits: int, chunk: int) -> np.ndarray:
+    """[num_seqs, num_splits, 2] array of [begin, end); unused splits are [L, L)."""
+    seq_lens = [int(x) for x in np.asarray(seq_lens).tolist()]
+    r = np.zeros((len(seq_lens), num_splits, 2), dtype=np.int32)
+    for b, L in enumerate(seq_lens):
+        for s in range(num_splits):
+            lo = min(s * chunk, L)
+            hi = min((s + 1) * chunk, L)
+            r[b, s] = (lo, hi)
+    return r
+
+
+def kv_bytes_ref(seq_lens, num_kv_heads: int, head_dim: int, elem_bytes: int = 2) -> int:
+    """K and V bytes one call must read: every live (token, KV head) row once, K and V."""
+    return 2 * sum(int(x) for x in np.asarray(seq_lens).tolist()) * num_kv_heads * head_dim * elem_bytes

@@ -1,0 +1,230 @@
+"""Seeded synthetic inputs for paged decode attention.
+
+This module only *builds inputs*: random numbers, bf16 rounding of those
+numbers, page pools and block tables. It holds none of the attention
+arithmetic, and both the HIP path and the CPU oracle consume what it returns.
+
+Shapes follow the full-attention layers described in "DCU page832 attention"
+(luanjiahao.me), §4 (24 query heads, 4 KV heads, head size 256, BF16, cache
+``[num_physical_pages, BLOCK_SIZE, 4, 256]`` per component, or the combined
+``[num_physical_pages, 2, BLOCK_SIZE, 4, 256]``), with page sizes 784 and 832
+from §1-§2 of the same page and 16 as the common default.
+
+Random-number recipe (the pages only say "from a seed"):
+  * ``numpy.random.SeedSequence(seed).spawn(6)`` gives six independent PCG64
+    streams, used in the fixed order ``[q, k, v, mask, pages, lengths]``.
+  * Normal draws are float32 ``standard_normal`` values rounded to bf16 by
+    round-to-nearest-even on the bit pattern.
+  * Logical K/V are drawn per sequence in token order ``[L, Hkv, D]`` *before*
+    paging, so the same seed gives the same logical K/V for every page size.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Sequence
+
+import numpy as np
+
+BF16_NAN = np.uint16(0x7FC0)
+STREAMS = ("q", "k", "v", "mask", "pages", "lengths")
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest-even) and return the 16-bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = u + 0x7FFF + ((u >> 16) & 1)
+    return (u >> 16).astype(np.uint16)
+
+
+def streams(seed: int) -> dict:
+    children = np.random.SeedSequence(seed).spawn(len(STREAMS))
+    return {name: np.random.Generator(np.random.PCG64(c)) for name, c in zip(STREAMS, children)}
+
+
+def normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
+    return f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+
+
+def log_uniform_lengths(seed: int, n: int, lo: int, hi: int) -> np.ndarray:
+    """Context lengths drawn log-uniform in [lo, hi] from the ``lengths`` stream."""
+    rng = streams(seed)["lengths"]
+    u = rng.uniform(math.log(lo), math.log(hi), size=n)
+    return np.clip(np.rint(np.exp(u)), lo, hi).astype(np.int32)
+
+
+@dataclasses.dataclass
+class DecodeCase:
+    q: np.ndarray            # uint16 bf16 bits, [num_seqs, q_len, Hq, D]
+    k_cache: np.ndarray      # uint16 bf16 bits, [num_pages, B, Hkv, D] (may be a strided view)
+    v_cache: np.ndarray      # same layout as k_cache
+    block_table: np.ndarray  # int32 [num_seqs, max_pages]; entries past a sequence's pages are -1
+    seq_lens: np.ndarray     # int32 [num_seqs]
+    block_size: int
+    scale: float             # exactly representable in float32
+    logical_k: list          # per sequence: uint16 [L, Hkv, D] in token order (test convenience)
+    logical_v: list
+    kv_pool: np.ndarray | None = None   # combined [num_pages, 2, B, Hkv, D] when requested
+    meta: dict = dataclasses.field(default_factory=dict)
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def q_len(self) -> int:
+        return int(self.q.shape[1])
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k_cache.shape[0])
+
+    @property
+    def max_seq_len(self) -> int:
+        return int(self.seq_lens.max()) if self.seq_lens.size else 0
+
+
+def _deal_pages(perm: np.ndarray, n_pages: Sequence[int], interleave: bool) -> list:
+    """Split a permutation of physical page ids into per-sequence page lists."""
+    out = [[] for _ in n_pages]
+    if not interleave:
+        pos = 0
+        for b, n in enumerate(n_pages):
+            out[b] = list(perm[pos:pos + n])
+            pos += n
+        return out
+    pos = 0
+    for r in range(max(n_pages, default=0)):
+        for b, n in enumerate(n_pages):
+            if r < n:
+                out[b].append(perm[pos])
+                pos += 1
+    return out
+
+
+def make_case(
+    seed: int,
+    seq_lens: Sequence[int],
+    *,
+    q_len: int = 1,
+    num_q_heads: int = 24,
+    num_kv_heads: int = 4,
+    head_dim: int = 256,
+    block_size: int = 16,
+    scale: float | None = None,
+    pool_factor: float = 1.25,
+    pool_pages: int | None = None,
+    boost_frac: float = 0.0,
+    boost: float = 4.0,
+    poison: bool = True,
+    combined: bool = False,
+    interleave: bool = False,
+    extra_table_cols: int = 0,
+) -> DecodeCase:
+    """Build one paged decode input.
+
+    ``boost_frac`` scales exactly ``round(boost_frac * L * Hkv)`` logical
+    (token, KV head) key rows of each sequence by ``boost`` (a power of two, so
+    exact in bf16); this gives the peaked softmax of the long-context workloads.
+    With ``poison`` every slot that no sequence owns (unused pages and the tail
+    of each last page) holds bf16 NaN, and table entries past a sequence's pages
+    are -1, so any read outside the live range shows up in the output.
+    """
+    seq_lens = [int(x) for x in seq_lens]
+    ns, hq, hkv, d, bs = len(seq_lens), num_q_heads, num_kv_heads, head_dim, block_size
+    assert hq % hkv == 0 and bs >= 1 and ns >= 1
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(d)))
+    scale = float(np.float32(scale))
+    rng = streams(seed)
+
+    q = normal_bf16(rng["q"], (ns, q_len, hq, d))
+    logical_k, logical_v = [], []
+    for L in seq_lens:
+        k = normal_bf16(rng["k"], (L, hkv, d))
+        v = normal_bf16(rng["v"], (L, hkv, d))
+        if boost_frac > 0.0 and L > 0:
+            n_boost = int(round(boost_frac * L * hkv))
+            rows = rng["mask"].choice(L * hkv, size=n_boost, replace=False)
+            kf = k.reshape(L * hkv, d)
+            vals = (kf[rows].astype(np.uint32) << 16).view(np.float32) * np.float32(boost)
+            kf[rows] = f32_to_bf16_bits(vals)
+        logical_k.append(k)
+        logical_v.append(v)
+
+    n_pages = [-(-L // bs) for L in seq_lens]
+    total = sum(n_pages)
+    if pool_pages is None:
+        pool_pages = max(1, math.ceil(pool_factor * total))
+    assert pool_pages >= total
+    perm = rng["pages"].permutation(pool_pages).astype(np.int32)
+    pages = _deal_pages(perm, n_pages, interleave)
+
+    max_pages = max(max(n_pages, default=0), 1) + extra_table_cols
+    table = np.full((ns, max_pages), -1, dtype=np.int32)
+    fill = BF16_NAN if poison else np.uint16(0)
+    pool = np.full((pool_pages, 2, bs, hkv, d), fill, dtype=np.uint16)
+    for b, L in enumerate(seq_lens):
+        table[b, : n_pages[b]] = pages[b]
+        # Fill page by page: logical page p holds tokens [p*bs, min((p+1)*bs, L)).
+        for p, phys in enumerate(pages[b]):
+            lo, hi = p * bs, min((p + 1) * bs, L)
+            pool[phys, 0, : hi - lo] = logical_k[b][lo:hi]
+            pool[phys, 1, : hi - lo] = logical_v[b][lo:hi]
+
+    if combined:
+        k_cache, v_cache, kv_pool = pool[:, 0], pool[:, 1], pool
+    else:
+        k_cache = np.ascontiguousarray(pool[:, 0])
+        v_cache = np.ascontiguousarray(pool[:, 1])
+        kv_pool = None
+        del pool
+
+    return DecodeCase(
+        q=q, k_cache=k_cache, v_cache=v_cache, block_table=table,
+        seq_lens=np.asarray(seq_lens, dtype=np.int32), block_size=bs, scale=scale,
+        logical_k=logical_k, logical_v=logical_v, kv_pool=kv_pool,
+        meta=dict(seed=seed, q_len=q_len, hq=hq, hkv=hkv, d=d, block_size=bs,
+                  pool_pages=pool_pages, boost_frac=boost_frac, poison=poison,
+                  combined=combined, interleave=interleave),
+    )
+
+
+# ---------------------------------------------------------------------------
+# Named workloads. Seeds: 1001-1004 for the four decode workloads, 1005 for the
+# multi-row verify workload, 1006 for the dense-model control.
+# ---------------------------------------------------------------------------
+
+HYBRID_CONTEXTS = (1024, 4096, 16384, 32768)
+
+
+def single_seq_b16(**kw) -> DecodeCase:
+    """Batch 1, q_len 1, 24/4/256, page 16, 512 tokens; 32 pages of a 64-page pool."""
+    return make_case(1001, [512], block_size=16, pool_pages=64, **kw)
+
+
+def hybrid_long_context(context: int, block_size: int = 784, **kw) -> DecodeCase:
+    """Batch 1, q_len 1, 24/4/256, 5% of key rows x4, pool 1.25x the pages needed."""
+    return make_case(1002, [context], block_size=block_size, boost_frac=0.05, **kw)
+
+
+def mixed_batch(**kw) -> DecodeCase:
+    """16 sequences, lengths log-uniform in [500, 32000], page 784, pages dealt round-robin."""
+    lens = log_uniform_lengths(1004, 16, 500, 32000)
+    return make_case(1004, lens, block_size=784, interleave=True, **kw)
+
+
+def spec_verify(context: int = 32768, q_len: int = 16, **kw) -> DecodeCase:
+    """Batch 1, 16 causal query rows, 24/4/256, page 784."""
+    return make_case(1005, [context], q_len=q_len, block_size=784, **kw)
+
+
+def dense_control(context: int = 32768, **kw) -> DecodeCase:
+    """Batch 1, q_len 1, 32 query heads, 8 KV heads, head_dim 128, page 16."""
+    return make_case(1006, [context], num_q_heads=32, num_kv_heads=8, head_dim=128,
+                     block_size=16, **kw)
+
+
+def kv_read_bytes(seq_lens, num_kv_heads: int, head_dim: int, elem_bytes: int = 2) -> int:
+    """Algorithmic K+V bytes one decode call must read: every live token once."""
+    return int(2 * int(np.sum(np.asarray(seq_lens, dtype=np.int64))) * num_kv_heads * head_dim * elem_bytes)
