@@ -1,0 +1,291 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+A step is one paged decode-attention call for the whole batch (split kernel +
+LSE merge) on inputs already resident in HBM. The default workload is the
+hybrid-model long-context decode: batch 1, q_len 1, 24 query / 4 KV heads,
+head_dim 256, page 784, context 32768, bf16 K/V with 5% of key rows x4.
+
+To measure HBM and not the 256 MB Infinity Cache, steps rotate through
+``--pools`` independent copies of the KV pool (16 by default, about 2.7 GB, as
+16 full-attention layers of one decode step would). Timing uses HIP events on
+the stream the library launches on. One JSON line goes to stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn µs/step and KV-read GB/s (% of HBM peak) at 32K ctx, batch 1"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="hybrid", choices=["hybrid", "dense", "mixed"])
+    ap.add_argument("--context", type=int, default=32768)
+    ap.add_argument("--block-size", type=int, default=784)
+    ap.add_argument("--pools", type=int, default=16)
+    ap.add_argument("--splits", type=int, default=0, help="force a split count (0 = planner)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--repeats", type=int, default=5, help="extra timed regions for spread statistics")
+    return ap.parse_args()
+
+
+class Hip:
+    """HIP events through the runtime torch loaded (one runtime per process)."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so.7")
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+
+    def event(self):
+        ev = ctypes.c_void_p()
+        rc = self.h.hipEventCreate(ctypes.byref(ev))
+        assert rc == 0, f"hipEventCreate failed: {rc}"
+        return ev
+
+    def record(self, ev, stream):
+        rc = self.h.hipEventRecord(ev, ctypes.c_void_p(stream))
+        assert rc == 0, f"hipEventRecord failed: {rc}"
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.h.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        assert rc == 0, f"hipEventElapsedTime failed: {rc}"
+        return ms.value
+
+    def destroy(self, ev):
+        self.h.hipEventDestroy(ev)
+
+
+def make_workload(args):
+    from paged_kv_cache_08_amd import workloads as W
+    if args.workload == "hybrid":
+        case = W.hybrid_long_context(args.context, block_size=args.block_size, poison=False)
+        name = (f"hybrid decode: batch 1, q_len 1, 24 q / 4 KV heads, head_dim 256, page {args.block_size}, "
+                f"context {args.context}, 5% of keys x4")
+    elif args.workload == "dense":
+        case = W.dense_control(args.context, poison=False)
+        name = f"dense control: batch 1, q_len 1, 32 q / 8 KV heads, head_dim 128, page 16, context {args.context}"
+    else:
+        case = W.mixed_batch(poison=False)
+        name = "mixed batch: 16 sequences, q_len 1, 24 q / 4 KV heads, head_dim 256, page 784, log-uniform 500-32000"
+    return case, name
+
+
+def traffic_from_profiles(kernel_src_hash: str, workload_key: str):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path)).get(workload_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_src_sha256") != kernel_src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_08_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def cpu_baseline(case, kv_bytes_per_call, seconds):
+    """The oracle as it stands, on the host cores, over whole calls of the same
+    workload until about `seconds` of CPU work has run."""
+    import oracle.paged_attention as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    n, t0 = 0, time.perf_counter()
+    while True:
+        O.paged_attention_ref(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                              case.block_size, case.scale)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= 1000:
+            break
+    return {
+        "value": round(kv_bytes_per_call * n / el / 1e9, 3),
+        "unit": "GB/s",
+        "us_per_call": round(el / n * 1e6, 1),
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{n} full oracle calls on the benchmark input (fp64 NumPy, BLAS threads={threads}), {el:.1f} s",
+        "host_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence, KV head or context; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_08_amd as P
+    from paged_kv_cache_08_amd import workloads as W
+
+    assert torch.cuda.is_available(), "no GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    case, wl_name = make_workload(args)
+    print(f"[bench] workload: {wl_name}", file=sys.stderr, flush=True)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q = bf16(case.q)
+    k0, v0 = bf16(case.k_cache), bf16(case.v_cache)
+    table = torch.from_numpy(case.block_table).to(dev)
+    lens = torch.from_numpy(case.seq_lens).to(dev)
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(max(args.pools, 1) - 1)]
+    total_tokens = int(case.seq_lens.sum())
+    kv_bytes = W.kv_read_bytes(case.seq_lens, case.k_cache.shape[2], case.k_cache.shape[3])
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    call = P.PreparedDecode(q, k0, v0, table, lens, case.block_size, case.scale, max_seq_len=case.max_seq_len,
+                            total_tokens=total_tokens, num_splits=args.splits, stream=stream)
+    out = call.out
+
+    def step(i):
+        k, v = pools[i % len(pools)]
+        call.run(k, v)
+
+    hip = Hip()
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    variant = P.last_variant()
+    print(f"[bench] variant: {variant}", file=sys.stderr, flush=True)
+
+    # The contract's timed region: exactly `steps` calls between two events.
+    ev0, ev1 = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    hip.record(ev0, stream)
+    for i in range(args.steps):
+        step(i)
+    hip.record(ev1, stream)
+    torch.cuda.synchronize()
+    total_ms = hip.elapsed_ms(ev0, ev1)
+    ms_per_step = total_ms / args.steps
+
+    # Spread: more timed regions of the same length.
+    region_us = [ms_per_step * 1e3]
+    for _ in range(args.repeats):
+        torch.cuda.synchronize()
+        hip.record(ev0, stream)
+        for i in range(args.steps):
+            step(i)
+        hip.record(ev1, stream)
+        torch.cuda.synchronize()
+        region_us.append(hip.elapsed_ms(ev0, ev1) / args.steps * 1e3)
+
+    # Split-kernel duration: events recorded by the library right around it.
+    pairs = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        P.set_timing_events(pairs[i][0], pairs[i][1])
+        step(i)
+    P.set_timing_events(None, None)
+    torch.cuda.synchronize()
+    kern_us = [hip.elapsed_ms(a, b) * 1e3 for a, b in pairs]
+    for a, b in pairs:
+        hip.destroy(a)
+        hip.destroy(b)
+    kern_avg_us = sum(kern_us) / len(kern_us)
+
+    # Spot parity on sampled heads of the timed output (pool 0 holds the seeded input).
+    step(0)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    parity = None
+    try:
+        import oracle.paged_attention as O
+        ref = O.paged_attention_ref(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                                    case.block_size, case.scale)
+        parity = float(np.abs(got - ref).max())
+    except Exception as e:  # parity is reported, never required for the timing
+        print(f"[bench] parity check skipped: {e}", file=sys.stderr)
+
+    gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    kern_gbs = kv_bytes / (kern_avg_us * 1e-6) / 1e9
+    src_hash = kernel_source_hash()
+    wl_key = f"{args.workload}:{args.context}:{case.block_size}"
+    traffic = traffic_from_profiles(src_hash, wl_key)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(case, kv_bytes, args.cpu_seconds)
+
+    med = statistics.median(region_us)
+    rec = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl_name,
+            "batch": int(case.num_seqs),
+            "context": int(case.max_seq_len),
+            "block_size": int(case.block_size),
+            "kv_pools_rotated": len(pools),
+            "kv_bytes_per_step": kv_bytes,
+            "variant": variant,
+        },
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 1),
+        "us_per_step_regions": {"median": round(med, 2), "min": round(min(region_us), 2),
+                                "max": round(max(region_us), 2),
+                                "range_pct": round(100.0 * (max(region_us) - min(region_us)) / med, 2)},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_split_kernel",
+            "achieved": round(kern_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel_us_avg": round(kern_avg_us, 2),
+            "kernel_us_min": round(min(kern_us), 2),
+        },
+        "cpu_baseline": cpu,
+        "parity_max_abs_err": parity,
+    }
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,179 @@
+/*
+ * pkv.h — C ABI of the paged decode-attention library for AMD MI355X (gfx950).
+ *
+ * The operation (what one call computes) follows the statement of the problem
+ * in "DCU page832 attention" (luanjiahao.me): a token's logical page is
+ * token / BLOCK_SIZE, its in-page offset token % BLOCK_SIZE, the block table
+ * maps logical to physical page, and strides for page, token and KV head give
+ * the element address (§1, §4); per key tile, score = dot(Q, K) * scale and an
+ * online softmax accumulates V (§5); decode reads every logical page of the
+ * sequence (§7). The KV range of one (sequence, KV head) is cut into splits
+ * that run on separate workgroups and are merged afterwards, as the split-KV
+ * paragraph of "vLLM 下双卡 Radeon 上的混合 SSM 解码速率" describes; several
+ * query rows of one request share each K/V walk with a per-row causal mask and
+ * a merge of partial softmax statistics, as in "Qwen3.8 auf MI350P betreiben",
+ * Lektion 3.
+ *
+ * For sequence b, query row i and query head h (G = Hq / Hkv, KV head h / G):
+ *     out[b,i,h,:] = softmax_j( scale * q[b,i,h,:] . K_j ) V_j,
+ *     j over tokens 0 .. seq_lens[b] - q_len + i   (bottom-right causal window)
+ *
+ * Conventions shared by every entry point:
+ *   - All pointers named *device* point to device memory on the current HIP
+ *     device; everything else is host memory. The caller owns every buffer.
+ *   - bf16 is IEEE bfloat16 (uint16 storage). Strides are in elements.
+ *   - Functions return 0 (PKV_OK) or a negative PKV_ERR_* code and never throw.
+ *     pkv_strerror() turns a code into text; PKV_ERR_HIP also records the HIP
+ *     error string, available from pkv_last_error().
+ *   - Entry points that take a stream enqueue work on it and return without
+ *     synchronising. The library keeps no pointer after it returns.
+ *   - The library allocates no device memory in these calls; the caller passes
+ *     a workspace sized by pkv_workspace_bytes().
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_OK               0
+#define PKV_ERR_INVALID     -1  /* null pointer, bad size, Hq % Hkv != 0, stride or alignment error */
+#define PKV_ERR_UNSUPPORTED -2  /* head_dim not 128/256, q_len not in [1,16], group size > 8, ... */
+#define PKV_ERR_WORKSPACE   -3  /* workspace smaller than pkv_workspace_bytes() */
+#define PKV_ERR_HIP         -4  /* a HIP runtime call or launch failed */
+
+#define PKV_OUT_F32  0
+#define PKV_OUT_BF16 1
+
+/* Problem description. Layout is fixed: 10 x int32, 7 x int64, float, int32
+ * (104 bytes, natural alignment). */
+typedef struct pkv_decode_params {
+  int32_t num_seqs;          /* sequences in the batch, >= 1 */
+  int32_t q_len;             /* new query rows per sequence, 1..16 (1 = decode) */
+  int32_t num_q_heads;       /* Hq */
+  int32_t num_kv_heads;      /* Hkv; Hq % Hkv == 0 and Hq / Hkv <= 8 */
+  int32_t head_dim;          /* D: 128 or 256 */
+  int32_t block_size;        /* tokens per physical page, any value >= 1 (e.g. 16, 784, 832) */
+  int32_t max_pages_per_seq; /* row stride of block_table, in entries */
+  int32_t max_seq_len;       /* host-known upper bound of seq_lens[b]; <= max_pages_per_seq * block_size */
+  int32_t num_pages;         /* physical pages in the pool; table entries outside [0, num_pages) are never dereferenced */
+  int32_t num_splits;        /* 0 = planner's choice; > 0 asks for that many splits of the longest sequence */
+  int64_t total_tokens;      /* optional planner hint: sum of seq_lens (0 = unknown, assume num_seqs * max_seq_len) */
+  int64_t k_stride_page;     /* K cache strides in elements: page, token, KV head; the dim stride is 1 */
+  int64_t k_stride_tok;
+  int64_t k_stride_head;
+  int64_t v_stride_page;     /* V cache strides, same meaning */
+  int64_t v_stride_tok;
+  int64_t v_stride_head;
+  float   scale;             /* softmax scale applied to q . k (e.g. 1/sqrt(D)) */
+  int32_t out_dtype;         /* PKV_OUT_F32 or PKV_OUT_BF16 */
+} pkv_decode_params;
+
+/* Library version string (static storage). */
+const char* pkv_version(void);
+
+/* Text for a PKV_* code (static storage). */
+const char* pkv_strerror(int code);
+
+/* Detail of the most recent error on the calling thread (e.g. the HIP error
+ * string); empty when none. Static thread-local storage. */
+const char* pkv_last_error(void);
+
+/* Host-only check of *p (no HIP call): sizes, group size, head_dim, q_len,
+ * strides (positive, multiples of 8 so every K/V row starts on 16 bytes),
+ * max_seq_len <= max_pages_per_seq * block_size. Returns PKV_OK or an error. */
+int pkv_validate_params(const pkv_decode_params* p);
+
+/* Host-only split plan (no HIP call). With T = 64-token tiles:
+ *   n_tiles = ceil(max_seq_len / T);
+ *   work    = total_tokens, or num_seqs * max_seq_len when total_tokens == 0;
+ *   c       = max(min_tiles, ceil(Hkv * work / (cu_count * wg_per_cu * T))),
+ *             or ceil(n_tiles / num_splits) when num_splits > 0;
+ *   c       = clamp(c, 1, min(n_tiles, floor((tbl_cap - 2) * block_size / T)));
+ *   *num_splits = ceil(n_tiles / c); *chunk_tokens = c * T.
+ * Sequence b then uses ceil(L_b / chunk) splits; split s covers tokens
+ * [s * chunk, min((s + 1) * chunk, L_b)). cu_count must be >= 1. */
+int pkv_plan_splits(const pkv_decode_params* p, int32_t cu_count,
+                    int32_t* num_splits, int32_t* chunk_tokens);
+
+/* The planner's constants: tile T, workgroups per CU, minimum tiles per split,
+ * block-table entries a split may span. Any pointer may be NULL. */
+int pkv_plan_constants(int32_t* tile, int32_t* wg_per_cu, int32_t* min_tiles, int32_t* tbl_cap);
+
+/* Bytes of device workspace a call with *p needs when planned for cu_count
+ * CUs (cu_count <= 0: the current device's CU count, which initialises HIP).
+ * Returns the size (>= 256), or a negative PKV_ERR_* code. */
+int64_t pkv_workspace_bytes(const pkv_decode_params* p, int32_t cu_count);
+
+/* Compute units of the current HIP device. */
+int pkv_device_cu_count(int32_t* cu_count);
+
+/*
+ * The decode-attention call.
+ *   q           device bf16 [num_seqs, q_len, Hq, D], contiguous.
+ *   k_cache     device bf16, row (page, token, kv_head) at
+ *               page * k_stride_page + token * k_stride_tok + kv_head * k_stride_head;
+ *               both [P, B, Hkv, D] and views of [P, 2, B, Hkv, D] fit.
+ *   v_cache     device bf16, same with the v_* strides.
+ *   block_table device int32 [num_seqs, max_pages_per_seq]; entries past a
+ *               sequence's last page are never read.
+ *   seq_lens    device int32 [num_seqs]; tokens in the cache for each sequence,
+ *               the q_len new ones included. L = 0 gives zeros; a query row
+ *               with no visible token gives zeros.
+ *   out         device [num_seqs, q_len, Hq, D], float32 or bf16 (out_dtype).
+ *   workspace   device, >= pkv_workspace_bytes(p, 0) bytes, 256-byte aligned;
+ *               its first 4 bytes are a sticky error word (bit 0: a block-table
+ *               entry outside [0, num_pages) was met and its tokens skipped);
+ *               zero it once after allocating. Calls that share a workspace
+ *               must not overlap in time.
+ *   stream      hipStream_t (NULL = default stream).
+ * q, k_cache, v_cache and out must be 16-byte aligned. No input is written.
+ */
+int pkv_paged_decode_attention(const pkv_decode_params* p,
+                               const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               void* out, void* workspace, int64_t workspace_bytes,
+                               void* stream);
+
+/* Which kernels the last successful pkv_paged_decode_attention call on this
+ * thread launched, with the split plan, e.g.
+ * "decode_valu d256 g6 + lse_merge splits=64 chunk=512 B=784". Copies at most
+ * len-1 characters plus a terminator; returns the full length. */
+int pkv_last_variant(char* buf, int32_t len);
+
+/* Profiling hook: when both are non-NULL, later calls on this thread record
+ * ev_start immediately before and ev_stop immediately after the split kernel
+ * (hipEvent_t handles, on the call's stream). NULL, NULL turns it off. */
+int pkv_set_timing_events(void* ev_start, void* ev_stop);
+
+/* Debug: the element offset of every live token row of KV head kv_head, as the
+ * split kernel computes it (same device code: split range, table staging,
+ * division by block_size, stride arithmetic). k_off, v_off: device int64
+ * [num_seqs, max_seq_len]; slots j >= L_b get -1. */
+int pkv_debug_token_offsets(const pkv_decode_params* p, const int32_t* block_table,
+                            const int32_t* seq_lens, int32_t kv_head,
+                            int64_t* k_off, int64_t* v_off, void* stream);
+
+/* Debug: every split's token range [begin, end) as the split kernel derives it.
+ * ranges: device int32 [num_seqs, num_splits, 2] for the planned num_splits
+ * (pkv_plan_splits with the device CU count); unused splits get [L, L). */
+int pkv_debug_split_ranges(const pkv_decode_params* p, const int32_t* seq_lens,
+                           int32_t* ranges, void* stream);
+
+/* Host self-check of the division by an invariant integer used for
+ * token / block_size (Granlund & Montgomery, PLDI 1994, unsigned case): returns
+ * the first n in [0, n_max] whose quotient differs from n / divisor, or -1. */
+int64_t pkv_magic_div_check(int32_t divisor, int64_t n_max);
+
+/* Reads the workspace error word (synchronous copy to the host). */
+int pkv_read_error_word(const void* workspace, int32_t* value);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

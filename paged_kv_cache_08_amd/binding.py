@@ -1,0 +1,298 @@
+"""ctypes binding of the C ABI in include/pkv.h.
+
+Argument marshalling only: every step of the attention runs in the HIP library.
+PyTorch supplies device memory and the current stream. There is no fallback:
+if ``libpkv.so`` is missing or a call fails, a RuntimeError says so.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libpkv.so")
+
+PKV_OK = 0
+PKV_ERR_INVALID = -1
+PKV_ERR_UNSUPPORTED = -2
+PKV_ERR_WORKSPACE = -3
+PKV_ERR_HIP = -4
+PKV_OUT_F32 = 0
+PKV_OUT_BF16 = 1
+
+
+class DecodeParams(ctypes.Structure):
+    """Mirror of ``pkv_decode_params``."""
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("q_len", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+        ("total_tokens", ctypes.c_int64),
+        ("k_stride_page", ctypes.c_int64),
+        ("k_stride_tok", ctypes.c_int64),
+        ("k_stride_head", ctypes.c_int64),
+        ("v_stride_page", ctypes.c_int64),
+        ("v_stride_tok", ctypes.c_int64),
+        ("v_stride_head", ctypes.c_int64),
+        ("scale", ctypes.c_float),
+        ("out_dtype", ctypes.c_int32),
+    ]
+
+
+assert ctypes.sizeof(DecodeParams) == 104
+
+_lock = threading.Lock()
+_lib = None
+
+_P = ctypes.POINTER(DecodeParams)
+_vp = ctypes.c_void_p
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_SIGNATURES = {
+    "pkv_version": (ctypes.c_char_p, []),
+    "pkv_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "pkv_last_error": (ctypes.c_char_p, []),
+    "pkv_validate_params": (ctypes.c_int, [_P]),
+    "pkv_plan_splits": (ctypes.c_int, [_P, ctypes.c_int32, _i32p, _i32p]),
+    "pkv_plan_constants": (ctypes.c_int, [_i32p, _i32p, _i32p, _i32p]),
+    "pkv_workspace_bytes": (ctypes.c_int64, [_P, ctypes.c_int32]),
+    "pkv_device_cu_count": (ctypes.c_int, [_i32p]),
+    "pkv_paged_decode_attention": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64, _vp]),
+    "pkv_last_variant": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_int32]),
+    "pkv_set_timing_events": (ctypes.c_int, [_vp, _vp]),
+    "pkv_debug_token_offsets": (ctypes.c_int, [_P, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp]),
+    "pkv_debug_split_ranges": (ctypes.c_int, [_P, _vp, _vp, _vp]),
+    "pkv_magic_div_check": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int64]),
+    "pkv_read_error_word": (ctypes.c_int, [_vp, _i32p]),
+}
+EXPORTED = tuple(_SIGNATURES)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            # torch ships its own HIP runtime (same soname as /opt/rocm's). Load it
+            # first so libpkv.so binds to it: one runtime per process, and torch's
+            # stream handles are valid in the library's launches.
+            try:
+                import torch  # noqa: F401
+            except ImportError:
+                pass
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                                   "(run `python -m paged_kv_cache_08_amd.build`)")
+            h = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in _SIGNATURES.items():
+                fn = getattr(h, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = h
+    return _lib
+
+
+def check(rc: int, what: str) -> None:
+    if rc != PKV_OK:
+        L = lib()
+        raise RuntimeError(f"{what} failed: {L.pkv_strerror(rc).decode()} ({rc}): {L.pkv_last_error().decode()}")
+
+
+def version() -> str:
+    return lib().pkv_version().decode()
+
+
+def plan_constants() -> dict:
+    vals = [ctypes.c_int32() for _ in range(4)]
+    check(lib().pkv_plan_constants(*[ctypes.byref(v) for v in vals]), "pkv_plan_constants")
+    return dict(zip(("tile", "wg_per_cu", "min_tiles", "tbl_cap"), (v.value for v in vals)))
+
+
+def validate(p: DecodeParams) -> int:
+    return lib().pkv_validate_params(ctypes.byref(p))
+
+
+def plan_splits(p: DecodeParams, cu_count: int) -> tuple[int, int]:
+    s, c = ctypes.c_int32(), ctypes.c_int32()
+    check(lib().pkv_plan_splits(ctypes.byref(p), cu_count, ctypes.byref(s), ctypes.byref(c)), "pkv_plan_splits")
+    return s.value, c.value
+
+
+def workspace_bytes(p: DecodeParams, cu_count: int = 0) -> int:
+    n = lib().pkv_workspace_bytes(ctypes.byref(p), cu_count)
+    if n < 0:
+        check(int(n), "pkv_workspace_bytes")
+    return int(n)
+
+
+def device_cu_count() -> int:
+    c = ctypes.c_int32()
+    check(lib().pkv_device_cu_count(ctypes.byref(c)), "pkv_device_cu_count")
+    return c.value
+
+
+def magic_div_check(divisor: int, n_max: int) -> int:
+    return int(lib().pkv_magic_div_check(divisor, n_max))
+
+
+def last_variant() -> str:
+    buf = ctypes.create_string_buffer(512)
+    lib().pkv_last_variant(buf, 512)
+    return buf.value.decode()
+
+
+def set_timing_events(ev_start, ev_stop) -> None:
+    check(lib().pkv_set_timing_events(ev_start, ev_stop), "pkv_set_timing_events")
+
+
+# ---------------------------------------------------------------------------
+# torch-facing helpers (torch only for memory and streams).
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def make_params(q, k_cache, v_cache, block_table, block_size: int, scale: float, *, max_seq_len: int,
+                num_splits: int = 0, total_tokens: int = 0, out_dtype: int = PKV_OUT_F32) -> DecodeParams:
+    """Fill DecodeParams from tensor shapes and strides.
+
+    q: [num_seqs, q_len, Hq, D]; k_cache / v_cache: [num_pages, B, Hkv, D] with
+    unit stride on D; block_table: [num_seqs, max_pages]."""
+    ns, ql, hq, d = q.shape
+    P, B, hkv, d2 = k_cache.shape
+    assert d2 == d and tuple(v_cache.shape) == tuple(k_cache.shape) and B == block_size
+    assert k_cache.stride(-1) == 1 and v_cache.stride(-1) == 1
+    p = DecodeParams()
+    p.num_seqs, p.q_len, p.num_q_heads, p.num_kv_heads, p.head_dim = ns, ql, hq, hkv, d
+    p.block_size = block_size
+    p.max_pages_per_seq = block_table.shape[1]
+    p.max_seq_len = int(max_seq_len)
+    p.num_pages = P
+    p.num_splits = int(num_splits)
+    p.total_tokens = int(total_tokens)
+    p.k_stride_page, p.k_stride_tok, p.k_stride_head = k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)
+    p.v_stride_page, p.v_stride_tok, p.v_stride_head = v_cache.stride(0), v_cache.stride(1), v_cache.stride(2)
+    p.scale = float(scale)
+    p.out_dtype = out_dtype
+    return p
+
+
+def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, block_size: int, scale: float, *,
+                           max_seq_len: int | None = None, total_tokens: int = 0, num_splits: int = 0,
+                           out=None, out_dtype=None, workspace=None, stream=None):
+    """out[b,i,h,:] = softmax(scale * q[b,i,h,:] . K_j) V_j over the visible tokens of sequence b.
+
+    q: bf16 [num_seqs, q_len, Hq, D] (contiguous, on the GPU); k_cache / v_cache:
+    bf16 [num_pages, B, Hkv, D] (views of a combined [num_pages, 2, B, Hkv, D]
+    cache are fine); block_table / seq_lens: int32 on the GPU. max_seq_len is the
+    host-known bound of seq_lens (read from the GPU, with a sync, when omitted).
+    Returns out ([num_seqs, q_len, Hq, D], float32 unless out_dtype/out say bf16).
+    """
+    torch = _torch()
+    assert q.is_cuda and q.dtype == torch.bfloat16 and q.is_contiguous()
+    assert k_cache.dtype == torch.bfloat16 and v_cache.dtype == torch.bfloat16
+    assert block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
+    assert block_table.is_contiguous() and seq_lens.is_contiguous()
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if seq_lens.numel() else 0
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    odt = PKV_OUT_BF16 if out.dtype == torch.bfloat16 else PKV_OUT_F32
+    assert out.dtype in (torch.float32, torch.bfloat16) and out.is_contiguous() and out.shape == q.shape
+    p = make_params(q, k_cache, v_cache, block_table, block_size, scale, max_seq_len=max_seq_len,
+                    num_splits=num_splits, total_tokens=total_tokens, out_dtype=odt)
+    need = workspace_bytes(p, 0)
+    if workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib().pkv_paged_decode_attention(
+        ctypes.byref(p), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+        seq_lens.data_ptr(), out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        stream)
+    check(rc, "pkv_paged_decode_attention")
+    return out
+
+
+def debug_token_offsets(p: DecodeParams, block_table, seq_lens, kv_head: int):
+    """Per-token K and V row offsets as the split kernel computes them ([num_seqs, max_seq_len] int64)."""
+    torch = _torch()
+    shape = (p.num_seqs, max(p.max_seq_len, 1))
+    k_off = torch.empty(shape, dtype=torch.int64, device=block_table.device)
+    v_off = torch.empty(shape, dtype=torch.int64, device=block_table.device)
+    stream = torch.cuda.current_stream(block_table.device).cuda_stream
+    check(lib().pkv_debug_token_offsets(ctypes.byref(p), block_table.data_ptr(), seq_lens.data_ptr(), kv_head,
+                                        k_off.data_ptr(), v_off.data_ptr(), stream), "pkv_debug_token_offsets")
+    return k_off, v_off
+
+
+def debug_split_ranges(p: DecodeParams, seq_lens):
+    """[num_seqs, S, 2] split ranges as the split kernel derives them."""
+    torch = _torch()
+    S, _ = plan_splits(p, device_cu_count())
+    r = torch.empty((p.num_seqs, S, 2), dtype=torch.int32, device=seq_lens.device)
+    stream = torch.cuda.current_stream(seq_lens.device).cuda_stream
+    check(lib().pkv_debug_split_ranges(ctypes.byref(p), seq_lens.data_ptr(), r.data_ptr(), stream),
+          "pkv_debug_split_ranges")
+    return r
+
+
+def read_error_word(workspace) -> int:
+    v = ctypes.c_int32()
+    check(lib().pkv_read_error_word(workspace.data_ptr(), ctypes.byref(v)), "pkv_read_error_word")
+    return v.value
+
+
+class PreparedDecode:
+    """A decode call whose arguments are checked and marshalled once; ``run()``
+    then only crosses into the C library (for tight loops and benchmarks).
+
+    ``run(k_cache, v_cache)`` may swap in another pool with the same shape and
+    strides as the one given at construction."""
+
+    def __init__(self, q, k_cache, v_cache, block_table, seq_lens, block_size: int, scale: float, *,
+                 max_seq_len: int, total_tokens: int = 0, num_splits: int = 0, out=None, workspace=None,
+                 stream=None):
+        torch = _torch()
+        assert q.is_cuda and q.dtype == torch.bfloat16 and q.is_contiguous()
+        assert block_table.is_contiguous() and seq_lens.is_contiguous()
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        odt = PKV_OUT_BF16 if out.dtype == torch.bfloat16 else PKV_OUT_F32
+        self.params = make_params(q, k_cache, v_cache, block_table, block_size, scale, max_seq_len=max_seq_len,
+                                  num_splits=num_splits, total_tokens=total_tokens, out_dtype=odt)
+        check(validate(self.params), "pkv_validate_params")
+        need = workspace_bytes(self.params, 0)
+        if workspace is None:
+            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        assert workspace.numel() * workspace.element_size() >= need
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+        self.out, self.workspace = out, workspace
+        self._shape = (tuple(k_cache.shape), tuple(k_cache.stride()), tuple(v_cache.stride()))
+        self._keep = (q, k_cache, v_cache, block_table, seq_lens)
+        self._fn = lib().pkv_paged_decode_attention
+        self._pp = ctypes.byref(self.params)
+        self._fixed = (q.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
+                       workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
+        self._k, self._v = k_cache.data_ptr(), v_cache.data_ptr()
+
+    def run(self, k_cache=None, v_cache=None):
+        kp, vp = self._k, self._v
+        if k_cache is not None:
+            assert (tuple(k_cache.shape), tuple(k_cache.stride()), tuple(v_cache.stride())) == self._shape
+            kp, vp = k_cache.data_ptr(), v_cache.data_ptr()
+        qp, tp, lp, op, wp, wn, st = self._fixed
+        rc = self._fn(self._pp, qp, kp, vp, tp, lp, op, wp, wn, st)
+        if rc != PKV_OK:
+            check(rc, "pkv_paged_decode_attention")
+        return self.out

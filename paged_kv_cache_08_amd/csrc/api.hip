@@ -1,0 +1,323 @@
+// Host side of the C ABI declared in include/pkv.h: argument checks, the split
+// planner, workspace layout, kernel selection and launches. No device memory
+// is allocated here and no call synchronises the stream (the debug readers
+// excepted).
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "pkv.h"
+#include "pkv_common.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local std::string g_last_variant;
+thread_local hipEvent_t g_ev_start = nullptr;
+thread_local hipEvent_t g_ev_stop = nullptr;
+
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices] = {0};
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return PKV_ERR_HIP;
+}
+
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+bool mult8_pos(int64_t s) { return s > 0 && (s % 8) == 0; }
+
+int plan(const pkv_decode_params* p, int32_t cu_count, int32_t* S, int32_t* chunk) {
+  const int64_t T = pkv::kTile;
+  const int64_t n_tiles = p->max_seq_len > 0 ? cdiv64(p->max_seq_len, T) : 1;
+  int64_t cap = ((pkv::kTblCap - 2) * int64_t(p->block_size)) / T;
+  if (cap < 1) cap = 1;
+  int64_t c;
+  if (p->num_splits > 0) {
+    c = cdiv64(n_tiles, p->num_splits);
+  } else {
+    const int64_t work = p->total_tokens > 0 ? p->total_tokens : int64_t(p->num_seqs) * p->max_seq_len;
+    int64_t target = int64_t(cu_count) * pkv::kWgPerCu;
+    if (target < 1) target = 1;
+    c = cdiv64(int64_t(p->num_kv_heads) * work, target * T);
+    if (c < pkv::kMinTiles) c = pkv::kMinTiles;
+  }
+  if (c > n_tiles) c = n_tiles;
+  if (c > cap) c = cap;
+  if (c < 1) c = 1;
+  *S = int32_t(cdiv64(n_tiles, c));
+  *chunk = int32_t(c * T);
+  return PKV_OK;
+}
+
+int64_t workspace_for(const pkv_decode_params* p, int32_t S) {
+  const int64_t rows = int64_t(p->num_seqs) * p->q_len * p->num_q_heads;
+  return pkv::kWsHeaderBytes + align256(rows * S * 2 * 4) + align256(rows * S * int64_t(p->head_dim) * 4);
+}
+
+int device_cu_count(int32_t* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev >= 0 && dev < kMaxDevices && g_cu_count[dev] > 0) {
+    *out = g_cu_count[dev];
+    return PKV_OK;
+  }
+  int cu = 0;
+  e = hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(MultiprocessorCount)");
+  if (cu < 1) return fail(PKV_ERR_HIP, "device reports no compute units");
+  if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev] = cu;
+  *out = cu;
+  return PKV_OK;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
+
+pkv::DecodeArgs make_args(const pkv_decode_params* p, int32_t S, int32_t chunk) {
+  pkv::DecodeArgs a{};
+  a.k_sp = p->k_stride_page;
+  a.k_st = p->k_stride_tok;
+  a.k_sh = p->k_stride_head;
+  a.v_sp = p->v_stride_page;
+  a.v_st = p->v_stride_tok;
+  a.v_sh = p->v_stride_head;
+  a.num_seqs = p->num_seqs;
+  a.q_len = p->q_len;
+  a.hq = p->num_q_heads;
+  a.hkv = p->num_kv_heads;
+  a.max_pages = p->max_pages_per_seq;
+  a.num_pages = p->num_pages;
+  a.chunk = chunk;
+  a.num_splits = S;
+  a.bdiv = pkv::make_magic(uint32_t(p->block_size));
+  a.scale_log2 = float(double(p->scale) * 1.4426950408889634);
+  a.out_bf16 = p->out_dtype == PKV_OUT_BF16;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_version(void) { return "pkv 0.1.0 gfx950"; }
+
+const char* pkv_strerror(int code) {
+  switch (code) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported shape";
+    case PKV_ERR_WORKSPACE: return "workspace too small";
+    case PKV_ERR_HIP: return "HIP runtime error";
+    default: return "unknown error";
+  }
+}
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+int pkv_validate_params(const pkv_decode_params* p) {
+  if (!p) return fail(PKV_ERR_INVALID, "params is NULL");
+  if (p->num_seqs < 1 || p->q_len < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1 ||
+      p->block_size < 1 || p->max_pages_per_seq < 1 || p->num_pages < 1 || p->max_seq_len < 0 ||
+      p->num_splits < 0 || p->total_tokens < 0)
+    return fail(PKV_ERR_INVALID, "a size is out of range");
+  if (p->num_q_heads % p->num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID, "num_q_heads is not a multiple of num_kv_heads");
+  const int group = p->num_q_heads / p->num_kv_heads;
+  if (p->head_dim != 128 && p->head_dim != 256) return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 128 or 256");
+  if (group > 8) return fail(PKV_ERR_UNSUPPORTED, "more than 8 query heads per KV head");
+  if (p->q_len > 16) return fail(PKV_ERR_UNSUPPORTED, "q_len above 16");
+  if (p->q_len == 1 && !pkv::decode_supported(p->head_dim, group))
+    return fail(PKV_ERR_UNSUPPORTED, "no decode kernel for this head_dim / group");
+  if (p->q_len > 1 && !pkv::verify_supported(p->head_dim, group, p->q_len))
+    return fail(PKV_ERR_UNSUPPORTED, "no multi-row kernel for this head_dim / group / q_len");
+  if (int64_t(p->max_pages_per_seq) * p->block_size < p->max_seq_len)
+    return fail(PKV_ERR_INVALID, "max_seq_len exceeds max_pages_per_seq * block_size");
+  if (!mult8_pos(p->k_stride_page) || !mult8_pos(p->k_stride_tok) || !mult8_pos(p->k_stride_head) ||
+      !mult8_pos(p->v_stride_page) || !mult8_pos(p->v_stride_tok) || !mult8_pos(p->v_stride_head))
+    return fail(PKV_ERR_INVALID, "K/V strides must be positive multiples of 8 elements");
+  if (!isfinite(p->scale)) return fail(PKV_ERR_INVALID, "scale is not finite");
+  if (p->out_dtype != PKV_OUT_F32 && p->out_dtype != PKV_OUT_BF16)
+    return fail(PKV_ERR_INVALID, "unknown out_dtype");
+  return PKV_OK;
+}
+
+int pkv_plan_splits(const pkv_decode_params* p, int32_t cu_count, int32_t* num_splits, int32_t* chunk_tokens) {
+  int rc = pkv_validate_params(p);
+  if (rc) return rc;
+  if (cu_count < 1 || !num_splits || !chunk_tokens) return fail(PKV_ERR_INVALID, "bad cu_count or output pointer");
+  return plan(p, cu_count, num_splits, chunk_tokens);
+}
+
+int pkv_plan_constants(int32_t* tile, int32_t* wg_per_cu, int32_t* min_tiles, int32_t* tbl_cap) {
+  if (tile) *tile = pkv::kTile;
+  if (wg_per_cu) *wg_per_cu = pkv::kWgPerCu;
+  if (min_tiles) *min_tiles = pkv::kMinTiles;
+  if (tbl_cap) *tbl_cap = pkv::kTblCap;
+  return PKV_OK;
+}
+
+int64_t pkv_workspace_bytes(const pkv_decode_params* p, int32_t cu_count) {
+  int rc = pkv_validate_params(p);
+  if (rc) return rc;
+  if (cu_count <= 0) {
+    rc = device_cu_count(&cu_count);
+    if (rc) return rc;
+  }
+  int32_t S = 0, chunk = 0;
+  plan(p, cu_count, &S, &chunk);
+  return workspace_for(p, S);
+}
+
+int pkv_device_cu_count(int32_t* cu_count) {
+  if (!cu_count) return fail(PKV_ERR_INVALID, "cu_count is NULL");
+  return device_cu_count(cu_count);
+}
+
+int pkv_paged_decode_attention(const pkv_decode_params* p, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                               void* out, void* workspace, int64_t workspace_bytes, void* stream) {
+  int rc = pkv_validate_params(p);
+  if (rc) return rc;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out || !workspace)
+    return fail(PKV_ERR_INVALID, "a device pointer is NULL");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return fail(PKV_ERR_INVALID, "q, k_cache, v_cache and out must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return fail(PKV_ERR_INVALID, "workspace must be 256-byte aligned");
+  int32_t cu = 0;
+  rc = device_cu_count(&cu);
+  if (rc) return rc;
+  int32_t S = 0, chunk = 0;
+  plan(p, cu, &S, &chunk);
+  const int64_t need = workspace_for(p, S);
+  if (workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
+
+  pkv::DecodeArgs a = make_args(p, S, chunk);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_cache);
+  a.v = static_cast<const uint16_t*>(v_cache);
+  a.table = block_table;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  char* ws = static_cast<char*>(workspace);
+  const int64_t rows = int64_t(p->num_seqs) * p->q_len * p->num_q_heads;
+  a.err = reinterpret_cast<uint32_t*>(ws);
+  a.part_ml = reinterpret_cast<float*>(ws + pkv::kWsHeaderBytes);
+  a.part_acc = reinterpret_cast<float*>(ws + pkv::kWsHeaderBytes + align256(rows * S * 2 * 4));
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int group = p->num_q_heads / p->num_kv_heads;
+  hipError_t e;
+  if (g_ev_start && (e = hipEventRecord(g_ev_start, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  const char* split_name;
+  if (p->q_len == 1) {
+    e = pkv::launch_decode_split(a, p->head_dim, group, st);
+    split_name = "decode_valu";
+  } else {
+    e = pkv::launch_verify_split(a, p->head_dim, group, st);
+    split_name = "verify_mfma";
+  }
+  if (e != hipSuccess) return hip_fail(e, "split kernel launch");
+  if (g_ev_stop && (e = hipEventRecord(g_ev_stop, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if (S > 1) {
+    e = pkv::launch_lse_merge(a, p->head_dim, st);
+    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  }
+  char buf[256];
+  snprintf(buf, sizeof buf, "%s d%d g%d q%d%s splits=%d chunk=%d B=%d", split_name, p->head_dim, group,
+           p->q_len, S > 1 ? " + lse_merge" : "", S, chunk, p->block_size);
+  g_last_variant = buf;
+  g_last_error.clear();
+  return PKV_OK;
+}
+
+int pkv_last_variant(char* buf, int32_t len) {
+  const int n = int(g_last_variant.size());
+  if (buf && len > 0) {
+    const int c = n < len - 1 ? n : len - 1;
+    memcpy(buf, g_last_variant.data(), size_t(c));
+    buf[c] = '\0';
+  }
+  return n;
+}
+
+int pkv_set_timing_events(void* ev_start, void* ev_stop) {
+  if ((ev_start == nullptr) != (ev_stop == nullptr))
+    return fail(PKV_ERR_INVALID, "pass both events or neither");
+  g_ev_start = static_cast<hipEvent_t>(ev_start);
+  g_ev_stop = static_cast<hipEvent_t>(ev_stop);
+  return PKV_OK;
+}
+
+int pkv_debug_token_offsets(const pkv_decode_params* p, const int32_t* block_table, const int32_t* seq_lens,
+                            int32_t kv_head, int64_t* k_off, int64_t* v_off, void* stream) {
+  int rc = pkv_validate_params(p);
+  if (rc) return rc;
+  if (!block_table || !seq_lens || !k_off || !v_off) return fail(PKV_ERR_INVALID, "a device pointer is NULL");
+  if (kv_head < 0 || kv_head >= p->num_kv_heads) return fail(PKV_ERR_INVALID, "kv_head out of range");
+  int32_t cu = 0;
+  rc = device_cu_count(&cu);
+  if (rc) return rc;
+  int32_t S = 0, chunk = 0;
+  plan(p, cu, &S, &chunk);
+  pkv::DecodeArgs a = make_args(p, S, chunk);
+  a.table = block_table;
+  a.seq_lens = seq_lens;
+  a.err = nullptr;   // debug path: invalid entries still read as -2, nothing is flagged
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  const size_t n = size_t(p->num_seqs) * size_t(p->max_seq_len) * sizeof(int64_t);
+  if (n > 0) {
+    if ((e = hipMemsetAsync(k_off, 0xff, n, st)) != hipSuccess) return hip_fail(e, "hipMemsetAsync");
+    if ((e = hipMemsetAsync(v_off, 0xff, n, st)) != hipSuccess) return hip_fail(e, "hipMemsetAsync");
+  }
+  e = pkv::launch_debug_offsets(a, kv_head, p->max_seq_len, k_off, v_off, st);
+  if (e != hipSuccess) return hip_fail(e, "debug kernel launch");
+  return PKV_OK;
+}
+
+int pkv_debug_split_ranges(const pkv_decode_params* p, const int32_t* seq_lens, int32_t* ranges, void* stream) {
+  int rc = pkv_validate_params(p);
+  if (rc) return rc;
+  if (!seq_lens || !ranges) return fail(PKV_ERR_INVALID, "a device pointer is NULL");
+  int32_t cu = 0;
+  rc = device_cu_count(&cu);
+  if (rc) return rc;
+  int32_t S = 0, chunk = 0;
+  plan(p, cu, &S, &chunk);
+  pkv::DecodeArgs a = make_args(p, S, chunk);
+  a.seq_lens = seq_lens;
+  hipError_t e = pkv::launch_debug_ranges(a, ranges, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "debug kernel launch");
+  return PKV_OK;
+}
+
+int64_t pkv_magic_div_check(int32_t divisor, int64_t n_max) {
+  if (divisor < 1 || n_max < 0 || n_max > 0xffffffffLL) return -2;
+  const pkv::MagicDiv md = pkv::make_magic(uint32_t(divisor));
+  for (int64_t n = 0; n <= n_max; ++n) {
+    if (pkv::magic_div(uint32_t(n), md) != uint32_t(n / divisor)) return n;
+  }
+  return -1;
+}
+
+int pkv_read_error_word(const void* workspace, int32_t* value) {
+  if (!workspace || !value) return fail(PKV_ERR_INVALID, "NULL pointer");
+  hipError_t e = hipMemcpy(value, workspace, 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy");
+  return PKV_OK;
+}
+
+}  // extern "C"

@@ -30,11 +30,28 @@ BF16_NAN = np.uint16(0x7FC0)
 STREAMS = ("q", "k", "v", "mask", "pages", "lengths")
 
 
+def f32_to_bf16_bits_np(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest-even) and return the 16-bit patterns.
+
+    Finite and infinite inputs only (the rounding add cannot wrap for them)."""
+    u = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    r = u >> 16
+    r &= 1
+    r += 0x7FFF
+    u += r
+    u >>= 16
+    return u.astype(np.uint16)
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to bf16 (nearest-even) and return the 16-bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = u + 0x7FFF + ((u >> 16) & 1)
-    return (u >> 16).astype(np.uint16)
+    """Same rounding as :func:`f32_to_bf16_bits_np`; uses torch's multithreaded
+    float32 -> bfloat16 conversion (also round-to-nearest-even) when present."""
+    try:
+        import torch
+    except ImportError:
+        return f32_to_bf16_bits_np(x)
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
 
 
 def streams(seed: int) -> dict:

@@ -1,0 +1,59 @@
+"""Shared helpers for the GPU tests: move a seeded case to the device, run the
+HIP path through the C ABI, and the tolerance check against the fp64 oracle."""
+import sys
+
+import numpy as np
+
+ATOL = 2e-3        # max |gpu - oracle| over all elements
+RTOL = 1e-2        # max |gpu - oracle| / max(|oracle|, REL_FLOOR)
+REL_FLOOR = 1e-3
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def bf16_tensor(arr, device="cuda"):
+    import torch
+    a = np.ascontiguousarray(arr)
+    return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def to_device(case, device="cuda"):
+    import torch
+    q = bf16_tensor(case.q, device)
+    if case.kv_pool is not None:
+        pool = bf16_tensor(case.kv_pool, device)
+        k, v = pool[:, 0], pool[:, 1]
+    else:
+        k = bf16_tensor(case.k_cache, device)
+        v = bf16_tensor(case.v_cache, device)
+    table = torch.from_numpy(np.ascontiguousarray(case.block_table)).to(device)
+    lens = torch.from_numpy(np.ascontiguousarray(case.seq_lens)).to(device)
+    return q, k, v, table, lens
+
+
+def run_gpu(case, **kw):
+    import torch
+    import paged_kv_cache_08_amd as P
+    q, k, v, table, lens = to_device(case)
+    out = P.paged_decode_attention(q, k, v, table, lens, case.block_size, case.scale,
+                                   max_seq_len=case.max_seq_len, **kw)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def errors(gpu, ref):
+    err = np.abs(gpu - ref)
+    rel = err / np.maximum(np.abs(ref), REL_FLOOR)
+    return float(err.max(initial=0.0)), float(rel.max(initial=0.0))
+
+
+def assert_matches_oracle(gpu, ref, what=""):
+    assert gpu.shape == ref.shape
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite output"
+    mx, rel = errors(gpu, ref)
+    log(f"  {what}: max abs err {mx:.3e}, max rel err {rel:.3e}")
+    assert mx <= ATOL, f"{what}: max abs err {mx} > {ATOL}"
+    assert rel <= RTOL, f"{what}: max rel err {rel} > {RTOL}"

@@ -1,0 +1,139 @@
+"""Host-side checks of the C ABI (no GPU needed, no compute calls):
+the library loads and exports every symbol include/pkv.h declares, argument
+validation returns the documented codes, the split planner equals the
+oracle's plan exactly, and the invariant-divisor division is exact."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle.paged_attention as O
+import paged_kv_cache_08_amd as P
+from paged_kv_cache_08_amd import binding as Bn
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "pkv.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = P.lib()
+    names = declared_symbols()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(Bn.EXPORTED)
+
+
+def test_nm_shows_c_linkage():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", Bn.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\b(pkv_[a-z0-9_]+)\b", out))
+    assert set(declared_symbols()) <= exported
+
+
+def params(**kw):
+    p = P.DecodeParams()
+    base = dict(num_seqs=1, q_len=1, num_q_heads=24, num_kv_heads=4, head_dim=256, block_size=784,
+                max_pages_per_seq=42, max_seq_len=32768, num_pages=53, num_splits=0, total_tokens=0,
+                k_stride_page=784 * 4 * 256, k_stride_tok=4 * 256, k_stride_head=256,
+                v_stride_page=784 * 4 * 256, v_stride_tok=4 * 256, v_stride_head=256, scale=0.0625, out_dtype=0)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, 0),
+    ({"num_q_heads": 32, "num_kv_heads": 8, "head_dim": 128, "block_size": 16, "max_pages_per_seq": 2048,
+      "k_stride_page": 16 * 8 * 128, "k_stride_tok": 8 * 128, "k_stride_head": 128,
+      "v_stride_page": 16 * 8 * 128, "v_stride_tok": 8 * 128, "v_stride_head": 128}, 0),
+    ({"num_seqs": 0}, -1),
+    ({"num_q_heads": 25}, -1),
+    ({"head_dim": 64}, -2),
+    ({"head_dim": 512}, -2),
+    ({"num_q_heads": 36}, -2),           # group 9
+    ({"q_len": 17}, -2),
+    ({"q_len": 0}, -1),
+    ({"block_size": 0}, -1),
+    ({"max_seq_len": 42 * 784 + 1}, -1),
+    ({"max_seq_len": -1}, -1),
+    ({"k_stride_tok": 1020}, -1),        # not a multiple of 8 elements
+    ({"v_stride_head": 0}, -1),
+    ({"scale": float("nan")}, -1),
+    ({"out_dtype": 7}, -1),
+    ({"num_splits": -3}, -1),
+    ({"total_tokens": -1}, -1),
+])
+def test_validation_codes(kw, code):
+    assert P.validate(params(**kw)) == code
+
+
+def test_plan_constants_are_the_documented_ones():
+    assert P.plan_constants() == dict(tile=64, wg_per_cu=1, min_tiles=2, tbl_cap=2048)
+
+
+PLAN = [
+    dict(),
+    dict(block_size=16, max_pages_per_seq=2048),
+    dict(block_size=832, max_pages_per_seq=40),
+    dict(max_seq_len=512, block_size=16, max_pages_per_seq=32),
+    dict(num_seqs=16, max_seq_len=32000, total_tokens=121000, max_pages_per_seq=41),
+    dict(num_seqs=16, max_seq_len=32000, max_pages_per_seq=41),
+    dict(block_size=1, max_pages_per_seq=32768),
+    dict(block_size=3, max_pages_per_seq=20000),
+    dict(num_splits=1),
+    dict(num_splits=4),
+    dict(num_splits=64),
+    dict(num_splits=256),
+    dict(num_splits=100000),
+    dict(max_seq_len=0),
+    dict(max_seq_len=1),
+    dict(max_seq_len=65),
+    dict(num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, max_pages_per_seq=2048,
+         k_stride_page=16 * 8 * 128, k_stride_tok=8 * 128, k_stride_head=128,
+         v_stride_page=16 * 8 * 128, v_stride_tok=8 * 128, v_stride_head=128),
+]
+
+
+@pytest.mark.parametrize("kw", PLAN)
+@pytest.mark.parametrize("cu", [1, 80, 256, 304])
+def test_planner_matches_oracle_plan_exactly(kw, cu):
+    p = params(**kw)
+    got = P.plan_splits(p, cu)
+    ref = O.split_plan_ref(p.num_seqs, p.num_kv_heads, p.max_seq_len, p.block_size, cu,
+                           total_tokens=p.total_tokens, forced_splits=p.num_splits)
+    assert got == ref
+
+
+def test_workspace_holds_all_partials():
+    p = params()
+    S, _ = P.plan_splits(p, 256)
+    rows = p.num_seqs * p.q_len * p.num_q_heads
+    assert P.workspace_bytes(p, 256) >= 256 + rows * S * (p.head_dim + 2) * 4
+
+
+@pytest.mark.parametrize("d", list(range(1, 130)) + [784, 832, 1000, 1023, 1024, 4096, 65535, 1 << 20])
+def test_invariant_divisor_division_small_range(d):
+    assert P.magic_div_check(d, (1 << 18) - 1) == -1
+
+
+@pytest.mark.parametrize("d", [1, 3, 7, 16, 784, 832, 1000])
+def test_invariant_divisor_division_token_range(d):
+    # every token index below 2^24 (16.7M tokens)
+    assert P.magic_div_check(d, (1 << 24) - 1) == -1
+
+
+def test_invariant_divisor_division_all_divisors_to_1024():
+    for d in range(1, 1025):
+        assert P.magic_div_check(d, 1 << 16) == -1, d
+
+
+def test_bad_divisor_is_rejected():
+    assert P.magic_div_check(0, 10) == -2
