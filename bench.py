@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--repeats", type=int, default=5, help="extra timed regions for spread statistics")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
     return ap.parse_args()
 
 
@@ -172,9 +173,11 @@ def main():
                             total_tokens=total_tokens, num_splits=args.splits, stream=stream)
     out = call.out
 
-    def step(i):
-        k, v = pools[i % len(pools)]
-        call.run(k, v)
+    ptrs = [(k.data_ptr(), v.data_ptr()) for k, v in pools]
+
+    def step(i, c=call):
+        kp, vp = ptrs[i % len(ptrs)]
+        c.run_ptrs(kp, vp)
 
     hip = Hip()
     for i in range(args.warmup):
@@ -218,6 +221,34 @@ def main():
         hip.destroy(a)
         hip.destroy(b)
     kern_avg_us = sum(kern_us) / len(kern_us)
+
+    # The same K steps captured once in a HIP graph and replayed (launch overhead removed).
+    graph_us = None
+    if not args.no_graph:
+        gstream = torch.cuda.Stream(dev)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(gstream):
+            gcall = P.PreparedDecode(q, k0, v0, table, lens, case.block_size, case.scale,
+                                     max_seq_len=case.max_seq_len, total_tokens=total_tokens,
+                                     num_splits=args.splits, out=out, workspace=call.workspace,
+                                     stream=gstream.cuda_stream)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=gstream):
+            for i in range(args.steps):
+                step(i, gcall)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        rs = torch.cuda.current_stream(dev).cuda_stream
+        graph_regions = []
+        for _ in range(max(1, args.repeats)):
+            hip.record(ev0, rs)
+            graph.replay()
+            hip.record(ev1, rs)
+            torch.cuda.synchronize()
+            graph_regions.append(hip.elapsed_ms(ev0, ev1) / args.steps * 1e3)
+        graph_us = statistics.median(graph_regions)
+        del graph
 
     # Spot parity on sampled heads of the timed output (pool 0 holds the seeded input).
     step(0)
@@ -281,6 +312,8 @@ def main():
             "kernel_us_avg": round(kern_avg_us, 2),
             "kernel_us_min": round(min(kern_us), 2),
         },
+        "graph_us_per_step": None if graph_us is None else round(graph_us, 2),
+        "graph_gbs": None if graph_us is None else round(kv_bytes / (graph_us * 1e-6) / 1e9, 1),
         "cpu_baseline": cpu,
         "parity_max_abs_err": parity,
     }

@@ -84,7 +84,8 @@ const char* pkv_strerror(int code);
 const char* pkv_last_error(void);
 
 /* Host-only check of *p (no HIP call): sizes, group size, head_dim, q_len,
- * strides (positive, multiples of 8 so every K/V row starts on 16 bytes),
+ * strides (positive, multiples of 8 so every K/V row starts on 16 bytes;
+ * block_size * token stride below 2^31 elements, else PKV_ERR_UNSUPPORTED),
  * max_seq_len <= max_pages_per_seq * block_size. Returns PKV_OK or an error. */
 int pkv_validate_params(const pkv_decode_params* p);
 

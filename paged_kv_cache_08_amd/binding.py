@@ -286,6 +286,13 @@ class PreparedDecode:
                        workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
         self._k, self._v = k_cache.data_ptr(), v_cache.data_ptr()
 
+    def run_ptrs(self, k_ptr: int, v_ptr: int) -> None:
+        """Like run() with raw device pointers of a pool laid out like the original."""
+        qp, tp, lp, op, wp, wn, st = self._fixed
+        rc = self._fn(self._pp, qp, k_ptr, v_ptr, tp, lp, op, wp, wn, st)
+        if rc != PKV_OK:
+            check(rc, "pkv_paged_decode_attention")
+
     def run(self, k_cache=None, v_cache=None):
         kp, vp = self._k, self._v
         if k_cache is not None:

@@ -14,7 +14,11 @@
 namespace {
 
 thread_local std::string g_last_error;
-thread_local std::string g_last_variant;
+struct VariantInfo {
+  const char* split_name = nullptr;
+  int head_dim = 0, group = 0, q_len = 0, splits = 0, chunk = 0, block_size = 0;
+};
+thread_local VariantInfo g_last_variant;
 thread_local hipEvent_t g_ev_start = nullptr;
 thread_local hipEvent_t g_ev_stop = nullptr;
 
@@ -146,6 +150,9 @@ int pkv_validate_params(const pkv_decode_params* p) {
   if (!mult8_pos(p->k_stride_page) || !mult8_pos(p->k_stride_tok) || !mult8_pos(p->k_stride_head) ||
       !mult8_pos(p->v_stride_page) || !mult8_pos(p->v_stride_tok) || !mult8_pos(p->v_stride_head))
     return fail(PKV_ERR_INVALID, "K/V strides must be positive multiples of 8 elements");
+  if (int64_t(p->block_size) * p->k_stride_tok >= (int64_t(1) << 31) ||
+      int64_t(p->block_size) * p->v_stride_tok >= (int64_t(1) << 31))
+    return fail(PKV_ERR_UNSUPPORTED, "block_size * token stride must stay below 2^31 elements");
   if (!isfinite(p->scale)) return fail(PKV_ERR_INVALID, "scale is not finite");
   if (p->out_dtype != PKV_OUT_F32 && p->out_dtype != PKV_OUT_BF16)
     return fail(PKV_ERR_INVALID, "unknown out_dtype");
@@ -235,19 +242,22 @@ int pkv_paged_decode_attention(const pkv_decode_params* p, const void* q, const 
     e = pkv::launch_lse_merge(a, p->head_dim, st);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
   }
-  char buf[256];
-  snprintf(buf, sizeof buf, "%s d%d g%d q%d%s splits=%d chunk=%d B=%d", split_name, p->head_dim, group,
-           p->q_len, S > 1 ? " + lse_merge" : "", S, chunk, p->block_size);
-  g_last_variant = buf;
-  g_last_error.clear();
+  g_last_variant = VariantInfo{split_name, p->head_dim, group, p->q_len, S, chunk, p->block_size};
   return PKV_OK;
 }
 
 int pkv_last_variant(char* buf, int32_t len) {
-  const int n = int(g_last_variant.size());
+  const VariantInfo& v = g_last_variant;
+  char tmp[256];
+  int n = 0;
+  if (v.split_name)
+    n = snprintf(tmp, sizeof tmp, "%s d%d g%d q%d%s splits=%d chunk=%d B=%d", v.split_name, v.head_dim, v.group,
+                 v.q_len, v.splits > 1 ? " + lse_merge" : "", v.splits, v.chunk, v.block_size);
+  else
+    tmp[0] = '\0';
   if (buf && len > 0) {
     const int c = n < len - 1 ? n : len - 1;
-    memcpy(buf, g_last_variant.data(), size_t(c));
+    memcpy(buf, tmp, size_t(c));
     buf[c] = '\0';
   }
   return n;

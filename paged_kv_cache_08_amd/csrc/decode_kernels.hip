@@ -10,19 +10,27 @@
 // paragraph of "vLLM 下双卡 Radeon 上的混合 SSM 解码速率".
 //
 // Work mapping (one workgroup = one split of one (sequence, KV head)):
-//   * 4 waves x 4 token rows per wave: 16 consecutive logical tokens per
-//     sub-step, one token row per 16-lane DPP row.
+//   * 8 waves (2 per SIMD) x 4 token rows per wave: 32 consecutive logical
+//     tokens per sub-step, one token row per 16-lane DPP row.
+//   * Each wave keeps a ring of 4 sub-steps of K/V in registers: the loads of
+//     3 sub-steps are in flight while one is consumed.
 //   * Each lane owns D/16 head-dim elements of its token row and loads them
 //     with 16-byte global loads (a 512-byte K row of D=256 is read by 16 lanes
 //     in two fully used 256-byte segments).
 //   * The G query heads of the GQA group all use the row held in registers, so
 //     K and V are fetched once per group.
 //   * q.k partial sums are reduced across the 16 lanes of a row with four DPP
-//     butterfly adds (quad_perm, row_half_mirror, row_mirror); all lanes end up
-//     with the same bits.
-//   * Online softmax in log2 units, per token row, with a lazy reference max:
-//     the accumulators are rescaled only when a score exceeds the reference by
-//     more than 2^8, so probabilities stay <= 256 and rescales are rare.
+//     butterfly adds (quad_perm, row_half_mirror, row_mirror), interleaved
+//     across the G heads; all lanes end up with the same bits.
+//   * Online softmax in log2 units with a lazy reference max: lane h of a row
+//     keeps the state of head h, so each exponential is computed once per
+//     (token, head), and p is broadcast to the row with DPP row_newbcast. The
+//     accumulators are rescaled only when a score exceeds the reference by more
+//     than 2^8 (probabilities stay <= 256; rescales are rare). The reference
+//     starts at a finite floor, so rows that see no token need no select.
+//   * Page offsets (page * page_stride + head * head_stride, for K and V) are
+//     staged in LDS once per split; a token then costs one division by the
+//     page size (multiply-high), one LDS read and a 32-bit multiply-add.
 //   * Token rows, then waves, are merged in a fixed order; the split's
 //     (reference max, sum, accumulator) go to the workspace, or the normalised
 //     output directly when the sequence has a single split.
@@ -38,13 +46,15 @@ namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;                      // 2 waves per SIMD
 constexpr int kThreads = 64 * kWaves;
 constexpr int kLanesPerRow = 16;
 constexpr int kRowsPerWave = 64 / kLanesPerRow;
 constexpr int kStep = kWaves * kRowsPerWave;   // tokens per workgroup sub-step
-constexpr int kSub = 2;                        // sub-steps per pipeline stage
+constexpr int kRing = 4;                       // register ring depth (sub-steps)
 constexpr float kLazy = 8.0f;                  // log2 headroom before a rescale
+constexpr float kMinit = -1.0e30f;             // initial reference max (finite)
+constexpr int kMergeSplitsLds = 1024;          // splits whose weights the merge keeps in LDS
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -57,15 +67,6 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_move(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
                                                                CTRL, 0xF, 0xF, false));
-}
-
-// Sum over the 16 lanes of a DPP row; every lane of the row gets the same bits.
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp_move<0xB1>(x);    // quad_perm [1,0,3,2]
-  x += dpp_move<0x4E>(x);    // quad_perm [2,3,0,1]
-  x += dpp_move<0x141>(x);   // row_half_mirror
-  x += dpp_move<0x140>(x);   // row_mirror
-  return x;
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -109,42 +110,75 @@ __device__ __forceinline__ SplitSpan split_span(const DecodeArgs& a, int b, int 
   return r;
 }
 
-// Stage block-table entries [p_first, p_first + n) of sequence b in LDS.
-// Entries outside [0, num_pages) become -1 (their tokens are skipped) and set
-// bit 0 of the workspace error word.
-__device__ __forceinline__ void stage_table(const DecodeArgs& a, int b, int p_first, int n, int* tbl) {
+// Element offsets of one physical page's first row for KV head g, for K and
+// for V; k < 0 marks a table entry that is skipped.
+struct PageOffs {
+  int64_t k;
+  int64_t v;
+};
+
+// Stage block-table entries [p_first, p_first + n) of sequence b in LDS as
+// page offsets of KV head g. Entries outside [0, num_pages) are marked invalid
+// (their tokens are skipped) and set bit 0 of the workspace error word.
+__device__ __forceinline__ void stage_table(const DecodeArgs& a, int b, int g, int p_first, int n,
+                                            PageOffs* tbl) {
   const int32_t* row = a.table + int64_t(b) * a.max_pages + p_first;
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    int e = row[i];
+    const int e = row[i];
+    PageOffs po;
     if (uint32_t(e) >= uint32_t(a.num_pages)) {
       if (a.err) atomicOr(a.err, 1u);
-      e = -1;
+      po.k = -1;
+      po.v = -1;
+    } else {
+      po.k = int64_t(e) * a.k_sp + int64_t(g) * a.k_sh;
+      po.v = int64_t(e) * a.v_sp + int64_t(g) * a.v_sh;
     }
-    tbl[i] = e;
+    tbl[i] = po;
   }
 }
 
-// Element offsets of token t's K and V rows of KV head g; false if its page
-// entry is invalid.
-__device__ __forceinline__ bool token_row(const DecodeArgs& a, const int* tbl, int p_first, int t,
-                                          int g, int64_t& ko, int64_t& vo) {
+// Element offsets of token t's K and V rows; false if its page entry is
+// invalid. The in-page part off * stride_tok fits 32 bits (checked on the host).
+__device__ __forceinline__ bool token_row(const DecodeArgs& a, const PageOffs* tbl, int p_first, int t,
+                                          int64_t& ko, int64_t& vo) {
   const uint32_t pg = magic_div(uint32_t(t), a.bdiv);
   const int off = t - int(pg * a.bdiv.d);
-  const int phys = tbl[int(pg) - p_first];
-  ko = int64_t(phys) * a.k_sp + int64_t(off) * a.k_st + int64_t(g) * a.k_sh;
-  vo = int64_t(phys) * a.v_sp + int64_t(off) * a.v_st + int64_t(g) * a.v_sh;
-  return phys >= 0;
+  const PageOffs po = tbl[int(pg) - p_first];
+  ko = po.k + int64_t(off * int32_t(a.k_st));
+  vo = po.v + int64_t(off * int32_t(a.v_st));
+  return po.k >= 0;
+}
+
+// Lane n of each 16-lane row, broadcast to the whole row (DPP row_newbcast).
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+  return dpp_move<0x150 + N>(x);
+}
+
+template <int G>
+__device__ __forceinline__ void row_bcast_all(float x, float (&out)[G]) {
+  if constexpr (G > 0) out[0] = row_bcast<0>(x);
+  if constexpr (G > 1) out[1] = row_bcast<1>(x);
+  if constexpr (G > 2) out[2] = row_bcast<2>(x);
+  if constexpr (G > 3) out[3] = row_bcast<3>(x);
+  if constexpr (G > 4) out[4] = row_bcast<4>(x);
+  if constexpr (G > 5) out[5] = row_bcast<5>(x);
+  if constexpr (G > 6) out[6] = row_bcast<6>(x);
+  if constexpr (G > 7) out[7] = row_bcast<7>(x);
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a) {
   constexpr int kEpl = D / kLanesPerRow;   // head-dim elements per lane: 16 or 8
   constexpr int kCpl = kEpl / 8;           // 16-byte chunks per lane: 2 or 1
   static_assert(kCpl >= 1 && kEpl % 8 == 0, "head_dim must be a multiple of 128");
 
-  __shared__ int tbl[kTblCap];
+  __shared__ PageOffs tbl[kTblCap];
   __shared__ float mrg_acc[kWaves][G][D];
   __shared__ float mrg_ml[kWaves][G][2];
+  __shared__ float mrg_w[kWaves][G];
+  __shared__ float mrg_den[G];
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
@@ -158,7 +192,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   }
   const int p_first = int(magic_div(uint32_t(sp.begin), a.bdiv));
   const int p_last = int(magic_div(uint32_t(sp.end - 1), a.bdiv));
-  stage_table(a, b, p_first, p_last - p_first + 1, tbl);
+  stage_table(a, b, g, p_first, p_last - p_first + 1, tbl);
 
   const int lane = tid & 63, wave = tid >> 6;
   const int row = lane >> 4, col = lane & 15;
@@ -175,117 +209,140 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
   }
   __syncthreads();
 
-  float m[G], l[G], acc[G][kEpl];
+  // Accumulators of this lane's token row (its D/16 elements of each head).
+  float acc[G][kEpl];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.0f;
+  for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < kEpl; ++e) acc[h][e] = 0.0f;
-  }
+  // Softmax state of head `col` of this row, kept by lane col (< G) only, so each
+  // exponential is computed once per (token, head). The reference max starts at
+  // a finite floor: a row that sees no token keeps p = 2^(-inf) = 0.
+  float m_l = kMinit, l_l = 0.0f;
 
-  const int my = wave * kRowsPerWave + row;   // token of this row within a sub-step
+  const int my = wave * kRowsPerWave + row;   // this row's token within a sub-step
 
-  auto fetch = [&](int base, uint4 (&kk)[kSub][kCpl], uint4 (&vv)[kSub][kCpl], bool (&ok)[kSub]) {
+  // Issue the 16-byte K and V loads of one sub-step (token t0 + my). The loads
+  // are unconditional: a row past the split end, or whose page entry is
+  // invalid, reads the (finite, in-bounds) q row instead and is masked.
+  const uint16_t* const safe_row = a.q + out_row0 + col * 8;
+  auto fetch = [&](int t0, uint4 (&kk)[kCpl], uint4 (&vv)[kCpl], bool& ok) {
+    const int t = t0 + my;
+    const int tc = min(t, sp.end - 1);
+    int64_t ko, vo;
+    const bool has_page = token_row(a, tbl, p_first, tc, ko, vo);
+    ok = (t < sp.end) && has_page;
+    const uint16_t* kp = ok ? a.k + ko + col * 8 : safe_row;
+    const uint16_t* vp = ok ? a.v + vo + col * 8 : safe_row;
 #pragma unroll
-    for (int u = 0; u < kSub; ++u) {
-      const int t = base + u * kStep + my;
-      int64_t ko = 0, vo = 0;
-      bool valid = t < sp.end;
-      if (valid) valid = token_row(a, tbl, p_first, t, g, ko, vo);
-      ok[u] = valid;
-#pragma unroll
-      for (int k = 0; k < kCpl; ++k) {
-        kk[u][k] = make_uint4(0, 0, 0, 0);
-        vv[u][k] = make_uint4(0, 0, 0, 0);
-      }
-      if (valid) {
-        const uint16_t* kp = a.k + ko + col * 8;
-        const uint16_t* vp = a.v + vo + col * 8;
-#pragma unroll
-        for (int k = 0; k < kCpl; ++k) {
-          kk[u][k] = *reinterpret_cast<const uint4*>(kp + k * 128);
-          vv[u][k] = *reinterpret_cast<const uint4*>(vp + k * 128);
-        }
-      }
+    for (int k = 0; k < kCpl; ++k) {
+      kk[k] = *reinterpret_cast<const uint4*>(kp + k * 128);
+      vv[k] = *reinterpret_cast<const uint4*>(vp + k * 128);
     }
   };
 
-  auto consume = [&](const uint4 (&kk)[kSub][kCpl], const uint4 (&vv)[kSub][kCpl], const bool (&ok)[kSub]) {
-    float sc[kSub][G];
-#pragma unroll
-    for (int u = 0; u < kSub; ++u)
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float d0 = 0.0f;
-#pragma unroll
-        for (int k = 0; k < kCpl; ++k) {
-          d0 = dot2_bf16(qv[h][k].x, kk[u][k].x, d0);
-          d0 = dot2_bf16(qv[h][k].y, kk[u][k].y, d0);
-          d0 = dot2_bf16(qv[h][k].z, kk[u][k].z, d0);
-          d0 = dot2_bf16(qv[h][k].w, kk[u][k].w, d0);
-        }
-        const float r = row16_sum(d0) * a.scale_log2;
-        sc[u][h] = ok[u] ? r : -INFINITY;
-      }
-    float p[kSub][G];
+  // One token per row: q.k of the G heads (DPP butterflies interleaved across
+  // heads), the softmax update of head `col` in lane col, p broadcast to the
+  // row, then V accumulation.
+  auto consume = [&](const uint4 (&kk)[kCpl], const uint4 (&vv)[kCpl], bool ok) {
+    float dq[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float mx = sc[0][h];
-#pragma unroll
-      for (int u = 1; u < kSub; ++u) mx = fmaxf(mx, sc[u][h]);
-      if (mx > m[h] + kLazy) {
-        const float al = fast_exp2(m[h] - mx);
-        l[h] *= al;
-#pragma unroll
-        for (int e = 0; e < kEpl; ++e) acc[h][e] *= al;
-        m[h] = mx;
-      }
-#pragma unroll
-      for (int u = 0; u < kSub; ++u) {
-        p[u][h] = ok[u] ? fast_exp2(sc[u][h] - m[h]) : 0.0f;
-        l[h] += p[u][h];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kSub; ++u)
+      float d0 = 0.0f;
 #pragma unroll
       for (int k = 0; k < kCpl; ++k) {
-        const uint32_t w4[4] = {vv[u][k].x, vv[u][k].y, vv[u][k].z, vv[u][k].w};
+        d0 = dot2_bf16(qv[h][k].x, kk[k].x, d0);
+        d0 = dot2_bf16(qv[h][k].y, kk[k].y, d0);
+        d0 = dot2_bf16(qv[h][k].z, kk[k].z, d0);
+        d0 = dot2_bf16(qv[h][k].w, kk[k].w, d0);
+      }
+      dq[h] = d0;
+    }
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float v0 = bf16_lo(w4[w]), v1 = bf16_hi(w4[w]);
-          const int e = k * 8 + w * 2;
+    for (int h = 0; h < G; ++h) dq[h] += dpp_move<0xB1>(dq[h]);    // quad_perm [1,0,3,2]
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            acc[h][e] = fmaf(p[u][h], v0, acc[h][e]);
-            acc[h][e + 1] = fmaf(p[u][h], v1, acc[h][e + 1]);
-          }
+    for (int h = 0; h < G; ++h) dq[h] += dpp_move<0x4E>(dq[h]);    // quad_perm [2,3,0,1]
+#pragma unroll
+    for (int h = 0; h < G; ++h) dq[h] += dpp_move<0x141>(dq[h]);   // row_half_mirror
+#pragma unroll
+    for (int h = 0; h < G; ++h) dq[h] += dpp_move<0x140>(dq[h]);   // row_mirror
+    float mine = dq[0];
+#pragma unroll
+    for (int h = 1; h < G; ++h) mine = (col == h) ? dq[h] : mine;
+    const float sc = ok ? mine * a.scale_log2 : -INFINITY;
+    const bool resc = sc > m_l + kLazy;
+    if (__builtin_amdgcn_ballot_w64(resc) != 0) {   // wave-uniform; rare after the first tokens
+      const float al = resc ? fast_exp2(m_l - sc) : 1.0f;
+      m_l = resc ? sc : m_l;
+      l_l *= al;
+      float ah[G];
+      row_bcast_all<G>(al, ah);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < kEpl; ++e) acc[h][e] *= ah[h];
+    }
+    const float pl = fast_exp2(sc - m_l);
+    l_l += pl;
+    float p[G];
+    row_bcast_all<G>(pl, p);
+#pragma unroll
+    for (int k = 0; k < kCpl; ++k) {
+      const uint32_t w4[4] = {vv[k].x, vv[k].y, vv[k].z, vv[k].w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float v0 = bf16_lo(w4[w]), v1 = bf16_hi(w4[w]);
+        const int e = k * 8 + w * 2;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          acc[h][e] = fmaf(p[h], v0, acc[h][e]);
+          acc[h][e + 1] = fmaf(p[h], v1, acc[h][e + 1]);
         }
       }
+    }
   };
 
-  uint4 kA[kSub][kCpl], vA[kSub][kCpl], kB[kSub][kCpl], vB[kSub][kCpl];
-  bool okA[kSub], okB[kSub];
-  int base = sp.begin;
-  fetch(base, kA, vA, okA);
-  while (true) {
-    fetch(base + kSub * kStep, kB, vB, okB);
-    consume(kA, vA, okA);
-    base += kSub * kStep;
-    if (base >= sp.end) break;
-    fetch(base + kSub * kStep, kA, vA, okA);
-    consume(kB, vB, okB);
-    base += kSub * kStep;
-    if (base >= sp.end) break;
+  // Register ring of 4 sub-steps (named buffers, so each stays in fixed
+  // registers): the loads of 3 sub-steps are in flight while one is consumed.
+  // The main loop runs whole groups of 4 sub-steps and has a single exit; the
+  // 0-3 sub-steps left over are already in flight when it ends.
+  static_assert(kRing == 4, "the ring below is written out for 4 buffers");
+  uint4 k0[kCpl], v0[kCpl], k1[kCpl], v1[kCpl], k2[kCpl], v2[kCpl], k3[kCpl], v3[kCpl];
+  bool ok0, ok1, ok2, ok3;
+  const int n_sub = (sp.end - sp.begin + kStep - 1) / kStep;
+  const int n_groups = n_sub >> 2;
+  const int rem = n_sub & 3;
+  int t_fetch = sp.begin;
+  fetch(t_fetch, k0, v0, ok0);
+  fetch(t_fetch + kStep, k1, v1, ok1);
+  fetch(t_fetch + 2 * kStep, k2, v2, ok2);
+  t_fetch += 3 * kStep;
+  for (int it = 0; it < n_groups; ++it) {
+    fetch(t_fetch, k3, v3, ok3);
+    consume(k0, v0, ok0);
+    fetch(t_fetch + kStep, k0, v0, ok0);
+    consume(k1, v1, ok1);
+    fetch(t_fetch + 2 * kStep, k1, v1, ok1);
+    consume(k2, v2, ok2);
+    fetch(t_fetch + 3 * kStep, k2, v2, ok2);
+    consume(k3, v3, ok3);
+    t_fetch += 4 * kStep;
   }
+  if (rem > 0) consume(k0, v0, ok0);
+  if (rem > 1) consume(k1, v1, ok1);
+  if (rem > 2) consume(k2, v2, ok2);
+
+  // Row state per head, from lane h of each row.
+  float m[G], l[G];
+  row_bcast_all<G>(m_l, m);
+  row_bcast_all<G>(l_l, l);
 
   // Merge the 4 token rows of each wave (fixed butterfly order).
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float M = fmaxf(m[h], __shfl_xor(m[h], 16));
     M = fmaxf(M, __shfl_xor(M, 32));
-    const float w = (m[h] == -INFINITY) ? 0.0f : fast_exp2(m[h] - M);
+    const float w = fast_exp2(m[h] - M);
     float lw = l[h] * w;
     lw += __shfl_xor(lw, 16);
     lw += __shfl_xor(lw, 32);
@@ -314,80 +371,175 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeArgs a)
       }
   }
   __syncthreads();
+  // Per-head merge weights of the waves, once.
+  float M_h = 0.0f;
+  if (tid < G) {
+    const int h = tid;
+    float M = mrg_ml[0][h][0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mrg_ml[w][h][0]);
+    float den = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = fast_exp2(mrg_ml[w][h][0] - M);
+      mrg_w[w][h] = f;
+      den += f * mrg_ml[w][h][1];
+    }
+    mrg_den[h] = den;
+    M_h = M;
+  }
+  __syncthreads();
 
   // Merge the waves (fixed order) and write the split's result.
   const int64_t prow0 = int64_t(b) * a.q_len * a.hq + int64_t(g) * G;   // partial row of head 0, query row 0
   for (int i = tid; i < G * D; i += kThreads) {
     const int h = i / D, d = i - h * D;
-    float M = mrg_ml[0][h][0];
+    float num = 0.0f;
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mrg_ml[w][h][0]);
-    float num = 0.0f, den = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = mrg_ml[w][h][0];
-      const float f = (mw == -INFINITY) ? 0.0f : fast_exp2(mw - M);
-      num += f * mrg_acc[w][h][d];
-      den += f * mrg_ml[w][h][1];
-    }
+    for (int w = 0; w < kWaves; ++w) num += mrg_w[w][h] * mrg_acc[w][h][d];
+    const float den = mrg_den[h];
     if (sp.nsplit == 1) {
       store_out(a, out_row0 + i, den > 0.0f ? num / den : 0.0f);
     } else {
-      const int64_t pr = (prow0 + h) * a.num_splits + s;
-      a.part_acc[pr * D + d] = num;
-      if (d == 0) {
-        a.part_ml[pr * 2] = M;
-        a.part_ml[pr * 2 + 1] = den;
-      }
+      a.part_acc[((prow0 + h) * a.num_splits + s) * D + d] = num;
     }
+  }
+  if (sp.nsplit > 1 && tid < G) {
+    const int64_t pr = (prow0 + tid) * a.num_splits + s;
+    a.part_ml[pr * 2] = M_h;
+    a.part_ml[pr * 2 + 1] = mrg_den[tid];
   }
 }
 
+// Block-wide reductions over the 256 threads of a merge workgroup.
+__device__ __forceinline__ float block_max256(float x, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__device__ __forceinline__ float block_sum256(float x, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
 // out[b,i,h,:] = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s over the
-// sequence's splits, M = max_s m_s; splits with no visible token carry
-// m = -inf and weigh nothing. One workgroup per (query head, query row, seq).
+// sequence's splits with l_s > 0, M = max of their m_s; a row with no such
+// split gets zeros. Workgroup = (64-column block, query head, query row x
+// sequence), 4 waves; wave w sums splits w, w + 4, .... The accumulator and
+// (m, l) loads are all issued first; the per-split weights 2^(m_s - M) / den
+// are computed once into LDS. All sums run in a fixed order.
 template <int D>
-__global__ __launch_bounds__(D) void lse_merge_kernel(DecodeArgs a) {
-  const int h = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
-  const int d = threadIdx.x;
+__global__ __launch_bounds__(256) void lse_merge_kernel(DecodeArgs a) {
+  constexpr int kPerWave = 16;    // accumulator loads in flight per thread per pass
+  constexpr int kPass = 4 * kPerWave;
+  __shared__ float sm_m[kMergeSplitsLds];
+  __shared__ float sm_w[kMergeSplitsLds];
+  __shared__ float red[4];
+  __shared__ float part[4][64];
+  const int cb = blockIdx.x, h = blockIdx.y;
+  const int i = blockIdx.z % a.q_len, b = blockIdx.z / a.q_len;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int d = cb * 64 + lane;
   const SplitSpan sp = split_span(a, b, 0);
   if (sp.nsplit <= 1) return;    // written by the split kernel
+  const int ns = sp.nsplit;
   const int64_t prow = (int64_t(b) * a.q_len + i) * a.hq + h;
   const float* ml = a.part_ml + prow * a.num_splits * 2;
   const float* ac = a.part_acc + prow * a.num_splits * D;
-  const int64_t oidx = prow * D + d;
-  float M = -INFINITY;
-  for (int s = 0; s < sp.nsplit; ++s) M = fmaxf(M, ml[2 * s]);
+
+  float vals[kPerWave];
+#pragma unroll
+  for (int j = 0; j < kPerWave; ++j) {
+    const int sidx = wave + 4 * j;
+    vals[j] = sidx < ns ? ac[int64_t(sidx) * D + d] : 0.0f;
+  }
+  // (m, l) of every split; a split with l = 0 (no visible token) gets m = -inf.
+  float mloc = -INFINITY;
+  for (int t = tid; t < ns; t += 256) {
+    const float2 v = reinterpret_cast<const float2*>(ml)[t];
+    const float mv = v.y > 0.0f ? v.x : -INFINITY;
+    if (t < kMergeSplitsLds) {
+      sm_m[t] = mv;
+      sm_w[t] = v.y;
+    }
+    mloc = fmaxf(mloc, mv);
+  }
+  const float M = block_max256(mloc, red);
   if (M == -INFINITY) {
-    store_out(a, oidx, 0.0f);
+    if (wave == 0) store_out(a, prow * D + d, 0.0f);
     return;
   }
-  float num = 0.0f, den = 0.0f;
-  for (int s = 0; s < sp.nsplit; ++s) {
-    const float ms = ml[2 * s];
-    const float f = (ms == -INFINITY) ? 0.0f : fast_exp2(ms - M);
-    den += f * ml[2 * s + 1];
-    num += f * ac[int64_t(s) * D + d];
+  float dloc = 0.0f;
+  for (int t = tid; t < ns; t += 256) {
+    float mv, lv;
+    if (t < kMergeSplitsLds) {
+      mv = sm_m[t];
+      lv = sm_w[t];
+    } else {
+      const float2 v = reinterpret_cast<const float2*>(ml)[t];
+      mv = v.y > 0.0f ? v.x : -INFINITY;
+      lv = v.y;
+    }
+    const float f = fast_exp2(mv - M);    // 0 for empty splits
+    dloc += f * lv;
+    if (t < kMergeSplitsLds) sm_w[t] = f;
   }
-  store_out(a, oidx, den > 0.0f ? num / den : 0.0f);
+  const float inv_den = 1.0f / block_sum256(dloc, red);   // barrier inside: sm_w is complete
+
+  float num = 0.0f;
+  for (int s0 = 0; s0 < ns; s0 += kPass) {
+    if (s0 > 0) {
+#pragma unroll
+      for (int j = 0; j < kPerWave; ++j) {
+        const int sidx = s0 + wave + 4 * j;
+        vals[j] = sidx < ns ? ac[int64_t(sidx) * D + d] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j) {
+      const int sidx = s0 + wave + 4 * j;
+      if (sidx < ns) {
+        float f;
+        if (sidx < kMergeSplitsLds) {
+          f = sm_w[sidx];
+        } else {
+          const float2 v = reinterpret_cast<const float2*>(ml)[sidx];
+          f = v.y > 0.0f ? fast_exp2(v.x - M) : 0.0f;
+        }
+        num += f * vals[j];
+      }
+    }
+  }
+  part[wave][lane] = num;
+  __syncthreads();
+  if (wave == 0)
+    store_out(a, prow * D + d, ((part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane])) * inv_den);
 }
 
 // Debug: offsets of every live token row, through the same split range,
 // table staging and token_row() the split kernel uses.
 __global__ __launch_bounds__(kThreads) void debug_offsets_kernel(DecodeArgs a, int g, int max_seq_len,
                                                                  int64_t* k_off, int64_t* v_off) {
-  __shared__ int tbl[kTblCap];
+  __shared__ PageOffs tbl[kTblCap];
   const int s = blockIdx.x, b = blockIdx.y;
   const SplitSpan sp = split_span(a, b, s);
   if (sp.begin >= sp.L) return;
   const int p_first = int(magic_div(uint32_t(sp.begin), a.bdiv));
   const int p_last = int(magic_div(uint32_t(sp.end - 1), a.bdiv));
-  stage_table(a, b, p_first, p_last - p_first + 1, tbl);
+  stage_table(a, b, g, p_first, p_last - p_first + 1, tbl);
   __syncthreads();
   const int t_end = min(sp.end, max_seq_len);
   for (int t = sp.begin + threadIdx.x; t < t_end; t += kThreads) {
     int64_t ko, vo;
-    const bool ok = token_row(a, tbl, p_first, t, g, ko, vo);
+    const bool ok = token_row(a, tbl, p_first, t, ko, vo);
     k_off[int64_t(b) * max_seq_len + t] = ok ? ko : -2;
     v_off[int64_t(b) * max_seq_len + t] = ok ? vo : -2;
   }
@@ -439,11 +591,11 @@ hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int group, hip
 }
 
 hipError_t launch_lse_merge(const DecodeArgs& a, int head_dim, hipStream_t st) {
-  dim3 grid(a.hq, a.q_len, a.num_seqs);
+  dim3 grid(head_dim / 64, a.hq, a.q_len * a.num_seqs);
   if (head_dim == 256)
     hipLaunchKernelGGL(lse_merge_kernel<256>, grid, dim3(256), 0, st, a);
   else if (head_dim == 128)
-    hipLaunchKernelGGL(lse_merge_kernel<128>, grid, dim3(128), 0, st, a);
+    hipLaunchKernelGGL(lse_merge_kernel<128>, grid, dim3(256), 0, st, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
