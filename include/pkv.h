@@ -85,7 +85,8 @@ const char* pkv_last_error(void);
 
 /* Host-only check of *p (no HIP call): sizes, group size, head_dim, q_len,
  * strides (positive, multiples of 8 so every K/V row starts on 16 bytes;
- * block_size * token stride below 2^31 elements, else PKV_ERR_UNSUPPORTED),
+ * block_size <= 2^20 and block_size * token stride below 2^31 elements, else
+ * PKV_ERR_UNSUPPORTED),
  * max_seq_len <= max_pages_per_seq * block_size. Returns PKV_OK or an error. */
 int pkv_validate_params(const pkv_decode_params* p);
 
@@ -94,16 +95,18 @@ int pkv_validate_params(const pkv_decode_params* p);
  *   work    = total_tokens, or num_seqs * max_seq_len when total_tokens == 0;
  *   c       = max(min_tiles, ceil(Hkv * work / (cu_count * wg_per_cu * T))),
  *             or ceil(n_tiles / num_splits) when num_splits > 0;
- *   c       = clamp(c, 1, min(n_tiles, floor((tbl_cap - 2) * block_size / T)));
+ *   c       = clamp(c, 1, min(n_tiles, max_tiles));
  *   *num_splits = ceil(n_tiles / c); *chunk_tokens = c * T.
  * Sequence b then uses ceil(L_b / chunk) splits; split s covers tokens
- * [s * chunk, min((s + 1) * chunk, L_b)). cu_count must be >= 1. */
+ * [s * chunk, min((s + 1) * chunk, L_b)). A split never exceeds max_tiles * T
+ * tokens (one unrolled window of the split kernel), so a requested num_splits
+ * may be raised. cu_count must be >= 1. */
 int pkv_plan_splits(const pkv_decode_params* p, int32_t cu_count,
                     int32_t* num_splits, int32_t* chunk_tokens);
 
-/* The planner's constants: tile T, workgroups per CU, minimum tiles per split,
- * block-table entries a split may span. Any pointer may be NULL. */
-int pkv_plan_constants(int32_t* tile, int32_t* wg_per_cu, int32_t* min_tiles, int32_t* tbl_cap);
+/* The planner's constants: tile T, workgroups per CU, minimum and maximum
+ * tiles per split. Any pointer may be NULL. */
+int pkv_plan_constants(int32_t* tile, int32_t* wg_per_cu, int32_t* min_tiles, int32_t* max_tiles);
 
 /* Bytes of device workspace a call with *p needs when planned for cu_count
  * CUs (cu_count <= 0: the current device's CU count, which initialises HIP).

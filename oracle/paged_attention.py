@@ -212,11 +212,10 @@ def split_attention_ref(q, k_cache, v_cache, block_table, seq_lens, block_size: 
 #   T          tile of logical tokens; split boundaries are multiples of T
 #   n_tiles    = ceil(max_seq_len / T)
 #   work       = total_tokens if given, else num_seqs * max_seq_len
-#   c (tiles)  = ceil(Hkv * work / (cu_count * wg_per_cu * T)), at least min_tiles,
-#                at most n_tiles, and at most floor((tbl_cap - 2) * B / T) (>= 1)
-#                so a split's block-table entries fit the kernel's table cache;
-#                a forced split count S_f instead gives c = ceil(n_tiles / S_f)
-#                (then the same two upper bounds)
+#   c (tiles)  = ceil(Hkv * work / (cu_count * wg_per_cu * T)), at least min_tiles;
+#                a forced split count S_f instead gives c = ceil(n_tiles / S_f);
+#                then at most n_tiles and at most max_tiles (a split is one
+#                window of the split kernel)
 #   S          = ceil(n_tiles / c);   chunk = c * T tokens
 #   sequence b uses S_b = ceil(L_b / chunk) splits; split s covers
 #   [s * chunk, min((s + 1) * chunk, L_b)).
@@ -229,17 +228,16 @@ def _cdiv(a: int, b: int) -> int:
 def split_plan_ref(num_seqs: int, num_kv_heads: int, max_seq_len: int, block_size: int,
                    cu_count: int, *, total_tokens: int = 0, forced_splits: int = 0,
                    tile: int = 64, wg_per_cu: int = 1, min_tiles: int = 2,
-                   tbl_cap: int = 2048) -> tuple[int, int]:
-    """Return (S, chunk_tokens)."""
+                   max_tiles: int = 8) -> tuple[int, int]:
+    """Return (S, chunk_tokens). block_size does not enter the plan."""
     n_tiles = max(1, _cdiv(max_seq_len, tile))
-    cap = max(1, ((tbl_cap - 2) * block_size) // tile)
     if forced_splits > 0:
         c = _cdiv(n_tiles, forced_splits)
     else:
         work = total_tokens if total_tokens > 0 else num_seqs * max_seq_len
         target = max(1, cu_count * wg_per_cu)
         c = max(min_tiles, _cdiv(num_kv_heads * work, target * tile))
-    c = max(1, min(c, n_tiles, cap))
+    c = max(1, min(c, n_tiles, max_tiles))
     return _cdiv(n_tiles, c), c * tile
 
 

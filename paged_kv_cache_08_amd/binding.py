@@ -112,7 +112,7 @@ def version() -> str:
 def plan_constants() -> dict:
     vals = [ctypes.c_int32() for _ in range(4)]
     check(lib().pkv_plan_constants(*[ctypes.byref(v) for v in vals]), "pkv_plan_constants")
-    return dict(zip(("tile", "wg_per_cu", "min_tiles", "tbl_cap"), (v.value for v in vals)))
+    return dict(zip(("tile", "wg_per_cu", "min_tiles", "max_tiles"), (v.value for v in vals)))
 
 
 def validate(p: DecodeParams) -> int:

@@ -44,8 +44,7 @@ bool mult8_pos(int64_t s) { return s > 0 && (s % 8) == 0; }
 int plan(const pkv_decode_params* p, int32_t cu_count, int32_t* S, int32_t* chunk) {
   const int64_t T = pkv::kTile;
   const int64_t n_tiles = p->max_seq_len > 0 ? cdiv64(p->max_seq_len, T) : 1;
-  int64_t cap = ((pkv::kTblCap - 2) * int64_t(p->block_size)) / T;
-  if (cap < 1) cap = 1;
+  const int64_t cap = pkv::kMaxTiles;
   int64_t c;
   if (p->num_splits > 0) {
     c = cdiv64(n_tiles, p->num_splits);
@@ -150,6 +149,7 @@ int pkv_validate_params(const pkv_decode_params* p) {
   if (!mult8_pos(p->k_stride_page) || !mult8_pos(p->k_stride_tok) || !mult8_pos(p->k_stride_head) ||
       !mult8_pos(p->v_stride_page) || !mult8_pos(p->v_stride_tok) || !mult8_pos(p->v_stride_head))
     return fail(PKV_ERR_INVALID, "K/V strides must be positive multiples of 8 elements");
+  if (p->block_size > (1 << 20)) return fail(PKV_ERR_UNSUPPORTED, "block_size above 2^20 tokens");
   if (int64_t(p->block_size) * p->k_stride_tok >= (int64_t(1) << 31) ||
       int64_t(p->block_size) * p->v_stride_tok >= (int64_t(1) << 31))
     return fail(PKV_ERR_UNSUPPORTED, "block_size * token stride must stay below 2^31 elements");
@@ -166,11 +166,11 @@ int pkv_plan_splits(const pkv_decode_params* p, int32_t cu_count, int32_t* num_s
   return plan(p, cu_count, num_splits, chunk_tokens);
 }
 
-int pkv_plan_constants(int32_t* tile, int32_t* wg_per_cu, int32_t* min_tiles, int32_t* tbl_cap) {
+int pkv_plan_constants(int32_t* tile, int32_t* wg_per_cu, int32_t* min_tiles, int32_t* max_tiles) {
   if (tile) *tile = pkv::kTile;
   if (wg_per_cu) *wg_per_cu = pkv::kWgPerCu;
   if (min_tiles) *min_tiles = pkv::kMinTiles;
-  if (tbl_cap) *tbl_cap = pkv::kTblCap;
+  if (max_tiles) *max_tiles = pkv::kMaxTiles;
   return PKV_OK;
 }
 

@@ -39,6 +39,8 @@
 // bitwise-identical output for any page size or page placement.
 #include <math.h>
 
+#include <type_traits>
+
 #include "pkv_common.h"
 
 namespace pkv {
@@ -51,9 +53,10 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kLanesPerRow = 16;
 constexpr int kRowsPerWave = 64 / kLanesPerRow;
 constexpr int kStep = kWaves * kRowsPerWave;   // tokens per workgroup sub-step
-constexpr int kRing = 4;                       // register ring depth (sub-steps)
-constexpr float kLazy = 8.0f;                  // log2 headroom before a rescale
-constexpr float kMinit = -1.0e30f;             // initial reference max (finite)
+constexpr int kSubSteps = kMaxChunk / kStep;   // sub-steps of one split (one window)
+constexpr int kRing = 6;                       // register ring depth (steps)
+constexpr int kTblSplit = kMaxChunk + 2;       // page entries one split can span (B = 1)
+constexpr float kMinit = -1.0e30f;             // floor of a row's max (finite: no inf - inf)
 constexpr int kMergeSplitsLds = 1024;          // splits whose weights the merge keeps in LDS
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
@@ -150,31 +153,78 @@ __device__ __forceinline__ bool token_row(const DecodeArgs& a, const PageOffs* t
   return po.k >= 0;
 }
 
+// Calls f(std::integral_constant<int, J>) for J = I .. N-1, so every index the
+// body uses is a compile-time constant (no dynamic register indexing).
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 // Lane n of each 16-lane row, broadcast to the whole row (DPP row_newbcast).
 template <int N>
 __device__ __forceinline__ float row_bcast(float x) {
   return dpp_move<0x150 + N>(x);
 }
 
+// out[h] = value held by lane 2h of the row (the lanes that own head h after
+// the reduce-scatter below).
 template <int G>
-__device__ __forceinline__ void row_bcast_all(float x, float (&out)[G]) {
+__device__ __forceinline__ void head_bcast(float x, float (&out)[G]) {
   if constexpr (G > 0) out[0] = row_bcast<0>(x);
-  if constexpr (G > 1) out[1] = row_bcast<1>(x);
-  if constexpr (G > 2) out[2] = row_bcast<2>(x);
-  if constexpr (G > 3) out[3] = row_bcast<3>(x);
-  if constexpr (G > 4) out[4] = row_bcast<4>(x);
-  if constexpr (G > 5) out[5] = row_bcast<5>(x);
-  if constexpr (G > 6) out[6] = row_bcast<6>(x);
-  if constexpr (G > 7) out[7] = row_bcast<7>(x);
+  if constexpr (G > 1) out[1] = row_bcast<2>(x);
+  if constexpr (G > 2) out[2] = row_bcast<4>(x);
+  if constexpr (G > 3) out[3] = row_bcast<6>(x);
+  if constexpr (G > 4) out[4] = row_bcast<8>(x);
+  if constexpr (G > 5) out[5] = row_bcast<10>(x);
+  if constexpr (G > 6) out[6] = row_bcast<12>(x);
+  if constexpr (G > 7) out[7] = row_bcast<14>(x);
+}
+
+// Reduce-scatter of up to 8 per-lane partial sums over the 16 lanes of a row.
+// Partners are lane ^ 15 (row_mirror), ^ 7 (row_half_mirror), ^ 2 and ^ 1
+// (quad_perm); at each step a lane keeps the half of the heads selected by one
+// bit of its lane index and receives its partner's copy of that half. Lanes 2h
+// and 2h + 1 end with the full sum of head h (bitwise equal); the order of the
+// additions depends only on the lane index.
+template <int G>
+__device__ __forceinline__ float reduce_scatter16(const float (&x)[G], int col) {
+  float y[4], z[2];
+  const bool b3 = col >= 8, b2 = (col & 4) != 0, b1 = (col & 2) != 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float lo = j < G ? x[j] : 0.0f;
+    const float hi = j + 4 < G ? x[j + 4] : 0.0f;
+    const float keep = b3 ? hi : lo;
+    const float send = b3 ? lo : hi;
+    y[j] = keep + dpp_move<0x140>(send);   // row_mirror
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float keep = b2 ? y[j + 2] : y[j];
+    const float send = b2 ? y[j] : y[j + 2];
+    z[j] = keep + dpp_move<0x141>(send);   // row_half_mirror
+  }
+  float w;
+  {
+    const float keep = b1 ? z[1] : z[0];
+    const float send = b1 ? z[0] : z[1];
+    w = keep + dpp_move<0x4E>(send);       // quad_perm [2,3,0,1]
+  }
+  return w + dpp_move<0xB1>(w);            // quad_perm [1,0,3,2]
 }
 
 template <int D, int G>
 __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a) {
   constexpr int kEpl = D / kLanesPerRow;   // head-dim elements per lane: 16 or 8
   constexpr int kCpl = kEpl / 8;           // 16-byte chunks per lane: 2 or 1
+  constexpr int kSteps = 2 * kSubSteps;    // K pass, then V pass
   static_assert(kCpl >= 1 && kEpl % 8 == 0, "head_dim must be a multiple of 128");
+  static_assert(G <= 8, "at most 8 query heads per KV head");
 
-  __shared__ PageOffs tbl[kTblCap];
+  __shared__ PageOffs tbl[kTblSplit];
   __shared__ float mrg_acc[kWaves][G][D];
   __shared__ float mrg_ml[kWaves][G][2];
   __shared__ float mrg_w[kWaves][G];
@@ -209,42 +259,53 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   }
   __syncthreads();
 
-  // Accumulators of this lane's token row (its D/16 elements of each head).
+  // The split is one window of at most kSubSteps sub-steps of kStep tokens;
+  // row `row` of wave `wave` owns tokens begin + j * kStep + my.
+  const int my = wave * kRowsPerWave + row;
+  const int n_sub = (sp.end - sp.begin + kStep - 1) / kStep;   // uniform, <= kSubSteps
+
   float acc[G][kEpl];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < kEpl; ++e) acc[h][e] = 0.0f;
-  // Softmax state of head `col` of this row, kept by lane col (< G) only, so each
-  // exponential is computed once per (token, head). The reference max starts at
-  // a finite floor: a row that sees no token keeps p = 2^(-inf) = 0.
-  float m_l = kMinit, l_l = 0.0f;
+  float sc[kSubSteps];        // score of head (col / 2) for each sub-step's token (log2 units)
+  uint32_t tix[kSubSteps];    // (table slot << 20) | in-page offset of that token; ~0u if masked
+  float m_row = kMinit, l_row = 0.0f;
 
-  const int my = wave * kRowsPerWave + row;   // this row's token within a sub-step
+  const uint16_t* const safe_row = a.q + out_row0 + col * 8;   // finite, in bounds
+  uint4 ring[kRing][kCpl];
 
-  // Issue the 16-byte K and V loads of one sub-step (token t0 + my). The loads
-  // are unconditional: a row past the split end, or whose page entry is
-  // invalid, reads the (finite, in-bounds) q row instead and is masked.
-  const uint16_t* const safe_row = a.q + out_row0 + col * 8;
-  auto fetch = [&](int t0, uint4 (&kk)[kCpl], uint4 (&vv)[kCpl], bool& ok) {
-    const int t = t0 + my;
+  // K step j: locate the token, remember where it is (tix: bit 31 = masked,
+  // bits 20..30 = table slot, bits 0..19 = in-page offset), load its K chunk.
+  // Branch-free: a masked row (past the split end, or an invalid page entry)
+  // reads the q row instead.
+  auto fetch_k = [&](int j, uint4 (&buf)[kCpl]) {
+    const int t = sp.begin + j * kStep + my;
     const int tc = min(t, sp.end - 1);
-    int64_t ko, vo;
-    const bool has_page = token_row(a, tbl, p_first, tc, ko, vo);
-    ok = (t < sp.end) && has_page;
-    const uint16_t* kp = ok ? a.k + ko + col * 8 : safe_row;
-    const uint16_t* vp = ok ? a.v + vo + col * 8 : safe_row;
+    const uint32_t pg = magic_div(uint32_t(tc), a.bdiv);
+    const int off = tc - int(pg * a.bdiv.d);
+    const int slot = int(pg) - p_first;
+    const int64_t pk = tbl[slot].k;
+    const bool ok = (t < sp.end) && pk >= 0;
+    tix[j] = (ok ? 0u : 0x80000000u) | (uint32_t(slot) << 20) | uint32_t(off);
+    const uint16_t* real = a.k + (pk + int64_t(off * int32_t(a.k_st))) + col * 8;
+    const uint16_t* kp = ok ? real : safe_row;
 #pragma unroll
-    for (int k = 0; k < kCpl; ++k) {
-      kk[k] = *reinterpret_cast<const uint4*>(kp + k * 128);
-      vv[k] = *reinterpret_cast<const uint4*>(vp + k * 128);
-    }
+    for (int k = 0; k < kCpl; ++k) buf[k] = *reinterpret_cast<const uint4*>(kp + k * 128);
   };
-
-  // One token per row: q.k of the G heads (DPP butterflies interleaved across
-  // heads), the softmax update of head `col` in lane col, p broadcast to the
-  // row, then V accumulation.
-  auto consume = [&](const uint4 (&kk)[kCpl], const uint4 (&vv)[kCpl], bool ok) {
+  // V step j: the same token's V chunk (the slot of a masked row is still a
+  // staged entry, so the LDS read is in range).
+  auto fetch_v = [&](int j, uint4 (&buf)[kCpl]) {
+    const uint32_t ti = tix[j];
+    const int slot = int((ti >> 20) & 0x7ffu), off = int(ti & 0xfffffu);
+    const uint16_t* real = a.v + (tbl[slot].v + int64_t(off * int32_t(a.v_st))) + col * 8;
+    const uint16_t* vp = (ti & 0x80000000u) ? safe_row : real;
+#pragma unroll
+    for (int k = 0; k < kCpl; ++k) buf[k] = *reinterpret_cast<const uint4*>(vp + k * 128);
+  };
+  // q.k of the G heads; lanes 2h, 2h+1 keep head h's score.
+  auto consume_k = [&](int j, const uint4 (&kk)[kCpl]) {
     float dq[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -258,34 +319,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
       }
       dq[h] = d0;
     }
-#pragma unroll
-    for (int h = 0; h < G; ++h) dq[h] += dpp_move<0xB1>(dq[h]);    // quad_perm [1,0,3,2]
-#pragma unroll
-    for (int h = 0; h < G; ++h) dq[h] += dpp_move<0x4E>(dq[h]);    // quad_perm [2,3,0,1]
-#pragma unroll
-    for (int h = 0; h < G; ++h) dq[h] += dpp_move<0x141>(dq[h]);   // row_half_mirror
-#pragma unroll
-    for (int h = 0; h < G; ++h) dq[h] += dpp_move<0x140>(dq[h]);   // row_mirror
-    float mine = dq[0];
-#pragma unroll
-    for (int h = 1; h < G; ++h) mine = (col == h) ? dq[h] : mine;
-    const float sc = ok ? mine * a.scale_log2 : -INFINITY;
-    const bool resc = sc > m_l + kLazy;
-    if (__builtin_amdgcn_ballot_w64(resc) != 0) {   // wave-uniform; rare after the first tokens
-      const float al = resc ? fast_exp2(m_l - sc) : 1.0f;
-      m_l = resc ? sc : m_l;
-      l_l *= al;
-      float ah[G];
-      row_bcast_all<G>(al, ah);
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < kEpl; ++e) acc[h][e] *= ah[h];
-    }
-    const float pl = fast_exp2(sc - m_l);
-    l_l += pl;
+    const float r = reduce_scatter16<G>(dq, col) * a.scale_log2;
+    sc[j] = (tix[j] & 0x80000000u) ? -INFINITY : r;
+  };
+  // p of head (col / 2), broadcast to the row, V accumulation.
+  auto consume_v = [&](int j, const uint4 (&vv)[kCpl]) {
+    const float pl = fast_exp2(sc[j] - m_row);
+    l_row += pl;
     float p[G];
-    row_bcast_all<G>(pl, p);
+    head_bcast<G>(pl, p);
 #pragma unroll
     for (int k = 0; k < kCpl; ++k) {
       const uint32_t w4[4] = {vv[k].x, vv[k].y, vv[k].z, vv[k].w};
@@ -301,41 +343,40 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
       }
     }
   };
+  // One stream of 2 * kSubSteps steps (K pass, then V pass) through a ring of
+  // kRing register buffers: kRing - 1 steps of loads stay in flight. Fully
+  // unrolled, so every buffer lives in fixed registers; steps past n_sub are
+  // skipped with uniform branches.
+#pragma unroll
+  for (int j = 0; j < kSubSteps; ++j) sc[j] = -INFINITY;
+  // Loads are issued for every step (a dead step only reads the q row); the
+  // arithmetic of steps past n_sub is skipped with uniform branches.
+  static_for<0, kRing - 1>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    if constexpr (j < kSubSteps) fetch_k(j, ring[j % kRing]);
+    else fetch_v(j - kSubSteps, ring[j % kRing]);
+  });
+  static_for<0, kSteps>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    constexpr int jn = j + kRing - 1;
+    if constexpr (jn < kSteps) {
+      if constexpr (jn < kSubSteps) fetch_k(jn, ring[jn % kRing]);
+      else fetch_v(jn - kSubSteps, ring[jn % kRing]);
+    }
+    if ((j < kSubSteps ? j : j - kSubSteps) < n_sub) {
+      if constexpr (j < kSubSteps) consume_k(j, ring[j % kRing]);
+      else consume_v(j - kSubSteps, ring[j % kRing]);
+    }
+    if constexpr (j == kSubSteps - 1) {
+#pragma unroll
+      for (int i = 0; i < kSubSteps; ++i) m_row = fmaxf(m_row, sc[i]);
+    }
+  });
 
-  // Register ring of 4 sub-steps (named buffers, so each stays in fixed
-  // registers): the loads of 3 sub-steps are in flight while one is consumed.
-  // The main loop runs whole groups of 4 sub-steps and has a single exit; the
-  // 0-3 sub-steps left over are already in flight when it ends.
-  static_assert(kRing == 4, "the ring below is written out for 4 buffers");
-  uint4 k0[kCpl], v0[kCpl], k1[kCpl], v1[kCpl], k2[kCpl], v2[kCpl], k3[kCpl], v3[kCpl];
-  bool ok0, ok1, ok2, ok3;
-  const int n_sub = (sp.end - sp.begin + kStep - 1) / kStep;
-  const int n_groups = n_sub >> 2;
-  const int rem = n_sub & 3;
-  int t_fetch = sp.begin;
-  fetch(t_fetch, k0, v0, ok0);
-  fetch(t_fetch + kStep, k1, v1, ok1);
-  fetch(t_fetch + 2 * kStep, k2, v2, ok2);
-  t_fetch += 3 * kStep;
-  for (int it = 0; it < n_groups; ++it) {
-    fetch(t_fetch, k3, v3, ok3);
-    consume(k0, v0, ok0);
-    fetch(t_fetch + kStep, k0, v0, ok0);
-    consume(k1, v1, ok1);
-    fetch(t_fetch + 2 * kStep, k1, v1, ok1);
-    consume(k2, v2, ok2);
-    fetch(t_fetch + 3 * kStep, k2, v2, ok2);
-    consume(k3, v3, ok3);
-    t_fetch += 4 * kStep;
-  }
-  if (rem > 0) consume(k0, v0, ok0);
-  if (rem > 1) consume(k1, v1, ok1);
-  if (rem > 2) consume(k2, v2, ok2);
-
-  // Row state per head, from lane h of each row.
+  // Row state per head, from lanes 2h of each row.
   float m[G], l[G];
-  row_bcast_all<G>(m_l, m);
-  row_bcast_all<G>(l_l, l);
+  head_bcast<G>(m_row, m);
+  head_bcast<G>(l_row, l);
 
   // Merge the 4 token rows of each wave (fixed butterfly order).
 #pragma unroll
@@ -528,7 +569,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(DecodeArgs a) {
 // table staging and token_row() the split kernel uses.
 __global__ __launch_bounds__(kThreads) void debug_offsets_kernel(DecodeArgs a, int g, int max_seq_len,
                                                                  int64_t* k_off, int64_t* v_off) {
-  __shared__ PageOffs tbl[kTblCap];
+  __shared__ PageOffs tbl[kTblSplit];
   const int s = blockIdx.x, b = blockIdx.y;
   const SplitSpan sp = split_span(a, b, s);
   if (sp.begin >= sp.L) return;

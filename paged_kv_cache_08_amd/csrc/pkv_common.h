@@ -10,7 +10,8 @@ namespace pkv {
 constexpr int kTile = 64;        // split boundaries are multiples of this many tokens
 constexpr int kWgPerCu = 1;      // planner target: this many split workgroups per CU
 constexpr int kMinTiles = 2;     // a split covers at least this many tiles when planned
-constexpr int kTblCap = 2048;    // block-table entries one split may span (LDS staging)
+constexpr int kMaxTiles = 8;     // a split covers at most this many tiles (one kernel window)
+constexpr int kMaxChunk = kMaxTiles * kTile;
 
 constexpr int kWsHeaderBytes = 256;   // workspace: error word, then partials
 

@@ -65,6 +65,8 @@ def params(**kw):
     ({"max_seq_len": 42 * 784 + 1}, -1),
     ({"max_seq_len": -1}, -1),
     ({"k_stride_tok": 1020}, -1),        # not a multiple of 8 elements
+    ({"block_size": (1 << 20) + 16, "max_pages_per_seq": 1, "max_seq_len": 100}, -2),
+    ({"block_size": 1 << 20, "max_pages_per_seq": 1, "max_seq_len": 100, "k_stride_tok": 4096}, -2),
     ({"v_stride_head": 0}, -1),
     ({"scale": float("nan")}, -1),
     ({"out_dtype": 7}, -1),
@@ -76,7 +78,7 @@ def test_validation_codes(kw, code):
 
 
 def test_plan_constants_are_the_documented_ones():
-    assert P.plan_constants() == dict(tile=64, wg_per_cu=1, min_tiles=2, tbl_cap=2048)
+    assert P.plan_constants() == dict(tile=64, wg_per_cu=1, min_tiles=2, max_tiles=8)
 
 
 PLAN = [

@@ -84,7 +84,8 @@ def test_forced_split_counts_agree(splits):
     log(f"case: context 16384, page 784, {splits} splits")
     case = hybrid(16384)
     got = run_gpu(case, num_splits=splits)
-    assert f"splits={min(splits, 256)}" in P.last_variant()
+    S, chunk = O.split_plan_ref(1, 4, 16384, 784, P.device_cu_count(), forced_splits=splits)
+    assert f"splits={S} chunk={chunk} " in P.last_variant()
     assert_matches_oracle(got, oracle_out(case), f"S={splits}")
 
 

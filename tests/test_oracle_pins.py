@@ -357,12 +357,13 @@ PLAN_CASES = [
 @pytest.mark.parametrize("ns,hkv,L,bs,cu,total,forced", PLAN_CASES)
 def test_split_plan_invariants(ns, hkv, L, bs, cu, total, forced):
     S, chunk = O.split_plan_ref(ns, hkv, L, bs, cu, total_tokens=total, forced_splits=forced)
-    assert S >= 1 and chunk >= 64 and chunk % 64 == 0
+    assert S >= 1 and chunk >= 64 and chunk % 64 == 0 and chunk <= 512
     assert S * chunk >= L and (L == 0 or (S - 1) * chunk < L)
-    # a split's table entries fit the kernel's 2048-entry table cache
-    assert (chunk - 1) // bs + 2 <= 2048
-    if forced:
-        assert S <= max(forced, -(-L // ((2046 * bs) // 64 * 64)) if L else 1)
+    if forced and L:
+        # a forced count sets the chunk unless that chunk would exceed 512 tokens
+        n_tiles = -(-L // 64)
+        assert chunk == 64 * min(8, -(-n_tiles // forced))
+        assert S <= max(forced, -(-L // 512))
     lens = [L] + [max(0, L - 17 * k) for k in range(1, ns)]
     r = O.split_ranges_ref(lens, S, chunk)
     for b, Lb in enumerate(lens):
