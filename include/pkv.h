@@ -42,7 +42,7 @@ extern "C" {
 
 #define PKV_OK               0
 #define PKV_ERR_INVALID     -1  /* null pointer, bad size, Hq % Hkv != 0, stride or alignment error */
-#define PKV_ERR_UNSUPPORTED -2  /* head_dim not 128/256, q_len not in [1,16], group size > 8, ... */
+#define PKV_ERR_UNSUPPORTED -2  /* head_dim not 128/256, q_len not in [1,16], too many query rows per KV head, ... */
 #define PKV_ERR_WORKSPACE   -3  /* workspace smaller than pkv_workspace_bytes() */
 #define PKV_ERR_HIP         -4  /* a HIP runtime call or launch failed */
 
@@ -55,7 +55,8 @@ typedef struct pkv_decode_params {
   int32_t num_seqs;          /* sequences in the batch, >= 1 */
   int32_t q_len;             /* new query rows per sequence, 1..16 (1 = decode) */
   int32_t num_q_heads;       /* Hq */
-  int32_t num_kv_heads;      /* Hkv; Hq % Hkv == 0 and Hq / Hkv <= 8 */
+  int32_t num_kv_heads;      /* Hkv; Hq % Hkv == 0; Hq / Hkv <= 8 when q_len == 1,
+                                (Hq / Hkv) * q_len <= 128 when q_len > 1 */
   int32_t head_dim;          /* D: 128 or 256 */
   int32_t block_size;        /* tokens per physical page, any value >= 1 (e.g. 16, 784, 832) */
   int32_t max_pages_per_seq; /* row stride of block_table, in entries */

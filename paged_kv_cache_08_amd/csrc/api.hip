@@ -138,12 +138,11 @@ int pkv_validate_params(const pkv_decode_params* p) {
     return fail(PKV_ERR_INVALID, "num_q_heads is not a multiple of num_kv_heads");
   const int group = p->num_q_heads / p->num_kv_heads;
   if (p->head_dim != 128 && p->head_dim != 256) return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 128 or 256");
-  if (group > 8) return fail(PKV_ERR_UNSUPPORTED, "more than 8 query heads per KV head");
   if (p->q_len > 16) return fail(PKV_ERR_UNSUPPORTED, "q_len above 16");
   if (p->q_len == 1 && !pkv::decode_supported(p->head_dim, group))
-    return fail(PKV_ERR_UNSUPPORTED, "no decode kernel for this head_dim / group");
+    return fail(PKV_ERR_UNSUPPORTED, "decode (q_len 1) needs at most 8 query heads per KV head");
   if (p->q_len > 1 && !pkv::verify_supported(p->head_dim, group, p->q_len))
-    return fail(PKV_ERR_UNSUPPORTED, "no multi-row kernel for this head_dim / group / q_len");
+    return fail(PKV_ERR_UNSUPPORTED, "multi-row calls need (Hq / Hkv) * q_len <= 128");
   if (int64_t(p->max_pages_per_seq) * p->block_size < p->max_seq_len)
     return fail(PKV_ERR_INVALID, "max_seq_len exceeds max_pages_per_seq * block_size");
   if (!mult8_pos(p->k_stride_page) || !mult8_pos(p->k_stride_tok) || !mult8_pos(p->k_stride_head) ||

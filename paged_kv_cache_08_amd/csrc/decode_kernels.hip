@@ -39,14 +39,10 @@
 // bitwise-identical output for any page size or page placement.
 #include <math.h>
 
-#include <type_traits>
-
-#include "pkv_common.h"
+#include "pkv_device.h"
 
 namespace pkv {
 namespace {
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;                      // 2 waves per SIMD
 constexpr int kThreads = 64 * kWaves;
@@ -58,110 +54,6 @@ constexpr int kRing = 6;                       // register ring depth (steps)
 constexpr int kTblSplit = kMaxChunk + 2;       // page entries one split can span (B = 1)
 constexpr float kMinit = -1.0e30f;             // floor of a row's max (finite: no inf - inf)
 constexpr int kMergeSplitsLds = 1024;          // splits whose weights the merge keeps in LDS
-
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_move(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                               CTRL, 0xF, 0xF, false));
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40);   // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
-
-__device__ __forceinline__ void store_out(const DecodeArgs& a, int64_t idx, float x) {
-  if (a.out_bf16)
-    static_cast<uint16_t*>(a.out)[idx] = f32_to_bf16_rne(x);
-  else
-    static_cast<float*>(a.out)[idx] = x;
-}
-
-struct SplitSpan {
-  int L;        // live tokens of the sequence (clamped to what the table can map)
-  int begin;    // first token of the split
-  int end;      // one past the last token
-  int nsplit;   // splits this sequence uses
-};
-
-// Split s of sequence b: [s * chunk, min((s + 1) * chunk, L)). L is clamped to
-// what the block table can map and to what the planned splits cover, so a
-// length above the host's max_seq_len can never index past the table, the
-// grid or the workspace.
-__device__ __forceinline__ SplitSpan split_span(const DecodeArgs& a, int b, int s) {
-  int64_t cap = int64_t(a.max_pages) * int64_t(a.bdiv.d);
-  const int64_t planned = int64_t(a.num_splits) * a.chunk;
-  cap = cap < planned ? cap : planned;
-  int64_t L = a.seq_lens[b];
-  L = L < 0 ? 0 : (L > cap ? cap : L);
-  SplitSpan r;
-  r.L = int(L);
-  r.begin = s * a.chunk;
-  r.end = min(r.begin + a.chunk, r.L);
-  r.nsplit = (r.L + a.chunk - 1) / a.chunk;
-  return r;
-}
-
-// Element offsets of one physical page's first row for KV head g, for K and
-// for V; k < 0 marks a table entry that is skipped.
-struct PageOffs {
-  int64_t k;
-  int64_t v;
-};
-
-// Stage block-table entries [p_first, p_first + n) of sequence b in LDS as
-// page offsets of KV head g. Entries outside [0, num_pages) are marked invalid
-// (their tokens are skipped) and set bit 0 of the workspace error word.
-__device__ __forceinline__ void stage_table(const DecodeArgs& a, int b, int g, int p_first, int n,
-                                            PageOffs* tbl) {
-  const int32_t* row = a.table + int64_t(b) * a.max_pages + p_first;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const int e = row[i];
-    PageOffs po;
-    if (uint32_t(e) >= uint32_t(a.num_pages)) {
-      if (a.err) atomicOr(a.err, 1u);
-      po.k = -1;
-      po.v = -1;
-    } else {
-      po.k = int64_t(e) * a.k_sp + int64_t(g) * a.k_sh;
-      po.v = int64_t(e) * a.v_sp + int64_t(g) * a.v_sh;
-    }
-    tbl[i] = po;
-  }
-}
-
-// Element offsets of token t's K and V rows; false if its page entry is
-// invalid. The in-page part off * stride_tok fits 32 bits (checked on the host).
-__device__ __forceinline__ bool token_row(const DecodeArgs& a, const PageOffs* tbl, int p_first, int t,
-                                          int64_t& ko, int64_t& vo) {
-  const uint32_t pg = magic_div(uint32_t(t), a.bdiv);
-  const int off = t - int(pg * a.bdiv.d);
-  const PageOffs po = tbl[int(pg) - p_first];
-  ko = po.k + int64_t(off * int32_t(a.k_st));
-  vo = po.v + int64_t(off * int32_t(a.v_st));
-  return po.k >= 0;
-}
-
-// Calls f(std::integral_constant<int, J>) for J = I .. N-1, so every index the
-// body uses is a compile-time constant (no dynamic register indexing).
-template <int I, int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
 
 // Lane n of each 16-lane row, broadcast to the whole row (DPP row_newbcast).
 template <int N>

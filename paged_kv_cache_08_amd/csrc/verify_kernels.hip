@@ -1,11 +1,283 @@
-// Multi-row (speculative verify) split kernel: placeholder until the MFMA
-// kernel lands; every multi-row shape is reported unsupported.
-#include "pkv_common.h"
+// Multi-row (speculative verify) paged attention for gfx950: q_len in [2, 16]
+// new query rows per sequence, each with its own causal bound, sharing one
+// walk over the paged K/V. This is the case where q.k and p.v become small
+// dense contractions, so they run on MFMA.
+//
+// Following "Qwen3.8 auf MI350P betreiben", Lektion 3: every K/V tile is
+// reused by all verify rows of the request (here the G * q_len rows of one KV
+// head, at most 128), each row applies its own causal mask, and partial
+// softmax statistics are merged (by the LSE merge kernel across splits).
+// Addresses follow "DCU page832 attention" §1/§5 as in the decode kernel.
+//
+// Workgroup = one split (<= 512 tokens) of one (sequence, KV head), 8 waves.
+//   * All 8 waves stage 64-token K and V tiles into LDS (double buffered, rows
+//     padded to 528 bytes) with 16-byte loads through the block table.
+//   * Wave w owns query rows f = 16w .. 16w + 15 of the flattened
+//     (head, position) list, head-major (f = h_local * q_len + i); waves past
+//     the last row only stage tiles.
+//   * S^T = K Q^T per 16-token block with v_mfma_f32_16x16x32_bf16 (A = K rows
+//     from LDS, B = the wave's Q rows held in registers). Its accumulator
+//     layout (lane l: tokens 4(l/16)..+3 of row l%16) is exactly the A-operand
+//     layout of P for O = P V, so P never leaves registers.
+//   * Online softmax per row with the exact tile max (log2 units); rows are
+//     reduced across the four 16-lane groups with two shuffles.
+//   * P is split into bf16 hi + lo (hi = bf16(p), lo = bf16(p - hi)), two MFMAs
+//     per block, so the bf16 operand costs about 2^-16 relative error instead of
+//     2^-9. V enters as the B operand through ds_read_b64_tr_b16: lane j of a
+//     16-lane group points at V[4q + j/4][d0 + 4(j%4)] and lane i receives the
+//     column V[4q..4q+3][d0 + i].
+//   * O (16 rows x D) stays in MFMA accumulators; the split writes it
+//     un-normalised with the row's (max, sum), or normalised when the
+//     sequence has a single split.
+#include "pkv_device.h"
 
 namespace pkv {
+namespace {
 
-bool verify_supported(int, int, int) { return false; }
+constexpr int kVWaves = 8;
+constexpr int kVThreads = 64 * kVWaves;
+constexpr int kVTile = 64;      // tokens per K/V tile
+constexpr int kRowsPerWave = 16;
+constexpr float kMinitV = -1.0e30f;   // floor of a row's running max (finite: no inf - inf)
 
-hipError_t launch_verify_split(const DecodeArgs&, int, int, hipStream_t) { return hipErrorInvalidValue; }
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t* lds_short4_ptr;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+// bf16 bits of x rounded to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int D>
+__global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a) {
+  constexpr int kPitch = D * 2 + 16;              // LDS bytes per token row (padded)
+  constexpr int kChunks = D * 2 / 16;             // 16-byte chunks per row
+  constexpr int kLoads = kVTile * kChunks / kVThreads;   // K (and V) chunks per thread per tile
+  constexpr int kKSteps = D / 32;                 // 32-wide k steps of q.k
+  constexpr int kDBlocks = D / 16;                // 16-column blocks of O
+  static_assert(kLoads >= 1 && kVTile * kChunks % kVThreads == 0, "tile must split evenly");
+
+  __shared__ __attribute__((aligned(16))) uint8_t kv[2][2][kVTile * kPitch];
+  __shared__ PageOffs tbl[kMaxChunk + 2];
+
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = lane >> 4, ln = lane & 15;
+  const int q_len = a.q_len;
+  const int G = a.hq / a.hkv;
+  const int R = G * q_len;                        // rows of this KV head (<= 128)
+  const SplitSpan sp = split_span(a, b, s);
+
+  if (sp.begin >= sp.L) {
+    if (s == 0)   // empty sequence: zeros for every row of this KV head
+      for (int i = tid; i < R * D; i += kVThreads) {
+        const int f = i / D, d = i - f * D;
+        const int64_t prow = (int64_t(b) * q_len + f % q_len) * a.hq + int64_t(g) * G + f / q_len;
+        store_out(a, prow * D + d, 0.0f);
+      }
+    return;
+  }
+  const int p_first = int(magic_div(uint32_t(sp.begin), a.bdiv));
+  const int p_last = int(magic_div(uint32_t(sp.end - 1), a.bdiv));
+  stage_table(a, b, g, p_first, p_last - p_first + 1, tbl);
+
+  // This lane's S^T row (row ln of the wave's block).
+  const bool computes = wave * kRowsPerWave < R;  // uniform per wave
+  const int f_row = wave * kRowsPerWave + ln;
+  const bool row_valid = f_row < R;
+  const int h_row = row_valid ? f_row / q_len : 0;
+  const int i_row = row_valid ? f_row % q_len : 0;
+  const int pos_row = sp.L - q_len + i_row;      // last visible token of the row
+
+  // Q of row ln, as the B operand of S^T: k step kk holds d = 32 kk + 8 grp .. +8.
+  uint4 qreg[kKSteps];
+  {
+    const int64_t qoff = ((int64_t(b) * q_len + i_row) * a.hq + int64_t(g) * G + h_row) * D + 8 * grp;
+#pragma unroll
+    for (int kk = 0; kk < kKSteps; ++kk)
+      qreg[kk] = (computes && row_valid) ? *reinterpret_cast<const uint4*>(a.q + qoff + 32 * kk)
+                                         : make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();   // table staged
+
+  float4_t o[kDBlocks];
+#pragma unroll
+  for (int db = 0; db < kDBlocks; ++db) o[db] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = kMinitV, l_run = 0.0f;            // stats of row ln
+
+  // Tile staging: thread tid moves chunks c = tid + kVThreads * k of K and V.
+  uint4 stk[kLoads], stv[kLoads];
+  auto load_tile = [&](int tile) {
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+      const int c = tid + kVThreads * k;
+      const int tt = c / kChunks, piece = c - tt * kChunks;
+      const int t = sp.begin + tile * kVTile + tt;
+      const int tc = min(t, sp.end - 1);
+      int64_t ko, vo;
+      const bool ok = token_row(a, tbl, p_first, tc, ko, vo) && t < sp.end;
+      const uint16_t* kp = ok ? a.k + ko + piece * 8 : a.q;   // masked rows read q (finite)
+      const uint16_t* vp = ok ? a.v + vo + piece * 8 : a.q;
+      stk[k] = *reinterpret_cast<const uint4*>(kp);
+      stv[k] = *reinterpret_cast<const uint4*>(vp);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+      const int c = tid + kVThreads * k;
+      const int tt = c / kChunks, piece = c - tt * kChunks;
+      *reinterpret_cast<uint4*>(&kv[buf][0][tt * kPitch + piece * 16]) = stk[k];
+      *reinterpret_cast<uint4*>(&kv[buf][1][tt * kPitch + piece * 16]) = stv[k];
+    }
+  };
+
+  const int n_tiles = (sp.end - sp.begin + kVTile - 1) / kVTile;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const int buf = tile & 1;
+    const bool more = tile + 1 < n_tiles;
+    if (more) load_tile(tile + 1);
+    if (computes) {
+      const uint8_t* kb = kv[buf][0];
+      // S^T for the 4 token blocks: st[tb][r] = score of token tb*16 + 4 grp + r, row ln.
+      float4_t st[4];
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        st[tb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < kKSteps; ++kk) {
+          const uint4 kr = *reinterpret_cast<const uint4*>(kb + (tb * 16 + ln) * kPitch + (32 * kk + 8 * grp) * 2);
+          st[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr), as_bf16x8(qreg[kk]), st[tb], 0, 0, 0);
+        }
+      }
+      // Scale, causal / range mask, tile max of row ln.
+      const int t0 = sp.begin + tile * kVTile + 4 * grp;
+      float mt = -INFINITY;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = t0 + tb * 16 + r;
+          const bool vis = row_valid && t < sp.end && t <= pos_row;
+          const float x = vis ? st[tb][r] * a.scale_log2 : -INFINITY;
+          st[tb][r] = x;
+          mt = fmaxf(mt, x);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = fast_exp2(m_run - m_new);
+      float ls = 0.0f;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = fast_exp2(st[tb][r] - m_new);
+          st[tb][r] = p;
+          ls += p;
+        }
+      ls += __shfl_xor(ls, 16);
+      ls += __shfl_xor(ls, 32);
+      l_run = l_run * alpha + ls;
+      m_run = m_new;
+      // O rows 4 grp + r take the alpha of that row (held by lane 4 grp + r of the group).
+      float al[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 16 * grp + 4 * grp + r);
+#pragma unroll
+      for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[db][r] *= al[r];
+      // P as A operands (hi and lo) of the two 32-token halves.
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float p0 = st[2 * hh + (t >> 1)][(t & 1) * 2];
+          const float p1 = st[2 * hh + (t >> 1)][(t & 1) * 2 + 1];
+          const uint32_t h0 = bf16_bits(p0), h1 = bf16_bits(p1);
+          const uint32_t l0 = bf16_bits(p0 - __uint_as_float(h0 << 16));
+          const uint32_t l1 = bf16_bits(p1 - __uint_as_float(h1 << 16));
+          hi[t] = h0 | (h1 << 16);
+          lo[t] = l0 | (l1 << 16);
+        }
+        const bf16x8_t ph = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
+        const bf16x8_t pl = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+        // V (32 tokens x 16 columns) per column block: two transposed reads.
+        const int rowa = (2 * hh) * 16 + 4 * grp + (ln >> 2);
+        const int rowb = rowa + 16;
+#pragma unroll
+        for (int db = 0; db < kDBlocks; ++db) {
+          const int colb = (16 * db + 4 * (ln & 3)) * 2;
+          const short4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_short4_ptr)(kv[buf][1] + rowa * kPitch + colb));
+          const short4_t vb2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_short4_ptr)(kv[buf][1] + rowb * kPitch + colb));
+          const uint4 vu = make_uint4(uint32_t(uint16_t(va[0])) | (uint32_t(uint16_t(va[1])) << 16),
+                                      uint32_t(uint16_t(va[2])) | (uint32_t(uint16_t(va[3])) << 16),
+                                      uint32_t(uint16_t(vb2[0])) | (uint32_t(uint16_t(vb2[1])) << 16),
+                                      uint32_t(uint16_t(vb2[2])) | (uint32_t(uint16_t(vb2[3])) << 16));
+          o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, as_bf16x8(vu), o[db], 0, 0, 0);
+          o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, as_bf16x8(vu), o[db], 0, 0, 0);
+        }
+      }
+    }
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (!computes) return;
+  // Rows 4 grp + r of O; their (max, sum) are held by lane 4 grp + r of each group.
+  const int64_t prow_base = (int64_t(b) * q_len) * a.hq + int64_t(g) * G;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int src = 16 * grp + 4 * grp + r;
+    const float lr = __shfl(l_run, src);
+    const float mr = __shfl(m_run, src);
+    const int f = wave * kRowsPerWave + 4 * grp + r;
+    if (f >= R) continue;
+    const int h = f / q_len, i = f % q_len;
+    const int64_t prow = prow_base + int64_t(i) * a.hq + h;
+    if (sp.nsplit == 1) {
+      const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+#pragma unroll
+      for (int db = 0; db < kDBlocks; ++db) store_out(a, prow * D + 16 * db + ln, o[db][r] * inv);
+    } else {
+      const int64_t pr = prow * a.num_splits + s;
+#pragma unroll
+      for (int db = 0; db < kDBlocks; ++db) a.part_acc[pr * D + 16 * db + ln] = o[db][r];
+      if (ln == 0) {
+        a.part_ml[pr * 2] = mr;
+        a.part_ml[pr * 2 + 1] = lr;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool verify_supported(int head_dim, int group, int q_len) {
+  return (head_dim == 128 || head_dim == 256) && group >= 1 && q_len >= 2 && q_len <= 16 &&
+         group * q_len <= kVWaves * kRowsPerWave;
+}
+
+hipError_t launch_verify_split(const DecodeArgs& a, int head_dim, int group, hipStream_t st) {
+  if (!verify_supported(head_dim, group, a.q_len)) return hipErrorInvalidValue;
+  dim3 grid(a.num_splits, a.hkv, a.num_seqs);
+  if (head_dim == 256)
+    hipLaunchKernelGGL(verify_split_kernel<256>, grid, dim3(kVThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(verify_split_kernel<128>, grid, dim3(kVThreads), 0, st, a);
+  return hipGetLastError();
+}
 
 }  // namespace pkv
