@@ -15,7 +15,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import statistics
@@ -34,7 +33,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="hybrid", choices=["hybrid", "dense", "mixed"])
+    ap.add_argument("--workload", default="hybrid", choices=["hybrid", "dense", "mixed", "verify"])
     ap.add_argument("--context", type=int, default=32768)
     ap.add_argument("--block-size", type=int, default=784)
     ap.add_argument("--pools", type=int, default=16)
@@ -43,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--repeats", type=int, default=5, help="extra timed regions for spread statistics")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay measurement")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before timing, copy this many MiB once (a kernel of known traffic, used to "
+                         "scale rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -82,9 +84,13 @@ def make_workload(args):
     elif args.workload == "dense":
         case = W.dense_control(args.context, poison=False)
         name = f"dense control: batch 1, q_len 1, 32 q / 8 KV heads, head_dim 128, page 16, context {args.context}"
-    else:
+    elif args.workload == "mixed":
         case = W.mixed_batch(poison=False)
         name = "mixed batch: 16 sequences, q_len 1, 24 q / 4 KV heads, head_dim 256, page 784, log-uniform 500-32000"
+    else:
+        case = W.spec_verify(args.context, poison=False)
+        name = (f"speculative verify: batch 1, q_len 16 causal rows, 24 q / 4 KV heads, head_dim 256, "
+                f"page 784, context {args.context}")
     return case, name
 
 
@@ -99,15 +105,6 @@ def traffic_from_profiles(kernel_src_hash: str, workload_key: str):
     if not rec or rec.get("kernel_src_sha256") != kernel_src_hash:
         return None
     return rec.get("hbm_bytes_per_launch")
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "paged_kv_cache_08_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
-    return h.hexdigest()
 
 
 def cpu_baseline(case, kv_bytes_per_call, seconds):
@@ -178,6 +175,18 @@ def main():
     def step(i, c=call):
         kp, vp = ptrs[i % len(ptrs)]
         c.run_ptrs(kp, vp)
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        flush.fill_(3)                      # evict src from the caches before the measured copy
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy: {n} bytes read, {n} bytes written", file=sys.stderr, flush=True)
+        del src, dst, flush
 
     hip = Hip()
     for i in range(args.warmup):
@@ -265,6 +274,7 @@ def main():
 
     gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
     kern_gbs = kv_bytes / (kern_avg_us * 1e-6) / 1e9
+    from paged_kv_cache_08_amd.profiling import kernel_source_hash
     src_hash = kernel_source_hash()
     wl_key = f"{args.workload}:{args.context}:{case.block_size}"
     traffic = traffic_from_profiles(src_hash, wl_key)
@@ -303,7 +313,7 @@ def main():
                                 "range_pct": round(100.0 * (max(region_us) - min(region_us)) / med, 2)},
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_split_kernel",
+            "kernel": "verify_split_kernel" if case.q_len > 1 else "decode_split_kernel",
             "achieved": round(kern_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -150,9 +150,10 @@ int pkv_paged_decode_attention(const pkv_decode_params* p,
  * len-1 characters plus a terminator; returns the full length. */
 int pkv_last_variant(char* buf, int32_t len);
 
-/* Profiling hook: when both are non-NULL, later calls on this thread record
- * ev_start immediately before and ev_stop immediately after the split kernel
- * (hipEvent_t handles, on the call's stream). NULL, NULL turns it off. */
+/* Profiling hook: when both are non-NULL, later calls on this thread launch
+ * the split kernel with hipExtLaunchKernel so that ev_start and ev_stop
+ * (hipEvent_t handles) are stamped at the start and end of its execution.
+ * NULL, NULL turns it off. */
 int pkv_set_timing_events(void* ev_start, void* ev_stop);
 
 /* Debug: the element offset of every live token row of KV head kv_head, as the

@@ -226,17 +226,15 @@ int pkv_paged_decode_attention(const pkv_decode_params* p, const void* q, const 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int group = p->num_q_heads / p->num_kv_heads;
   hipError_t e;
-  if (g_ev_start && (e = hipEventRecord(g_ev_start, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   const char* split_name;
   if (p->q_len == 1) {
-    e = pkv::launch_decode_split(a, p->head_dim, group, st);
+    e = pkv::launch_decode_split(a, p->head_dim, group, st, g_ev_start, g_ev_stop);
     split_name = "decode_valu";
   } else {
-    e = pkv::launch_verify_split(a, p->head_dim, group, st);
+    e = pkv::launch_verify_split(a, p->head_dim, group, st, g_ev_start, g_ev_stop);
     split_name = "verify_mfma";
   }
   if (e != hipSuccess) return hip_fail(e, "split kernel launch");
-  if (g_ev_stop && (e = hipEventRecord(g_ev_stop, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if (S > 1) {
     e = pkv::launch_lse_merge(a, p->head_dim, st);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");

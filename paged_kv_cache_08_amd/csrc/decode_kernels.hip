@@ -39,6 +39,8 @@
 // bitwise-identical output for any page size or page placement.
 #include <math.h>
 
+#include <hip/hip_ext.h>
+
 #include "pkv_device.h"
 
 namespace pkv {
@@ -50,7 +52,9 @@ constexpr int kLanesPerRow = 16;
 constexpr int kRowsPerWave = 64 / kLanesPerRow;
 constexpr int kStep = kWaves * kRowsPerWave;   // tokens per workgroup sub-step
 constexpr int kSubSteps = kMaxChunk / kStep;   // sub-steps of one split (one window)
-constexpr int kRing = 6;                       // register ring depth (steps)
+// Register ring depth (steps in flight + 1); shallower where G * D leaves
+// fewer registers (depths 4..10 measured alike at G = 6, D = 256).
+constexpr int ring_depth(int D, int G) { return (D == 256 && G >= 7) ? 3 : 6; }
 constexpr int kTblSplit = kMaxChunk + 2;       // page entries one split can span (B = 1)
 constexpr float kMinit = -1.0e30f;             // floor of a row's max (finite: no inf - inf)
 constexpr int kMergeSplitsLds = 1024;          // splits whose weights the merge keeps in LDS
@@ -113,6 +117,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   constexpr int kEpl = D / kLanesPerRow;   // head-dim elements per lane: 16 or 8
   constexpr int kCpl = kEpl / 8;           // 16-byte chunks per lane: 2 or 1
   constexpr int kSteps = 2 * kSubSteps;    // K pass, then V pass
+  constexpr int kRing = ring_depth(D, G);
   static_assert(kCpl >= 1 && kEpl % 8 == 0, "head_dim must be a multiple of 128");
   static_assert(G <= 8, "at most 8 query heads per KV head");
 
@@ -490,23 +495,26 @@ __global__ void debug_ranges_kernel(DecodeArgs a, int32_t* ranges) {
 }
 
 template <int D, int G>
-hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   dim3 grid(a.num_splits, a.hkv, a.num_seqs);
-  hipLaunchKernelGGL((decode_split_kernel<D, G>), grid, dim3(kThreads), 0, st, a);
+  if (e0 && e1)
+    hipExtLaunchKernelGGL((decode_split_kernel<D, G>), grid, dim3(kThreads), 0, st, e0, e1, 0, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<D, G>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_decode_d(const DecodeArgs& a, int group, hipStream_t st) {
+hipError_t launch_decode_d(const DecodeArgs& a, int group, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   switch (group) {
-    case 1: return launch_decode_t<D, 1>(a, st);
-    case 2: return launch_decode_t<D, 2>(a, st);
-    case 3: return launch_decode_t<D, 3>(a, st);
-    case 4: return launch_decode_t<D, 4>(a, st);
-    case 5: return launch_decode_t<D, 5>(a, st);
-    case 6: return launch_decode_t<D, 6>(a, st);
-    case 7: return launch_decode_t<D, 7>(a, st);
-    case 8: return launch_decode_t<D, 8>(a, st);
+    case 1: return launch_decode_t<D, 1>(a, st, e0, e1);
+    case 2: return launch_decode_t<D, 2>(a, st, e0, e1);
+    case 3: return launch_decode_t<D, 3>(a, st, e0, e1);
+    case 4: return launch_decode_t<D, 4>(a, st, e0, e1);
+    case 5: return launch_decode_t<D, 5>(a, st, e0, e1);
+    case 6: return launch_decode_t<D, 6>(a, st, e0, e1);
+    case 7: return launch_decode_t<D, 7>(a, st, e0, e1);
+    case 8: return launch_decode_t<D, 8>(a, st, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }
@@ -517,9 +525,10 @@ bool decode_supported(int head_dim, int group) {
   return (head_dim == 128 || head_dim == 256) && group >= 1 && group <= 8;
 }
 
-hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int group, hipStream_t st) {
-  if (head_dim == 256) return launch_decode_d<256>(a, group, st);
-  if (head_dim == 128) return launch_decode_d<128>(a, group, st);
+hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int group, hipStream_t st, hipEvent_t e0,
+                               hipEvent_t e1) {
+  if (head_dim == 256) return launch_decode_d<256>(a, group, st, e0, e1);
+  if (head_dim == 128) return launch_decode_d<128>(a, group, st, e0, e1);
   return hipErrorInvalidValue;
 }
 

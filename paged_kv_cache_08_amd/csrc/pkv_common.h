@@ -69,8 +69,12 @@ struct DecodeArgs {
 };
 
 // Launchers (decode_kernels.hip, verify_kernels.hip). Return hipError_t.
-hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int group, hipStream_t st);
-hipError_t launch_verify_split(const DecodeArgs& a, int head_dim, int group, hipStream_t st);
+// The split launchers take optional start/stop events, stamped at the start and
+// end of the kernel's execution (hipExtLaunchKernel) when both are non-null.
+hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
+                               hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_verify_split(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
+                               hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_lse_merge(const DecodeArgs& a, int head_dim, hipStream_t st);
 hipError_t launch_debug_offsets(const DecodeArgs& a, int kv_head, int max_seq_len,
                                 int64_t* k_off, int64_t* v_off, hipStream_t st);

@@ -29,6 +29,8 @@
 //   * O (16 rows x D) stays in MFMA accumulators; the split writes it
 //     un-normalised with the row's (max, sum), or normalised when the
 //     sequence has a single split.
+#include <hip/hip_ext.h>
+
 #include "pkv_device.h"
 
 namespace pkv {
@@ -43,6 +45,7 @@ constexpr float kMinitV = -1.0e30f;   // floor of a row's running max (finite: n
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t* lds_short4_ptr;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
@@ -111,10 +114,10 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
   float m_run = kMinitV, l_run = 0.0f;            // stats of row ln
 
   // Tile staging: thread tid moves chunks c = tid + kVThreads * k of K and V.
-  uint4 stk[kLoads], stv[kLoads];
-  auto load_tile = [&](int tile) {
-#pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
+  u32x4_t stk[kLoads], stv[kLoads];   // native vectors: kept in registers
+  auto load_tile = [&](int tile) __attribute__((always_inline)) {
+    static_for<0, kLoads>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
       const int c = tid + kVThreads * k;
       const int tt = c / kChunks, piece = c - tt * kChunks;
       const int t = sp.begin + tile * kVTile + tt;
@@ -123,18 +126,18 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
       const bool ok = token_row(a, tbl, p_first, tc, ko, vo) && t < sp.end;
       const uint16_t* kp = ok ? a.k + ko + piece * 8 : a.q;   // masked rows read q (finite)
       const uint16_t* vp = ok ? a.v + vo + piece * 8 : a.q;
-      stk[k] = *reinterpret_cast<const uint4*>(kp);
-      stv[k] = *reinterpret_cast<const uint4*>(vp);
-    }
+      stk[k] = *reinterpret_cast<const u32x4_t*>(kp);
+      stv[k] = *reinterpret_cast<const u32x4_t*>(vp);
+    });
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
+  auto store_tile = [&](int buf) __attribute__((always_inline)) {
+    static_for<0, kLoads>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
       const int c = tid + kVThreads * k;
       const int tt = c / kChunks, piece = c - tt * kChunks;
-      *reinterpret_cast<uint4*>(&kv[buf][0][tt * kPitch + piece * 16]) = stk[k];
-      *reinterpret_cast<uint4*>(&kv[buf][1][tt * kPitch + piece * 16]) = stv[k];
-    }
+      *reinterpret_cast<u32x4_t*>(&kv[buf][0][tt * kPitch + piece * 16]) = stk[k];
+      *reinterpret_cast<u32x4_t*>(&kv[buf][1][tt * kPitch + piece * 16]) = stv[k];
+    });
   };
 
   const int n_tiles = (sp.end - sp.begin + kVTile - 1) / kVTile;
@@ -197,11 +200,11 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
 #pragma unroll
         for (int r = 0; r < 4; ++r) o[db][r] *= al[r];
       // P as A operands (hi and lo) of the two 32-token halves.
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
+      static_for<0, 2>([&](auto hc) {
+        constexpr int hh = decltype(hc)::value;
         uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        static_for<0, 4>([&](auto tc) {
+          constexpr int t = decltype(tc)::value;
           const float p0 = st[2 * hh + (t >> 1)][(t & 1) * 2];
           const float p1 = st[2 * hh + (t >> 1)][(t & 1) * 2 + 1];
           const uint32_t h0 = bf16_bits(p0), h1 = bf16_bits(p1);
@@ -209,14 +212,14 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
           const uint32_t l1 = bf16_bits(p1 - __uint_as_float(h1 << 16));
           hi[t] = h0 | (h1 << 16);
           lo[t] = l0 | (l1 << 16);
-        }
+        });
         const bf16x8_t ph = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
         const bf16x8_t pl = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
         // V (32 tokens x 16 columns) per column block: two transposed reads.
         const int rowa = (2 * hh) * 16 + 4 * grp + (ln >> 2);
         const int rowb = rowa + 16;
-#pragma unroll
-        for (int db = 0; db < kDBlocks; ++db) {
+        static_for<0, kDBlocks>([&](auto dc) {
+          constexpr int db = decltype(dc)::value;
           const int colb = (16 * db + 4 * (ln & 3)) * 2;
           const short4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_short4_ptr)(kv[buf][1] + rowa * kPitch + colb));
@@ -228,8 +231,8 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
                                       uint32_t(uint16_t(vb2[2])) | (uint32_t(uint16_t(vb2[3])) << 16));
           o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, as_bf16x8(vu), o[db], 0, 0, 0);
           o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, as_bf16x8(vu), o[db], 0, 0, 0);
-        }
-      }
+        });
+      });
     }
     if (more) store_tile(buf ^ 1);
     __syncthreads();
@@ -270,13 +273,18 @@ bool verify_supported(int head_dim, int group, int q_len) {
          group * q_len <= kVWaves * kRowsPerWave;
 }
 
-hipError_t launch_verify_split(const DecodeArgs& a, int head_dim, int group, hipStream_t st) {
+hipError_t launch_verify_split(const DecodeArgs& a, int head_dim, int group, hipStream_t st, hipEvent_t e0,
+                               hipEvent_t e1) {
   if (!verify_supported(head_dim, group, a.q_len)) return hipErrorInvalidValue;
   dim3 grid(a.num_splits, a.hkv, a.num_seqs);
-  if (head_dim == 256)
-    hipLaunchKernelGGL(verify_split_kernel<256>, grid, dim3(kVThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL(verify_split_kernel<128>, grid, dim3(kVThreads), 0, st, a);
+  const bool timed = e0 && e1;
+  if (head_dim == 256) {
+    if (timed) hipExtLaunchKernelGGL(verify_split_kernel<256>, grid, dim3(kVThreads), 0, st, e0, e1, 0, a);
+    else hipLaunchKernelGGL(verify_split_kernel<256>, grid, dim3(kVThreads), 0, st, a);
+  } else {
+    if (timed) hipExtLaunchKernelGGL(verify_split_kernel<128>, grid, dim3(kVThreads), 0, st, e0, e1, 0, a);
+    else hipLaunchKernelGGL(verify_split_kernel<128>, grid, dim3(kVThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -1,0 +1,145 @@
+"""Summaries of rocprofv3 results for this library's kernels.
+
+    python -m paged_kv_cache_08_amd.profiling stats DB...
+        per-kernel dispatch count and duration (avg/min/max, us) from
+        rocprofv3 --kernel-trace result databases, as a markdown table.
+
+    python -m paged_kv_cache_08_amd.profiling traffic --fetch-db DB --write-db DB \\
+            --kernel NAME --calib-bytes N --key KEY --out profiles/traffic.json
+        HBM bytes per dispatch of kernel NAME from one --pmc FETCH_SIZE run and
+        one --pmc WRITE_SIZE run. Each counter is scaled by what it reads for a
+        plain copy of known size in the same run (the largest
+        __amd_rocclr_copyBuffer dispatch, which copies N bytes). The record is
+        stored under KEY with the hash of the kernel sources it was taken on.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import glob
+import hashlib
+import json
+import os
+import sqlite3
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources (file names and contents, sorted)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(PKG, "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def _db(path: str) -> sqlite3.Connection:
+    cand = glob.glob(path) or glob.glob(os.path.join(path, "*.db"))
+    if not cand:
+        raise FileNotFoundError(path)
+    return sqlite3.connect(cand[0])
+
+
+def kernel_durations(path: str) -> dict:
+    """{kernel name: [duration_us, ...]} from a kernel-trace database."""
+    con = _db(path)
+    out = collections.defaultdict(list)
+    for name, dur in con.execute("select name, duration from kernels"):
+        out[name].append(dur / 1e3)
+    return out
+
+
+def pmc_per_dispatch(path: str, counter: str) -> dict:
+    """{kernel name: [per-dispatch value summed over instances, ...]} for one counter."""
+    con = _db(path)
+    per = collections.defaultdict(float)
+    name = {}
+    for did, nm, cn, cv in con.execute("select dispatch_id, name, counter_name, counter_value from pmc_events"):
+        if cn != counter:
+            continue
+        per[did] += cv or 0.0
+        name[did] = nm
+    out = collections.defaultdict(list)
+    for did, v in per.items():
+        out[name[did]].append(v)
+    return out
+
+
+def short(name: str) -> str:
+    n = name.replace("pkv::(anonymous namespace)::", "").replace("void ", "")
+    return n.split("(")[0]
+
+
+def stats_table(paths) -> str:
+    rows = ["| kernel | calls | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
+    for p in paths:
+        for name, d in sorted(kernel_durations(p).items(), key=lambda kv: -sum(kv[1])):
+            rows.append(f"| `{short(name)}` | {len(d)} | {sum(d) / len(d):.2f} | {min(d):.2f} | {max(d):.2f} |")
+    return "\n".join(rows)
+
+
+def traffic(fetch_db: str, write_db: str, kernel: str, calib_bytes: int) -> dict:
+    f = pmc_per_dispatch(fetch_db, "FETCH_SIZE")
+    w = pmc_per_dispatch(write_db, "WRITE_SIZE")
+
+    def pick(d, what):
+        ks = [k for k in d if kernel in k]
+        if not ks:
+            raise KeyError(f"no {what} dispatches of {kernel}")
+        vals = d[ks[0]]
+        cal = max(d.get(next(k for k in d if "copyBuffer" in k), [0.0]))
+        return sum(vals) / len(vals), cal
+
+    fk, fcal = pick(f, "FETCH_SIZE")
+    wk, wcal = pick(w, "WRITE_SIZE")
+    f_scale = calib_bytes / (fcal * 1024.0)
+    w_scale = calib_bytes / (wcal * 1024.0)
+    read_b = fk * 1024.0 * f_scale
+    write_b = wk * 1024.0 * w_scale
+    return {
+        "kernel": kernel,
+        "fetch_kib_raw": round(fk, 1),
+        "write_kib_raw": round(wk, 1),
+        "calib_copy_bytes": calib_bytes,
+        "fetch_scale": round(f_scale, 4),
+        "write_scale": round(w_scale, 4),
+        "read_bytes_per_launch": int(read_b),
+        "write_bytes_per_launch": int(write_b),
+        "hbm_bytes_per_launch": int(read_b + write_b),
+        "kernel_src_sha256": kernel_source_hash(),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("db", nargs="+")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch-db", required=True)
+    t.add_argument("--write-db", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--calib-bytes", type=int, required=True)
+    t.add_argument("--key", required=True)
+    t.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        print(stats_table(a.db))
+        return 0
+    rec = traffic(a.fetch_db, a.write_db, a.kernel, a.calib_bytes)
+    data = {}
+    if os.path.exists(a.out):
+        with open(a.out) as fh:
+            data = json.load(fh)
+    data[a.key] = rec
+    with open(a.out, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+    print(json.dumps(rec, indent=1))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
