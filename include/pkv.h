@@ -87,7 +87,7 @@ const char* pkv_last_error(void);
 /* Host-only check of *p (no HIP call): sizes, group size, head_dim, q_len,
  * strides (positive, multiples of 8 so every K/V row starts on 16 bytes;
  * block_size <= 2^20 and block_size * token stride below 2^31 elements, else
- * PKV_ERR_UNSUPPORTED),
+ * PKV_ERR_UNSUPPORTED), max_seq_len <= 2^30 (else PKV_ERR_UNSUPPORTED) and
  * max_seq_len <= max_pages_per_seq * block_size. Returns PKV_OK or an error. */
 int pkv_validate_params(const pkv_decode_params* p);
 

@@ -143,6 +143,7 @@ int pkv_validate_params(const pkv_decode_params* p) {
     return fail(PKV_ERR_UNSUPPORTED, "decode (q_len 1) needs at most 8 query heads per KV head");
   if (p->q_len > 1 && !pkv::verify_supported(p->head_dim, group, p->q_len))
     return fail(PKV_ERR_UNSUPPORTED, "multi-row calls need (Hq / Hkv) * q_len <= 128");
+  if (p->max_seq_len > (1 << 30)) return fail(PKV_ERR_UNSUPPORTED, "max_seq_len above 2^30 tokens");
   if (int64_t(p->max_pages_per_seq) * p->block_size < p->max_seq_len)
     return fail(PKV_ERR_INVALID, "max_seq_len exceeds max_pages_per_seq * block_size");
   if (!mult8_pos(p->k_stride_page) || !mult8_pos(p->k_stride_tok) || !mult8_pos(p->k_stride_head) ||

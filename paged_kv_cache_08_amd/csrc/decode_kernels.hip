@@ -79,6 +79,35 @@ __device__ __forceinline__ void head_bcast(float x, float (&out)[G]) {
   if constexpr (G > 7) out[7] = row_bcast<14>(x);
 }
 
+// gfx950 lane swaps. swap32(a, b) returns {[a_lo, b_lo], [a_hi, b_hi]} (wave
+// halves of 32 lanes); swap16(a, b) returns {[a0, b0, a2, b2], [a1, b1, a3, b3]}
+// (16-lane rows). With a == b they pair lane l with l ^ 32, or l ^ 16.
+struct Pair {
+  float lo, hi;
+};
+__device__ __forceinline__ Pair swap32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ Pair swap16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+// Max and sum over the 4 rows of a wave (same lane column); every lane gets
+// the result, in a fixed order.
+__device__ __forceinline__ float rows_max(float x) {
+  const Pair p = swap32(x, x);
+  const float y = fmaxf(p.lo, p.hi);
+  const Pair q = swap16(y, y);
+  return fmaxf(q.lo, q.hi);
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const Pair p = swap32(x, x);
+  const float y = p.lo + p.hi;
+  const Pair q = swap16(y, y);
+  return q.lo + q.hi;
+}
+
 // Reduce-scatter of up to 8 per-lane partial sums over the 16 lanes of a row.
 // Partners are lane ^ 15 (row_mirror), ^ 7 (row_half_mirror), ^ 2 and ^ 1
 // (quad_perm); at each step a lane keeps the half of the heads selected by one
@@ -122,28 +151,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   static_assert(G <= 8, "at most 8 query heads per KV head");
 
   __shared__ PageOffs tbl[kTblSplit];
-  __shared__ float mrg_acc[kWaves][G][D];
+  __shared__ __attribute__((aligned(16))) float mrg_acc[kWaves][G][D];
   __shared__ float mrg_ml[kWaves][G][2];
-  __shared__ float mrg_w[kWaves][G];
-  __shared__ float mrg_den[G];
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
-  const SplitSpan sp = split_span(a, b, s);
   const int64_t out_row0 = (int64_t(b) * a.hq + int64_t(g) * G) * D;   // q_len == 1
-
-  if (sp.begin >= sp.L) {
-    if (s == 0)   // empty sequence: zeros
-      for (int i = tid; i < G * D; i += kThreads) store_out(a, out_row0 + i, 0.0f);
-    return;
-  }
-  const int p_first = int(magic_div(uint32_t(sp.begin), a.bdiv));
-  const int p_last = int(magic_div(uint32_t(sp.end - 1), a.bdiv));
-  stage_table(a, b, g, p_first, p_last - p_first + 1, tbl);
-
   const int lane = tid & 63, wave = tid >> 6;
   const int row = lane >> 4, col = lane & 15;
 
+  // The table slots and q do not depend on the sequence length: fetch them
+  // while seq_lens is still in flight.
+  const SplitPages pages = split_pages(a, s);
+  const int p_first = pages.p_first;
+  stage_table(a, b, g, p_first, pages.n, tbl);
   // q of the group's G heads: lane col holds elements [k*128 + col*8, +8) of each head.
   uint4 qv[G][kCpl];
   {
@@ -154,7 +175,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
       for (int k = 0; k < kCpl; ++k)
         qv[h][k] = *reinterpret_cast<const uint4*>(qp + h * D + k * 128);
   }
+
+  const SplitSpan sp = split_span(a, b, s);
+  if (sp.begin >= sp.L) {
+    if (s == 0)   // empty sequence: zeros
+      for (int i = tid; i < G * D; i += kThreads) store_out(a, out_row0 + i, 0.0f);
+    return;
+  }
   __syncthreads();
+  flag_invalid_entries(a, tbl, int(magic_div(uint32_t(sp.end - 1), a.bdiv)) - p_first + 1);
 
   // The split is one window of at most kSubSteps sub-steps of kStep tokens;
   // row `row` of wave `wave` owns tokens begin + j * kStep + my.
@@ -248,7 +277,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   for (int j = 0; j < kSubSteps; ++j) sc[j] = -INFINITY;
   // Loads are issued for every step (a dead step only reads the q row); the
   // arithmetic of steps past n_sub is skipped with uniform branches.
-  static_for<0, kRing - 1>([&](auto jc) {
+  static_for<0, (kRing - 1 < kSteps ? kRing - 1 : kSteps)>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
     if constexpr (j < kSubSteps) fetch_k(j, ring[j % kRing]);
     else fetch_v(j - kSubSteps, ring[j % kRing]);
@@ -275,33 +304,48 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   head_bcast<G>(m_row, m);
   head_bcast<G>(l_row, l);
 
-  // Merge the 4 token rows of each wave (fixed butterfly order).
+  // Merge the wave's 4 token rows: rescale every head to the wave's max, then
+  // reduce-scatter over the rows with lane swaps (wave halves, then row
+  // pairs). Row r of lane column col ends with the sums of elements
+  // e in [r * kEpl / 4, (r + 1) * kEpl / 4) of each head.
+  constexpr int kE2 = kEpl / 2, kE4 = kEpl / 4;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float M = fmaxf(m[h], __shfl_xor(m[h], 16));
-    M = fmaxf(M, __shfl_xor(M, 32));
+    const float M = rows_max(m[h]);
     const float w = fast_exp2(m[h] - M);
-    float lw = l[h] * w;
-    lw += __shfl_xor(lw, 16);
-    lw += __shfl_xor(lw, 32);
-#pragma unroll
-    for (int e = 0; e < kEpl; ++e) {
-      float x = acc[h][e] * w;
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      acc[h][e] = x;
-    }
+    l[h] = rows_sum(l[h] * w);
     m[h] = M;
-    l[h] = lw;
+#pragma unroll
+    for (int e = 0; e < kEpl; ++e) acc[h][e] *= w;
   }
-  if (row == 0) {
+  float part[G][kE4];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+  for (int h = 0; h < G; ++h) {
+    float half[kE2];
 #pragma unroll
-      for (int k = 0; k < kCpl; ++k)
+    for (int e = 0; e < kE2; ++e) {
+      const Pair p = swap32(acc[h][e], acc[h][e + kE2]);
+      half[e] = p.lo + p.hi;
+    }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) mrg_acc[wave][h][k * 128 + col * 8 + j] = acc[h][k * 8 + j];
-    if (col == 0)
+    for (int e = 0; e < kE4; ++e) {
+      const Pair p = swap16(half[e], half[e + kE4]);
+      part[h][e] = p.lo + p.hi;
+    }
+  }
+  {
+    const int e0 = row * kE4;                             // within one 8-element chunk
+    const int d0 = (e0 / 8) * 128 + col * 8 + (e0 % 8);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float* dst = &mrg_acc[wave][h][d0];
+      if constexpr (kE4 == 4) {
+        *reinterpret_cast<float4*>(dst) = make_float4(part[h][0], part[h][1], part[h][2], part[h][3]);
+      } else {
+        *reinterpret_cast<float2*>(dst) = make_float2(part[h][0], part[h][1]);
+      }
+    }
+    if (lane == 0)
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         mrg_ml[wave][h][0] = m[h];
@@ -309,43 +353,32 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
       }
   }
   __syncthreads();
-  // Per-head merge weights of the waves, once.
-  float M_h = 0.0f;
-  if (tid < G) {
-    const int h = tid;
-    float M = mrg_ml[0][h][0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mrg_ml[w][h][0]);
-    float den = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = fast_exp2(mrg_ml[w][h][0] - M);
-      mrg_w[w][h] = f;
-      den += f * mrg_ml[w][h][1];
-    }
-    mrg_den[h] = den;
-    M_h = M;
-  }
-  __syncthreads();
 
-  // Merge the waves (fixed order) and write the split's result.
+  // Merge the waves (fixed order; every thread derives the weights of its
+  // head) and write the split's result.
   const int64_t prow0 = int64_t(b) * a.q_len * a.hq + int64_t(g) * G;   // partial row of head 0, query row 0
   for (int i = tid; i < G * D; i += kThreads) {
     const int h = i / D, d = i - h * D;
-    float num = 0.0f;
+    float M = mrg_ml[0][h][0];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) num += mrg_w[w][h] * mrg_acc[w][h][d];
-    const float den = mrg_den[h];
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mrg_ml[w][h][0]);
+    float num = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = fast_exp2(mrg_ml[w][h][0] - M);
+      den = fmaf(f, mrg_ml[w][h][1], den);
+      num = fmaf(f, mrg_acc[w][h][d], num);
+    }
     if (sp.nsplit == 1) {
       store_out(a, out_row0 + i, den > 0.0f ? num / den : 0.0f);
     } else {
-      a.part_acc[((prow0 + h) * a.num_splits + s) * D + d] = num;
+      const int64_t pr = (prow0 + h) * a.num_splits + s;
+      a.part_acc[pr * D + d] = num;
+      if (d == 0) {
+        a.part_ml[pr * 2] = M;
+        a.part_ml[pr * 2 + 1] = den;
+      }
     }
-  }
-  if (sp.nsplit > 1 && tid < G) {
-    const int64_t pr = (prow0 + tid) * a.num_splits + s;
-    a.part_ml[pr * 2] = M_h;
-    a.part_ml[pr * 2 + 1] = mrg_den[tid];
   }
 }
 
@@ -468,11 +501,11 @@ __global__ __launch_bounds__(kThreads) void debug_offsets_kernel(DecodeArgs a, i
                                                                  int64_t* k_off, int64_t* v_off) {
   __shared__ PageOffs tbl[kTblSplit];
   const int s = blockIdx.x, b = blockIdx.y;
+  const SplitPages pages = split_pages(a, s);
+  const int p_first = pages.p_first;
+  stage_table(a, b, g, p_first, pages.n, tbl);
   const SplitSpan sp = split_span(a, b, s);
   if (sp.begin >= sp.L) return;
-  const int p_first = int(magic_div(uint32_t(sp.begin), a.bdiv));
-  const int p_last = int(magic_div(uint32_t(sp.end - 1), a.bdiv));
-  stage_table(a, b, g, p_first, p_last - p_first + 1, tbl);
   __syncthreads();
   const int t_end = min(sp.end, max_seq_len);
   for (int t = sp.begin + threadIdx.x; t < t_end; t += kThreads) {

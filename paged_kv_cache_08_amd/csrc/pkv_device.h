@@ -50,18 +50,25 @@ struct SplitSpan {
   int nsplit;   // splits this sequence uses
 };
 
-// Split s of sequence b: [s * chunk, min((s + 1) * chunk, L)). L is clamped to
-// what the block table can map and to what the planned splits cover, so a
+// Longest token range the launch can map: what the block table can address
+// and what the planned splits cover. A sequence length is clamped to it, so a
 // length above the host's max_seq_len can never index past the table, the
 // grid or the workspace.
-__device__ __forceinline__ SplitSpan split_span(const DecodeArgs& a, int b, int s) {
-  int64_t cap = int64_t(a.max_pages) * int64_t(a.bdiv.d);
+// (The host keeps max_seq_len <= 2^30, so the planned range fits an int.)
+__device__ __forceinline__ int planned_cap(const DecodeArgs& a) {
+  const int64_t cap = int64_t(a.max_pages) * int64_t(a.bdiv.d);
   const int64_t planned = int64_t(a.num_splits) * a.chunk;
-  cap = cap < planned ? cap : planned;
-  int64_t L = a.seq_lens[b];
+  return int(cap < planned ? cap : planned);
+}
+
+// Split s of sequence b: [s * chunk, min((s + 1) * chunk, L)), L clamped to
+// planned_cap().
+__device__ __forceinline__ SplitSpan split_span(const DecodeArgs& a, int b, int s) {
+  const int cap = planned_cap(a);
+  int L = a.seq_lens[b];
   L = L < 0 ? 0 : (L > cap ? cap : L);
   SplitSpan r;
-  r.L = int(L);
+  r.L = L;
   r.begin = s * a.chunk;
   r.end = min(r.begin + a.chunk, r.L);
   r.nsplit = (r.L + a.chunk - 1) / a.chunk;
@@ -75,9 +82,29 @@ struct PageOffs {
   int64_t v;
 };
 
+// Block-table slots split s may touch, from the launch plan alone: the pages
+// of [s * chunk, min((s + 1) * chunk, planned_cap())). They contain the pages
+// of the split's real range (which also depends on seq_lens) and start at the
+// same page, so the table can be fetched while seq_lens is still in flight.
+struct SplitPages {
+  int p_first;
+  int n;   // 0: the split is empty for every sequence length
+};
+
+__device__ __forceinline__ SplitPages split_pages(const DecodeArgs& a, int s) {
+  const int begin = s * a.chunk;
+  const int end = min(begin + a.chunk, planned_cap(a));
+  SplitPages r;
+  r.p_first = int(magic_div(uint32_t(begin), a.bdiv));
+  r.n = end > begin ? int(magic_div(uint32_t(end - 1), a.bdiv)) - r.p_first + 1 : 0;
+  return r;
+}
+
 // Stage block-table entries [p_first, p_first + n) of sequence b in LDS as
 // page offsets of KV head g. Entries outside [0, num_pages) are marked invalid
-// (their tokens are skipped) and set bit 0 of the workspace error word.
+// (k = v = -1); only those the split really reads are reported, by
+// flag_invalid_entries() once the sequence length is known. Entries past the
+// sequence's last page are never dereferenced.
 __device__ __forceinline__ void stage_table(const DecodeArgs& a, int b, int g, int p_first, int n,
                                             PageOffs* tbl) {
   const int32_t* row = a.table + int64_t(b) * a.max_pages + p_first;
@@ -85,7 +112,6 @@ __device__ __forceinline__ void stage_table(const DecodeArgs& a, int b, int g, i
     const int e = row[i];
     PageOffs po;
     if (uint32_t(e) >= uint32_t(a.num_pages)) {
-      if (a.err) atomicOr(a.err, 1u);
       po.k = -1;
       po.v = -1;
     } else {
@@ -94,6 +120,15 @@ __device__ __forceinline__ void stage_table(const DecodeArgs& a, int b, int g, i
     }
     tbl[i] = po;
   }
+}
+
+// Set bit 0 of the workspace error word if one of the first n staged entries
+// (the pages of the split's real range) is invalid. Call after the barrier
+// that publishes the staged table.
+__device__ __forceinline__ void flag_invalid_entries(const DecodeArgs& a, const PageOffs* tbl, int n) {
+  if (!a.err) return;
+  for (int i = threadIdx.x; i < n; i += blockDim.x)
+    if (tbl[i].k < 0) atomicOr(a.err, 1u);
 }
 
 // Element offsets of token t's K and V rows; false if its page entry is

@@ -74,6 +74,11 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
   const int q_len = a.q_len;
   const int G = a.hq / a.hkv;
   const int R = G * q_len;                        // rows of this KV head (<= 128)
+  // The table slots do not depend on the sequence length: fetch them while
+  // seq_lens is still in flight.
+  const SplitPages pages = split_pages(a, s);
+  const int p_first = pages.p_first;
+  stage_table(a, b, g, p_first, pages.n, tbl);
   const SplitSpan sp = split_span(a, b, s);
 
   if (sp.begin >= sp.L) {
@@ -85,9 +90,6 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
       }
     return;
   }
-  const int p_first = int(magic_div(uint32_t(sp.begin), a.bdiv));
-  const int p_last = int(magic_div(uint32_t(sp.end - 1), a.bdiv));
-  stage_table(a, b, g, p_first, p_last - p_first + 1, tbl);
 
   // This lane's S^T row (row ln of the wave's block).
   const bool computes = wave * kRowsPerWave < R;  // uniform per wave
@@ -107,6 +109,7 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
                                          : make_uint4(0, 0, 0, 0);
   }
   __syncthreads();   // table staged
+  flag_invalid_entries(a, tbl, int(magic_div(uint32_t(sp.end - 1), a.bdiv)) - p_first + 1);
 
   float4_t o[kDBlocks];
 #pragma unroll
