@@ -227,7 +227,7 @@ def _cdiv(a: int, b: int) -> int:
 
 def split_plan_ref(num_seqs: int, num_kv_heads: int, max_seq_len: int, block_size: int,
                    cu_count: int, *, total_tokens: int = 0, forced_splits: int = 0,
-                   tile: int = 64, wg_per_cu: int = 1, min_tiles: int = 2,
+                   tile: int = 64, wg_per_cu: int = 1, min_tiles: int = 1,
                    max_tiles: int = 8) -> tuple[int, int]:
     """Return (S, chunk_tokens). block_size does not enter the plan."""
     n_tiles = max(1, _cdiv(max_seq_len, tile))

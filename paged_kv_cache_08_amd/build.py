@@ -14,7 +14,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
-SOURCES = ["api.hip", "decode_kernels.hip", "verify_kernels.hip"]
+# The 512-token split kernels are the slowest to compile: listed first.
+SOURCES = ["decode_w512.hip", "decode_w256.hip", "verify_kernels.hip", "decode_w128.hip", "decode_w64.hip",
+           "decode_kernels.hip", "api.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

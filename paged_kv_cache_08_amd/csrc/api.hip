@@ -16,7 +16,7 @@ namespace {
 thread_local std::string g_last_error;
 struct VariantInfo {
   const char* split_name = nullptr;
-  int head_dim = 0, group = 0, q_len = 0, splits = 0, chunk = 0, block_size = 0;
+  int head_dim = 0, group = 0, q_len = 0, window = 0, splits = 0, chunk = 0, block_size = 0;
 };
 thread_local VariantInfo g_last_variant;
 thread_local hipEvent_t g_ev_start = nullptr;
@@ -228,19 +228,22 @@ int pkv_paged_decode_attention(const pkv_decode_params* p, const void* q, const 
   const int group = p->num_q_heads / p->num_kv_heads;
   hipError_t e;
   const char* split_name;
+  int window;
   if (p->q_len == 1) {
     e = pkv::launch_decode_split(a, p->head_dim, group, st, g_ev_start, g_ev_stop);
     split_name = "decode_valu";
+    window = pkv::decode_window(chunk);
   } else {
     e = pkv::launch_verify_split(a, p->head_dim, group, st, g_ev_start, g_ev_stop);
     split_name = "verify_mfma";
+    window = 64;   // 64-token K/V tiles, looped over the split
   }
   if (e != hipSuccess) return hip_fail(e, "split kernel launch");
   if (S > 1) {
     e = pkv::launch_lse_merge(a, p->head_dim, st);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
   }
-  g_last_variant = VariantInfo{split_name, p->head_dim, group, p->q_len, S, chunk, p->block_size};
+  g_last_variant = VariantInfo{split_name, p->head_dim, group, p->q_len, window, S, chunk, p->block_size};
   return PKV_OK;
 }
 
@@ -249,8 +252,8 @@ int pkv_last_variant(char* buf, int32_t len) {
   char tmp[256];
   int n = 0;
   if (v.split_name)
-    n = snprintf(tmp, sizeof tmp, "%s d%d g%d q%d%s splits=%d chunk=%d B=%d", v.split_name, v.head_dim, v.group,
-                 v.q_len, v.splits > 1 ? " + lse_merge" : "", v.splits, v.chunk, v.block_size);
+    n = snprintf(tmp, sizeof tmp, "%s d%d g%d q%d w%d%s splits=%d chunk=%d B=%d", v.split_name, v.head_dim,
+                 v.group, v.q_len, v.window, v.splits > 1 ? " + lse_merge" : "", v.splits, v.chunk, v.block_size);
   else
     tmp[0] = '\0';
   if (buf && len > 0) {

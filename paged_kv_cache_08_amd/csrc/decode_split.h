@@ -1,0 +1,428 @@
+// The single-query split kernel for gfx950 (wave64, CDNA4), templated on
+// head_dim D, group size G (query heads per KV head) and window NS (sub-steps
+// of 32 tokens; a split holds at most NS * 32 tokens). Each window size is
+// instantiated in its own source file (decode_w64.hip .. decode_w512.hip) so
+// the fully unrolled kernels compile in parallel.
+//
+// What is computed follows "DCU page832 attention" (luanjiahao.me): §1 and §5
+// for the address of a token row (logical page = t / B, offset = t % B,
+// physical page from the block table, then page / token / head strides), §5
+// for score = dot(q, k) * scale with a softmax-weighted sum of V, and §7 for
+// the fact that decode walks every logical page. The split of one (sequence,
+// KV head) context over many workgroups, merged afterwards, is the split-KV
+// paragraph of "vLLM 下双卡 Radeon 上的混合 SSM 解码速率".
+//
+// Work mapping (one workgroup = one split of one (sequence, KV head)):
+//   * 8 waves (2 per SIMD) x 4 token rows per wave: 32 consecutive logical
+//     tokens per sub-step, one token row per 16-lane DPP row. Each lane owns
+//     D/16 head-dim elements of its row and loads them with 16-byte global
+//     loads (a 512-byte K row of D = 256 is read by 16 lanes in two fully used
+//     256-byte segments). The G query heads of the group all use the row held
+//     in registers, so K and V are fetched once per group.
+//   * The split is one window, fully unrolled: a K pass over its NS sub-steps,
+//     then a V pass over the same tokens. Loads run through a ring of register
+//     buffers that spans both passes, so the first V loads are in flight while
+//     the last scores are computed. Loads are branch-free: a masked row (past
+//     the split end, or an invalid page entry) reads the q row instead.
+//   * K pass: q.k partial sums are reduced across the 16 lanes of a row with a
+//     DPP reduce-scatter (row_mirror, row_half_mirror, quad_perm); lanes 2h and
+//     2h + 1 keep head h's score, in log2 units.
+//   * V pass: with the exact maximum of the lane's own window scores, each
+//     probability is computed once per (token, head), broadcast to the row with
+//     DPP row_newbcast, and accumulated with fp32 FMAs.
+//   * Page offsets (page * page_stride + head * head_stride, for K and V) are
+//     staged in LDS once per split, fetched while seq_lens is still in flight;
+//     a token then costs one division by the page size (multiply-high), one
+//     LDS read and a 32-bit multiply-add.
+//   * Epilogue: the 4 token rows of a wave are merged by a reduce-scatter over
+//     lane swaps (v_permlane32_swap, v_permlane16_swap), the 8 waves through
+//     LDS, in a fixed order; the split's (max, sum, accumulator) go to the
+//     workspace, or the normalised output directly when the sequence has a
+//     single split.
+// Every reduction order depends only on logical token indices and the split
+// plan, never on block_size or physical page ids, so the same logical K/V gives
+// bitwise-identical output for any page size or page placement.
+#pragma once
+
+#include <math.h>
+
+#include <hip/hip_ext.h>
+
+#include "pkv_device.h"
+
+namespace pkv {
+namespace {
+
+
+constexpr int kWaves = 8;                      // 2 waves per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int kLanesPerRow = 16;
+constexpr int kRowsPerWave = 64 / kLanesPerRow;
+constexpr int kStep = kWaves * kRowsPerWave;   // tokens per workgroup sub-step
+// Register ring depth (steps in flight + 1); shallower where G * D leaves
+// fewer registers (depths 4..10 measured alike at G = 6, D = 256).
+constexpr int ring_depth(int D, int G) { return (D == 256 && G >= 7) ? 3 : 6; }
+constexpr int kTblSplit = kMaxChunk + 2;       // page entries one split can span (B = 1)
+constexpr float kMinit = -1.0e30f;             // floor of a row's max (finite: no inf - inf)
+
+// Lane n of each 16-lane row, broadcast to the whole row (DPP row_newbcast).
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+  return dpp_move<0x150 + N>(x);
+}
+
+// out[h] = value held by lane 2h of the row (the lanes that own head h after
+// the reduce-scatter below).
+template <int G>
+__device__ __forceinline__ void head_bcast(float x, float (&out)[G]) {
+  if constexpr (G > 0) out[0] = row_bcast<0>(x);
+  if constexpr (G > 1) out[1] = row_bcast<2>(x);
+  if constexpr (G > 2) out[2] = row_bcast<4>(x);
+  if constexpr (G > 3) out[3] = row_bcast<6>(x);
+  if constexpr (G > 4) out[4] = row_bcast<8>(x);
+  if constexpr (G > 5) out[5] = row_bcast<10>(x);
+  if constexpr (G > 6) out[6] = row_bcast<12>(x);
+  if constexpr (G > 7) out[7] = row_bcast<14>(x);
+}
+
+// gfx950 lane swaps. swap32(a, b) returns {[a_lo, b_lo], [a_hi, b_hi]} (wave
+// halves of 32 lanes); swap16(a, b) returns {[a0, b0, a2, b2], [a1, b1, a3, b3]}
+// (16-lane rows). With a == b they pair lane l with l ^ 32, or l ^ 16.
+struct Pair {
+  float lo, hi;
+};
+__device__ __forceinline__ Pair swap32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ Pair swap16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+// Max and sum over the 4 rows of a wave (same lane column); every lane gets
+// the result, in a fixed order.
+__device__ __forceinline__ float rows_max(float x) {
+  const Pair p = swap32(x, x);
+  const float y = fmaxf(p.lo, p.hi);
+  const Pair q = swap16(y, y);
+  return fmaxf(q.lo, q.hi);
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const Pair p = swap32(x, x);
+  const float y = p.lo + p.hi;
+  const Pair q = swap16(y, y);
+  return q.lo + q.hi;
+}
+
+// Reduce-scatter of up to 8 per-lane partial sums over the 16 lanes of a row.
+// Partners are lane ^ 15 (row_mirror), ^ 7 (row_half_mirror), ^ 2 and ^ 1
+// (quad_perm); at each step a lane keeps the half of the heads selected by one
+// bit of its lane index and receives its partner's copy of that half. Lanes 2h
+// and 2h + 1 end with the full sum of head h (bitwise equal); the order of the
+// additions depends only on the lane index.
+template <int G>
+__device__ __forceinline__ float reduce_scatter16(const float (&x)[G], int col) {
+  float y[4], z[2];
+  const bool b3 = col >= 8, b2 = (col & 4) != 0, b1 = (col & 2) != 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float lo = j < G ? x[j] : 0.0f;
+    const float hi = j + 4 < G ? x[j + 4] : 0.0f;
+    const float keep = b3 ? hi : lo;
+    const float send = b3 ? lo : hi;
+    y[j] = keep + dpp_move<0x140>(send);   // row_mirror
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float keep = b2 ? y[j + 2] : y[j];
+    const float send = b2 ? y[j] : y[j + 2];
+    z[j] = keep + dpp_move<0x141>(send);   // row_half_mirror
+  }
+  float w;
+  {
+    const float keep = b1 ? z[1] : z[0];
+    const float send = b1 ? z[0] : z[1];
+    w = keep + dpp_move<0x4E>(send);       // quad_perm [2,3,0,1]
+  }
+  return w + dpp_move<0xB1>(w);            // quad_perm [1,0,3,2]
+}
+
+template <int D, int G, int kSubSteps>
+__global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a) {
+  constexpr int kEpl = D / kLanesPerRow;   // head-dim elements per lane: 16 or 8
+  constexpr int kCpl = kEpl / 8;           // 16-byte chunks per lane: 2 or 1
+  constexpr int kSteps = 2 * kSubSteps;    // K pass, then V pass
+  constexpr int kRing = ring_depth(D, G);
+  static_assert(kCpl >= 1 && kEpl % 8 == 0, "head_dim must be a multiple of 128");
+  static_assert(G <= 8, "at most 8 query heads per KV head");
+  static_assert(kSubSteps >= 1 && kSubSteps * kStep <= kMaxChunk, "window of at most kMaxChunk tokens");
+
+  __shared__ PageOffs tbl[kTblSplit];
+  __shared__ __attribute__((aligned(16))) float mrg_acc[kWaves][G][D];
+  __shared__ float mrg_ml[kWaves][G][2];
+
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int64_t out_row0 = (int64_t(b) * a.hq + int64_t(g) * G) * D;   // q_len == 1
+  const int lane = tid & 63, wave = tid >> 6;
+  const int row = lane >> 4, col = lane & 15;
+
+  // The table slots and q do not depend on the sequence length: fetch them
+  // while seq_lens is still in flight.
+  const SplitPages pages = split_pages(a, s);
+  const int p_first = pages.p_first;
+  stage_table(a, b, g, p_first, pages.n, tbl);
+  // q of the group's G heads: lane col holds elements [k*128 + col*8, +8) of each head.
+  uint4 qv[G][kCpl];
+  {
+    const uint16_t* qp = a.q + out_row0 + col * 8;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int k = 0; k < kCpl; ++k)
+        qv[h][k] = *reinterpret_cast<const uint4*>(qp + h * D + k * 128);
+  }
+
+  const SplitSpan sp = split_span(a, b, s);
+  if (sp.begin >= sp.L) {
+    if (s == 0)   // empty sequence: zeros
+      for (int i = tid; i < G * D; i += kThreads) store_out(a, out_row0 + i, 0.0f);
+    return;
+  }
+  __syncthreads();
+  flag_invalid_entries(a, tbl, int(magic_div(uint32_t(sp.end - 1), a.bdiv)) - p_first + 1);
+
+  // The split is one window of at most kSubSteps sub-steps of kStep tokens;
+  // row `row` of wave `wave` owns tokens begin + j * kStep + my.
+  const int my = wave * kRowsPerWave + row;
+  const int n_sub = (sp.end - sp.begin + kStep - 1) / kStep;   // uniform, <= kSubSteps
+
+  float acc[G][kEpl];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < kEpl; ++e) acc[h][e] = 0.0f;
+  float sc[kSubSteps];        // score of head (col / 2) for each sub-step's token (log2 units)
+  uint32_t tix[kSubSteps];    // (table slot << 20) | in-page offset of that token; ~0u if masked
+  float m_row = kMinit, l_row = 0.0f;
+
+  const uint16_t* const safe_row = a.q + out_row0 + col * 8;   // finite, in bounds
+  uint4 ring[kRing][kCpl];
+
+  // K step j: locate the token, remember where it is (tix: bit 31 = masked,
+  // bits 20..30 = table slot, bits 0..19 = in-page offset), load its K chunk.
+  // Branch-free: a masked row (past the split end, or an invalid page entry)
+  // reads the q row instead.
+  auto fetch_k = [&](int j, uint4 (&buf)[kCpl]) {
+    const int t = sp.begin + j * kStep + my;
+    const int tc = min(t, sp.end - 1);
+    const uint32_t pg = magic_div(uint32_t(tc), a.bdiv);
+    const int off = tc - int(pg * a.bdiv.d);
+    const int slot = int(pg) - p_first;
+    const int64_t pk = tbl[slot].k;
+    const bool ok = (t < sp.end) && pk >= 0;
+    tix[j] = (ok ? 0u : 0x80000000u) | (uint32_t(slot) << 20) | uint32_t(off);
+    const uint16_t* real = a.k + (pk + int64_t(off * int32_t(a.k_st))) + col * 8;
+    const uint16_t* kp = ok ? real : safe_row;
+#pragma unroll
+    for (int k = 0; k < kCpl; ++k) buf[k] = *reinterpret_cast<const uint4*>(kp + k * 128);
+  };
+  // V step j: the same token's V chunk (the slot of a masked row is still a
+  // staged entry, so the LDS read is in range).
+  auto fetch_v = [&](int j, uint4 (&buf)[kCpl]) {
+    const uint32_t ti = tix[j];
+    const int slot = int((ti >> 20) & 0x7ffu), off = int(ti & 0xfffffu);
+    const uint16_t* real = a.v + (tbl[slot].v + int64_t(off * int32_t(a.v_st))) + col * 8;
+    const uint16_t* vp = (ti & 0x80000000u) ? safe_row : real;
+#pragma unroll
+    for (int k = 0; k < kCpl; ++k) buf[k] = *reinterpret_cast<const uint4*>(vp + k * 128);
+  };
+  // q.k of the G heads; lanes 2h, 2h+1 keep head h's score.
+  auto consume_k = [&](int j, const uint4 (&kk)[kCpl]) {
+    float dq[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float d0 = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kCpl; ++k) {
+        d0 = dot2_bf16(qv[h][k].x, kk[k].x, d0);
+        d0 = dot2_bf16(qv[h][k].y, kk[k].y, d0);
+        d0 = dot2_bf16(qv[h][k].z, kk[k].z, d0);
+        d0 = dot2_bf16(qv[h][k].w, kk[k].w, d0);
+      }
+      dq[h] = d0;
+    }
+    const float r = reduce_scatter16<G>(dq, col) * a.scale_log2;
+    sc[j] = (tix[j] & 0x80000000u) ? -INFINITY : r;
+  };
+  // p of head (col / 2), broadcast to the row, V accumulation.
+  auto consume_v = [&](int j, const uint4 (&vv)[kCpl]) {
+    const float pl = fast_exp2(sc[j] - m_row);
+    l_row += pl;
+    float p[G];
+    head_bcast<G>(pl, p);
+#pragma unroll
+    for (int k = 0; k < kCpl; ++k) {
+      const uint32_t w4[4] = {vv[k].x, vv[k].y, vv[k].z, vv[k].w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float v0 = bf16_lo(w4[w]), v1 = bf16_hi(w4[w]);
+        const int e = k * 8 + w * 2;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          acc[h][e] = fmaf(p[h], v0, acc[h][e]);
+          acc[h][e + 1] = fmaf(p[h], v1, acc[h][e + 1]);
+        }
+      }
+    }
+  };
+  // One stream of 2 * kSubSteps steps (K pass, then V pass) through a ring of
+  // kRing register buffers: kRing - 1 steps of loads stay in flight. Fully
+  // unrolled, so every buffer lives in fixed registers; steps past n_sub are
+  // skipped with uniform branches.
+#pragma unroll
+  for (int j = 0; j < kSubSteps; ++j) sc[j] = -INFINITY;
+  // Loads are issued for every step (a dead step only reads the q row); the
+  // arithmetic of steps past n_sub is skipped with uniform branches.
+  static_for<0, (kRing - 1 < kSteps ? kRing - 1 : kSteps)>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    if constexpr (j < kSubSteps) fetch_k(j, ring[j % kRing]);
+    else fetch_v(j - kSubSteps, ring[j % kRing]);
+  });
+  static_for<0, kSteps>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    constexpr int jn = j + kRing - 1;
+    if constexpr (jn < kSteps) {
+      if constexpr (jn < kSubSteps) fetch_k(jn, ring[jn % kRing]);
+      else fetch_v(jn - kSubSteps, ring[jn % kRing]);
+    }
+    if ((j < kSubSteps ? j : j - kSubSteps) < n_sub) {
+      if constexpr (j < kSubSteps) consume_k(j, ring[j % kRing]);
+      else consume_v(j - kSubSteps, ring[j % kRing]);
+    }
+    if constexpr (j == kSubSteps - 1) {
+#pragma unroll
+      for (int i = 0; i < kSubSteps; ++i) m_row = fmaxf(m_row, sc[i]);
+    }
+  });
+
+  // Row state per head, from lanes 2h of each row.
+  float m[G], l[G];
+  head_bcast<G>(m_row, m);
+  head_bcast<G>(l_row, l);
+
+  // Merge the wave's 4 token rows: rescale every head to the wave's max, then
+  // reduce-scatter over the rows with lane swaps (wave halves, then row
+  // pairs). Row r of lane column col ends with the sums of elements
+  // e in [r * kEpl / 4, (r + 1) * kEpl / 4) of each head.
+  constexpr int kE2 = kEpl / 2, kE4 = kEpl / 4;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float M = rows_max(m[h]);
+    const float w = fast_exp2(m[h] - M);
+    l[h] = rows_sum(l[h] * w);
+    m[h] = M;
+#pragma unroll
+    for (int e = 0; e < kEpl; ++e) acc[h][e] *= w;
+  }
+  float part[G][kE4];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float half[kE2];
+#pragma unroll
+    for (int e = 0; e < kE2; ++e) {
+      const Pair p = swap32(acc[h][e], acc[h][e + kE2]);
+      half[e] = p.lo + p.hi;
+    }
+#pragma unroll
+    for (int e = 0; e < kE4; ++e) {
+      const Pair p = swap16(half[e], half[e + kE4]);
+      part[h][e] = p.lo + p.hi;
+    }
+  }
+  {
+    const int e0 = row * kE4;                             // within one 8-element chunk
+    const int d0 = (e0 / 8) * 128 + col * 8 + (e0 % 8);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float* dst = &mrg_acc[wave][h][d0];
+      if constexpr (kE4 == 4) {
+        *reinterpret_cast<float4*>(dst) = make_float4(part[h][0], part[h][1], part[h][2], part[h][3]);
+      } else {
+        *reinterpret_cast<float2*>(dst) = make_float2(part[h][0], part[h][1]);
+      }
+    }
+    if (lane == 0)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        mrg_ml[wave][h][0] = m[h];
+        mrg_ml[wave][h][1] = l[h];
+      }
+  }
+  __syncthreads();
+
+  // Merge the waves (fixed order; every thread derives the weights of its
+  // head) and write the split's result.
+  const int64_t prow0 = int64_t(b) * a.q_len * a.hq + int64_t(g) * G;   // partial row of head 0, query row 0
+  for (int i = tid; i < G * D; i += kThreads) {
+    const int h = i / D, d = i - h * D;
+    float M = mrg_ml[0][h][0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mrg_ml[w][h][0]);
+    float num = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = fast_exp2(mrg_ml[w][h][0] - M);
+      den = fmaf(f, mrg_ml[w][h][1], den);
+      num = fmaf(f, mrg_acc[w][h][d], num);
+    }
+    if (sp.nsplit == 1) {
+      store_out(a, out_row0 + i, den > 0.0f ? num / den : 0.0f);
+    } else {
+      const int64_t pr = (prow0 + h) * a.num_splits + s;
+      a.part_acc[pr * D + d] = num;
+      if (d == 0) {
+        a.part_ml[pr * 2] = M;
+        a.part_ml[pr * 2 + 1] = den;
+      }
+    }
+  }
+}
+
+template <int D, int G, int NS>
+hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  dim3 grid(a.num_splits, a.hkv, a.num_seqs);
+  if (e0 && e1)
+    hipExtLaunchKernelGGL((decode_split_kernel<D, G, NS>), grid, dim3(kThreads), 0, st, e0, e1, 0, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<D, G, NS>), grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D, int NS>
+hipError_t launch_decode_d(const DecodeArgs& a, int group, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  switch (group) {
+    case 1: return launch_decode_t<D, 1, NS>(a, st, e0, e1);
+    case 2: return launch_decode_t<D, 2, NS>(a, st, e0, e1);
+    case 3: return launch_decode_t<D, 3, NS>(a, st, e0, e1);
+    case 4: return launch_decode_t<D, 4, NS>(a, st, e0, e1);
+    case 5: return launch_decode_t<D, 5, NS>(a, st, e0, e1);
+    case 6: return launch_decode_t<D, 6, NS>(a, st, e0, e1);
+    case 7: return launch_decode_t<D, 7, NS>(a, st, e0, e1);
+    case 8: return launch_decode_t<D, 8, NS>(a, st, e0, e1);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Launch the split kernel with a window of NS sub-steps (a.chunk <= NS * 32).
+template <int NS>
+hipError_t launch_decode_window(const DecodeArgs& a, int head_dim, int group, hipStream_t st, hipEvent_t e0,
+                                hipEvent_t e1) {
+  if (a.chunk > NS * kStep) return hipErrorInvalidValue;
+  if (head_dim == 256) return launch_decode_d<256, NS>(a, group, st, e0, e1);
+  if (head_dim == 128) return launch_decode_d<128, NS>(a, group, st, e0, e1);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+}  // namespace pkv

@@ -9,7 +9,7 @@ namespace pkv {
 // Split planner constants (the plan itself is documented in include/pkv.h).
 constexpr int kTile = 64;        // split boundaries are multiples of this many tokens
 constexpr int kWgPerCu = 1;      // planner target: this many split workgroups per CU
-constexpr int kMinTiles = 2;     // a split covers at least this many tiles when planned
+constexpr int kMinTiles = 1;     // a split covers at least this many tiles when planned
 constexpr int kMaxTiles = 8;     // a split covers at most this many tiles (one kernel window)
 constexpr int kMaxChunk = kMaxTiles * kTile;
 
@@ -68,11 +68,22 @@ struct DecodeArgs {
   int32_t out_bf16;
 };
 
-// Launchers (decode_kernels.hip, verify_kernels.hip). Return hipError_t.
-// The split launchers take optional start/stop events, stamped at the start and
-// end of the kernel's execution (hipExtLaunchKernel) when both are non-null.
+// Launchers (decode_kernels.hip, decode_w*.hip, verify_kernels.hip). Return
+// hipError_t. The split launchers take optional start/stop events, stamped at
+// the start and end of the kernel's execution (hipExtLaunchKernel) when both
+// are non-null. launch_decode_split picks the smallest window (64, 128, 256 or
+// 512 tokens, decode_window()) that holds a split of a.chunk tokens.
+int decode_window(int chunk);
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
                                hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_decode_split_w64(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
+                                   hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_decode_split_w128(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
+                                    hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_decode_split_w256(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
+                                    hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_decode_split_w512(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
+                                    hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_verify_split(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
                                hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_lse_merge(const DecodeArgs& a, int head_dim, hipStream_t st);

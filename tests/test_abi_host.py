@@ -81,7 +81,7 @@ def test_validation_codes(kw, code):
 
 
 def test_plan_constants_are_the_documented_ones():
-    assert P.plan_constants() == dict(tile=64, wg_per_cu=1, min_tiles=2, max_tiles=8)
+    assert P.plan_constants() == dict(tile=64, wg_per_cu=1, min_tiles=1, max_tiles=8)
 
 
 PLAN = [

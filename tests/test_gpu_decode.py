@@ -78,13 +78,18 @@ def test_dense_control_d128_gqa4():
     assert_matches_oracle(run_gpu(case), oracle_out(case), "dense control")
 
 
-@pytest.mark.parametrize("splits", [1, 4, 64, 256])
+# Forced split counts at 16384 tokens give chunks of 512, 320, 256, 192, 128 and
+# 64 tokens, so every kernel window (64, 128, 256, 512 tokens) runs, full and
+# with dead sub-steps.
+@pytest.mark.parametrize("splits", [1, 4, 52, 64, 86, 128, 256])
 def test_forced_split_counts_agree(splits):
     import paged_kv_cache_08_amd as P
     log(f"case: context 16384, page 784, {splits} splits")
     case = hybrid(16384)
     got = run_gpu(case, num_splits=splits)
     S, chunk = O.split_plan_ref(1, 4, 16384, 784, P.device_cu_count(), forced_splits=splits)
+    window = next(w for w in (64, 128, 256, 512) if chunk <= w)
+    assert f" w{window} " in P.last_variant()
     assert f"splits={S} chunk={chunk} " in P.last_variant()
     assert_matches_oracle(got, oracle_out(case), f"S={splits}")
 

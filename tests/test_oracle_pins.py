@@ -377,7 +377,11 @@ def test_split_plan_invariants(ns, hkv, L, bs, cu, total, forced):
 def test_split_plan_headline_shape():
     # 32K tokens x 4 KV heads spread over 256 CUs: 64 splits of 512 tokens per KV head.
     assert O.split_plan_ref(1, 4, 32768, 784, 256) == (64, 512)
-    assert O.split_plan_ref(1, 4, 512, 16, 256) == (4, 128)
+    # Shorter contexts: ceil(4 * L / (256 * 64)) tiles per split, at least one.
+    assert O.split_plan_ref(1, 4, 16384, 784, 256) == (64, 256)
+    assert O.split_plan_ref(1, 4, 4096, 784, 256) == (64, 64)
+    assert O.split_plan_ref(1, 4, 1024, 784, 256) == (16, 64)
+    assert O.split_plan_ref(1, 4, 512, 16, 256) == (8, 64)
 
 
 # ---------------------------------------------------------------------------
