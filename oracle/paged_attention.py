@@ -100,6 +100,23 @@ def gather_token_rows(cache, table_row, n_tokens: int, block_size: int, kv_head:
 # Attention by definition.
 # ---------------------------------------------------------------------------
 
+def kv_head_of(h: int, group: int) -> int:
+    """KV head of query head h: consecutive groups of `group` query heads share
+    one KV head (the pages give 24 query / 4 KV heads, group 6, and no order)."""
+    return h // group
+
+
+def last_visible(L: int, q_len: int, i: int) -> int:
+    """Last token query row i sees: the q_len new rows are the last q_len
+    tokens of the cache (bottom-right alignment); at q_len 1 that is L - 1."""
+    return L - q_len + i
+
+
+def _scaled_scores(keys: np.ndarray, qv: np.ndarray, sigma: float) -> np.ndarray:
+    """score_j = sigma * dot(q, k_j) (the DCU page, §5)."""
+    return sigma * (keys @ qv)
+
+
 def _softmax_weighted_sum(scores: np.ndarray, values: np.ndarray) -> np.ndarray:
     """sum_j exp(s_j - max s) v_j / sum_j exp(s_j - max s) for one row of scores."""
     if scores.size == 0:
@@ -128,15 +145,15 @@ def paged_attention_ref(q, k_cache, v_cache, block_table, seq_lens, block_size: 
         if L == 0:
             continue
         assert L >= q_len, "a sequence must hold at least its q_len new tokens"
-        for g in range(hkv):
-            K = gather_token_rows(k_cache, block_table[b], L, block_size, g)
-            V = gather_token_rows(v_cache, block_table[b], L, block_size, g)
-            for i in range(q_len):
-                pos = L - q_len + i                   # last visible token of row i
-                for h in range(g * G, (g + 1) * G):
-                    qv = bf16_bits_to_f64(q[b, i, h])
-                    s = sigma * (K[: pos + 1] @ qv)
-                    out[b, i, h] = _softmax_weighted_sum(s, V[: pos + 1])
+        K = [gather_token_rows(k_cache, block_table[b], L, block_size, g) for g in range(hkv)]
+        V = [gather_token_rows(v_cache, block_table[b], L, block_size, g) for g in range(hkv)]
+        for i in range(q_len):
+            pos = last_visible(L, q_len, i)
+            for h in range(hq):
+                g = kv_head_of(h, G)
+                qv = bf16_bits_to_f64(q[b, i, h])
+                s = _scaled_scores(K[g][: pos + 1], qv, sigma)
+                out[b, i, h] = _softmax_weighted_sum(s, V[g][: pos + 1])
     return out
 
 
@@ -185,22 +202,22 @@ def split_attention_ref(q, k_cache, v_cache, block_table, seq_lens, block_size: 
         L = int(seq_lens[b])
         if L == 0:
             continue
-        for g in range(hkv):
-            K = gather_token_rows(k_cache, block_table[b], L, block_size, g)
-            V = gather_token_rows(v_cache, block_table[b], L, block_size, g)
-            for i in range(q_len):
-                pos = L - q_len + i
-                for h in range(g * G, (g + 1) * G):
-                    qv = bf16_bits_to_f64(q[b, i, h])
-                    parts = []
-                    for (lo, hi) in ranges[b]:
-                        hi_vis = min(hi, pos + 1)
-                        if hi_vis <= lo:
-                            parts.append(partial_stats_ref(np.zeros(0), V[:0]))
-                            continue
-                        s = sigma * (K[lo:hi_vis] @ qv)
-                        parts.append(partial_stats_ref(s, V[lo:hi_vis]))
-                    out[b, i, h] = merge_partials_ref(parts)
+        K = [gather_token_rows(k_cache, block_table[b], L, block_size, g) for g in range(hkv)]
+        V = [gather_token_rows(v_cache, block_table[b], L, block_size, g) for g in range(hkv)]
+        for i in range(q_len):
+            pos = last_visible(L, q_len, i)
+            for h in range(hq):
+                g = kv_head_of(h, G)
+                qv = bf16_bits_to_f64(q[b, i, h])
+                parts = []
+                for (lo, hi) in ranges[b]:
+                    hi_vis = min(hi, pos + 1)
+                    if hi_vis <= lo:
+                        parts.append(partial_stats_ref(np.zeros(0), V[g][:0]))
+                        continue
+                    s = _scaled_scores(K[g][lo:hi_vis], qv, sigma)
+                    parts.append(partial_stats_ref(s, V[g][lo:hi_vis]))
+                out[b, i, h] = merge_partials_ref(parts)
     return out
 
 

@@ -419,9 +419,17 @@ def _softmax_no_shift_wrong_base(s, v):
     ("lossy bf16 widening", "bf16_bits_to_f64", _widen_truncated),
     ("missing normalisation", "_softmax_weighted_sum", _softmax_unnormalised),
     ("exp2 instead of exp", "_softmax_weighted_sum", _softmax_no_shift_wrong_base),
+    ("interleaved head groups", "kv_head_of", lambda h, group: h % (6 // group)),
+    ("causal bound one token short", "last_visible", lambda L, q_len, i: L - q_len + i - 1),
+    ("top-left causal alignment", "last_visible", lambda L, q_len, i: i),
+    ("scale dropped", "_scaled_scores", lambda keys, qv, sigma: keys @ qv),
+    ("score sign flipped", "_scaled_scores", lambda keys, qv, sigma: -sigma * (keys @ qv)),
 ])
-def test_planted_mistakes_fail_the_pins(monkeypatch, name, attr, bad):
-    case = W.make_case(51, [40, 23], q_len=1, num_q_heads=6, num_kv_heads=2, head_dim=8,
+@pytest.mark.parametrize("q_len", [1, 3])
+def test_planted_mistakes_fail_the_pins(monkeypatch, name, attr, bad, q_len):
+    if name == "top-left causal alignment" and q_len == 1:
+        pytest.skip("top-left and bottom-right alignment differ only for several rows")
+    case = W.make_case(51, [40, 23], q_len=q_len, num_q_heads=6, num_kv_heads=2, head_dim=8,
                        block_size=7, poison=False, interleave=True)
     ref = brute_force(case)
     monkeypatch.setattr(O, attr, bad)
