@@ -159,7 +159,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
 
   __shared__ PageOffs tbl[kTblSplit];
   __shared__ __attribute__((aligned(16))) float mrg_acc[kWaves][G][D];
-  __shared__ float mrg_ml[kWaves][G][2];
+  __shared__ float mrg_m[kWaves][G];
+  __shared__ float mrg_l[kWaves][G];
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
@@ -301,30 +302,23 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
       else consume_v(j - kSubSteps, ring[j % kRing]);
     }
     if constexpr (j == kSubSteps - 1) {
+      // Reference for the V pass: the max over the window scores of the
+      // wave's 4 rows (same lane column, so the same head).
 #pragma unroll
       for (int i = 0; i < kSubSteps; ++i) m_row = fmaxf(m_row, sc[i]);
+      m_row = rows_max(m_row);
     }
   });
 
-  // Row state per head, from lanes 2h of each row.
+  // Every row already shares the wave's reference m_row: sum l over the
+  // rows, and reduce-scatter the accumulators over the rows with lane swaps
+  // (wave halves, then row pairs). Row r of lane column col ends with the
+  // sums of elements e in [r * kEpl / 4, (r + 1) * kEpl / 4) of each head.
+  // All of this runs before the first barrier, while slower waves stream.
+  constexpr int kE2 = kEpl / 2, kE4 = kEpl / 4;
   float m[G], l[G];
   head_bcast<G>(m_row, m);
-  head_bcast<G>(l_row, l);
-
-  // Merge the wave's 4 token rows: rescale every head to the wave's max, then
-  // reduce-scatter over the rows with lane swaps (wave halves, then row
-  // pairs). Row r of lane column col ends with the sums of elements
-  // e in [r * kEpl / 4, (r + 1) * kEpl / 4) of each head.
-  constexpr int kE2 = kEpl / 2, kE4 = kEpl / 4;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float M = rows_max(m[h]);
-    const float w = fast_exp2(m[h] - M);
-    l[h] = rows_sum(l[h] * w);
-    m[h] = M;
-#pragma unroll
-    for (int e = 0; e < kEpl; ++e) acc[h][e] *= w;
-  }
+  head_bcast<G>(rows_sum(l_row), l);
   float part[G][kE4];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -340,6 +334,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
       part[h][e] = p.lo + p.hi;
     }
   }
+  if (lane == 0)
+#pragma unroll
+    for (int h = 0; h < G; ++h) mrg_m[wave][h] = m[h];
+  __syncthreads();
+
+  // Rescale the wave's sums to the workgroup max of each head.
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float M = mrg_m[0][h];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mrg_m[w][h]);
+    const float f = fast_exp2(m[h] - M);
+    l[h] *= f;
+#pragma unroll
+    for (int e = 0; e < kE4; ++e) part[h][e] *= f;
+  }
   {
     const int e0 = row * kE4;                             // within one 8-element chunk
     const int d0 = (e0 / 8) * 128 + col * 8 + (e0 % 8);
@@ -354,27 +364,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
     }
     if (lane == 0)
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        mrg_ml[wave][h][0] = m[h];
-        mrg_ml[wave][h][1] = l[h];
-      }
+      for (int h = 0; h < G; ++h) mrg_l[wave][h] = l[h];
   }
   __syncthreads();
 
-  // Merge the waves (fixed order; every thread derives the weights of its
-  // head) and write the split's result.
+  // Sum the waves (all already relative to the workgroup max; fixed order)
+  // and write the split's result.
   const int64_t prow0 = int64_t(b) * a.q_len * a.hq + int64_t(g) * G;   // partial row of head 0, query row 0
   for (int i = tid; i < G * D; i += kThreads) {
     const int h = i / D, d = i - h * D;
-    float M = mrg_ml[0][h][0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mrg_ml[w][h][0]);
     float num = 0.0f, den = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float f = fast_exp2(mrg_ml[w][h][0] - M);
-      den = fmaf(f, mrg_ml[w][h][1], den);
-      num = fmaf(f, mrg_acc[w][h][d], num);
+      num += mrg_acc[w][h][d];
+      den += mrg_l[w][h];
     }
     if (sp.nsplit == 1) {
       store_out(a, out_row0 + i, den > 0.0f ? num / den : 0.0f);
@@ -382,6 +385,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
       const int64_t pr = (prow0 + h) * a.num_splits + s;
       a.part_acc[pr * D + d] = num;
       if (d == 0) {
+        float M = mrg_m[0][h];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mrg_m[w][h]);
         a.part_ml[pr * 2] = M;
         a.part_ml[pr * 2 + 1] = den;
       }
