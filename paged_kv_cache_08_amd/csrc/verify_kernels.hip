@@ -50,11 +50,18 @@ typedef __attribute__((address_space(3))) short4_t* lds_short4_ptr;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
 
-// bf16 bits of x rounded to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-  uint32_t u = __float_as_uint(x);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// Two floats as a packed bf16 pair (one v_cvt_pk_bf16_f32); x in the low half.
+__device__ __forceinline__ uint32_t bf16_pair(float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){x, y}, bf16x2_t));
 }
+
+// A row's softmax reference moves only when a tile's max exceeds it by more
+// than this (log2 units), so probabilities stay <= 2^8 and most tiles need no
+// rescale of O.
+constexpr float kLazyMax = 8.0f;
 
 template <int D>
 __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a) {
@@ -179,7 +186,7 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
         }
       mt = fmaxf(mt, __shfl_xor(mt, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float m_new = fmaxf(m_run, mt);
+      const float m_new = mt > m_run + kLazyMax ? mt : m_run;
       const float alpha = fast_exp2(m_run - m_new);
       float ls = 0.0f;
 #pragma unroll
@@ -192,16 +199,20 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
         }
       ls += __shfl_xor(ls, 16);
       ls += __shfl_xor(ls, 32);
+      const bool moved = m_new != m_run;
       l_run = l_run * alpha + ls;
       m_run = m_new;
-      // O rows 4 grp + r take the alpha of that row (held by lane 4 grp + r of the group).
-      float al[4];
+      // O rows 4 grp + r take the alpha of that row (held by lane 4 grp + r of
+      // the group); skipped when no row of the wave moved its reference.
+      if (__any(moved ? 1 : 0)) {
+        float al[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 16 * grp + 4 * grp + r);
+        for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, 16 * grp + 4 * grp + r);
 #pragma unroll
-      for (int db = 0; db < kDBlocks; ++db)
+        for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[db][r] *= al[r];
+          for (int r = 0; r < 4; ++r) o[db][r] *= al[r];
+      }
       // P as A operands (hi and lo) of the two 32-token halves.
       static_for<0, 2>([&](auto hc) {
         constexpr int hh = decltype(hc)::value;
@@ -210,11 +221,9 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
           constexpr int t = decltype(tc)::value;
           const float p0 = st[2 * hh + (t >> 1)][(t & 1) * 2];
           const float p1 = st[2 * hh + (t >> 1)][(t & 1) * 2 + 1];
-          const uint32_t h0 = bf16_bits(p0), h1 = bf16_bits(p1);
-          const uint32_t l0 = bf16_bits(p0 - __uint_as_float(h0 << 16));
-          const uint32_t l1 = bf16_bits(p1 - __uint_as_float(h1 << 16));
-          hi[t] = h0 | (h1 << 16);
-          lo[t] = l0 | (l1 << 16);
+          const uint32_t h = bf16_pair(p0, p1);
+          hi[t] = h;
+          lo[t] = bf16_pair(p0 - __uint_as_float(h << 16), p1 - __uint_as_float(h & 0xffff0000u));
         });
         const bf16x8_t ph = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
         const bf16x8_t pl = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));

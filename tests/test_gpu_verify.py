@@ -87,3 +87,18 @@ def test_verify_repeat_bitwise_and_bf16_out():
     np.testing.assert_array_equal(a, b)
     b16 = run_gpu(case, out_dtype=torch.bfloat16).astype(np.float32)
     np.testing.assert_array_equal(W.f32_to_bf16_bits(b16), W.f32_to_bf16_bits(a.astype(np.float32)))
+
+
+@pytest.mark.parametrize("ql", [1, 16])
+def test_late_dominant_keys_move_the_softmax_reference(ql):
+    # Keys scaled x16 (exact in bf16) at tokens deep inside a split: many rows
+    # see their running max jump by far more than 2^8 after the accumulator
+    # already holds earlier tokens, so the rescale of that accumulator must run.
+    log(f"case: q_len {ql}, late dominant keys, 1500 tokens, page 784, forced 512-token splits")
+    case = W.make_case(956, [1500], q_len=ql, block_size=784)
+    for t in (400, 470, 1100, 1490):
+        page, off = int(case.block_table[0, t // 784]), t % 784
+        rows = case.k_cache[page, off].astype(np.uint32) << 16
+        case.k_cache[page, off] = W.f32_to_bf16_bits(rows.view(np.float32) * np.float32(16.0))
+    assert_matches_oracle(run_gpu(case, num_splits=1), oracle_out(case), f"late keys q{ql}")
+    assert_matches_oracle(run_gpu(case), oracle_out(case), f"late keys q{ql} planned")
