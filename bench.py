@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="hybrid", choices=["hybrid", "dense", "mixed", "verify"])
+    ap.add_argument("--workload", default="hybrid", choices=["hybrid", "dense", "mixed", "verify", "varlen"])
     ap.add_argument("--context", type=int, default=32768)
     ap.add_argument("--block-size", type=int, default=784)
     ap.add_argument("--pools", type=int, default=16)
@@ -87,11 +87,16 @@ def make_workload(args):
     elif args.workload == "mixed":
         case = W.mixed_batch(poison=False)
         name = "mixed batch: 16 sequences, q_len 1, 24 q / 4 KV heads, head_dim 256, page 784, log-uniform 500-32000"
+    elif args.workload == "varlen":
+        case, qp, cu = W.batched_verify(poison=False)
+        name = ("batched speculative verify (varlen): 32 requests, 1..5 rows each, 24 q / 4 KV heads, "
+                "head_dim 256, page 784, contexts log-uniform 512..2048")
+        return case, name, (qp, cu)
     else:
         case = W.spec_verify(args.context, poison=False)
         name = (f"speculative verify: batch 1, q_len 16 causal rows, 24 q / 4 KV heads, head_dim 256, "
                 f"page 784, context {args.context}")
-    return case, name
+    return case, name, None
 
 
 def traffic_from_profiles(kernel_src_hash: str, workload_key: str):
@@ -107,10 +112,20 @@ def traffic_from_profiles(kernel_src_hash: str, workload_key: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(case, kv_bytes_per_call, seconds):
+def oracle_call(case, varlen):
+    """The oracle's result for the benchmark input (pool 0)."""
+    import oracle.paged_attention as O
+    if varlen is not None:
+        qp, cu = varlen
+        return O.paged_attention_varlen_ref(qp, cu, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                                            case.block_size, case.scale)
+    return O.paged_attention_ref(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                                 case.block_size, case.scale)
+
+
+def cpu_baseline(case, varlen, kv_bytes_per_call, seconds):
     """The oracle as it stands, on the host cores, over whole calls of the same
     workload until about `seconds` of CPU work has run."""
-    import oracle.paged_attention as O
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -118,8 +133,7 @@ def cpu_baseline(case, kv_bytes_per_call, seconds):
         threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
     n, t0 = 0, time.perf_counter()
     while True:
-        O.paged_attention_ref(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
-                              case.block_size, case.scale)
+        oracle_call(case, varlen)
         n += 1
         el = time.perf_counter() - t0
         if el >= seconds or n >= 1000:
@@ -152,13 +166,18 @@ def main():
     assert torch.cuda.is_available(), "no GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    case, wl_name = make_workload(args)
+    case, wl_name, varlen = make_workload(args)
     print(f"[bench] workload: {wl_name}", file=sys.stderr, flush=True)
 
     def bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    q = bf16(case.q)
+    if varlen is None:
+        q, cu_t, max_q = bf16(case.q), None, None
+    else:
+        q = bf16(varlen[0])
+        cu_t = torch.from_numpy(varlen[1]).to(dev)
+        max_q = int(np.diff(varlen[1]).max())
     k0, v0 = bf16(case.k_cache), bf16(case.v_cache)
     table = torch.from_numpy(case.block_table).to(dev)
     lens = torch.from_numpy(case.seq_lens).to(dev)
@@ -167,7 +186,8 @@ def main():
     kv_bytes = W.kv_read_bytes(case.seq_lens, case.k_cache.shape[2], case.k_cache.shape[3])
     stream = torch.cuda.current_stream(dev).cuda_stream
     call = P.PreparedDecode(q, k0, v0, table, lens, case.block_size, case.scale, max_seq_len=case.max_seq_len,
-                            total_tokens=total_tokens, num_splits=args.splits, stream=stream)
+                            total_tokens=total_tokens, num_splits=args.splits, stream=stream,
+                            cu_seqlens_q=cu_t, max_q_len=max_q)
     out = call.out
 
     ptrs = [(k.data_ptr(), v.data_ptr()) for k, v in pools]
@@ -240,7 +260,7 @@ def main():
             gcall = P.PreparedDecode(q, k0, v0, table, lens, case.block_size, case.scale,
                                      max_seq_len=case.max_seq_len, total_tokens=total_tokens,
                                      num_splits=args.splits, out=out, workspace=call.workspace,
-                                     stream=gstream.cuda_stream)
+                                     stream=gstream.cuda_stream, cu_seqlens_q=cu_t, max_q_len=max_q)
         torch.cuda.synchronize()
         with torch.cuda.graph(graph, stream=gstream):
             for i in range(args.steps):
@@ -265,9 +285,7 @@ def main():
     got = out.cpu().numpy().astype(np.float64)
     parity = None
     try:
-        import oracle.paged_attention as O
-        ref = O.paged_attention_ref(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
-                                    case.block_size, case.scale)
+        ref = oracle_call(case, varlen)
         parity = float(np.abs(got - ref).max())
     except Exception as e:  # parity is reported, never required for the timing
         print(f"[bench] parity check skipped: {e}", file=sys.stderr)
@@ -281,7 +299,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(case, kv_bytes, args.cpu_seconds)
+        cpu = cpu_baseline(case, varlen, kv_bytes, args.cpu_seconds)
 
     med = statistics.median(region_us)
     rec = {
@@ -300,6 +318,7 @@ def main():
         "config": {
             "workload": wl_name,
             "batch": int(case.num_seqs),
+            "query_rows": int(case.num_seqs * case.q_len if varlen is None else varlen[1][-1]),
             "context": int(case.max_seq_len),
             "block_size": int(case.block_size),
             "kv_pools_rotated": len(pools),
@@ -313,7 +332,7 @@ def main():
                                 "range_pct": round(100.0 * (max(region_us) - min(region_us)) / med, 2)},
         "roofline": {
             "bound": "hbm",
-            "kernel": "verify_split_kernel" if case.q_len > 1 else "decode_split_kernel",
+            "kernel": "verify_split_kernel" if (case.q_len > 1 or varlen is not None) else "decode_split_kernel",
             "achieved": round(kern_gbs, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

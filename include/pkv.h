@@ -132,9 +132,11 @@ int pkv_device_cu_count(int32_t* cu_count);
  *   out         device [num_seqs, q_len, Hq, D], float32 or bf16 (out_dtype).
  *   workspace   device, >= pkv_workspace_bytes(p, 0) bytes, 256-byte aligned;
  *               its first 4 bytes are a sticky error word (bit 0: a block-table
- *               entry outside [0, num_pages) was met and its tokens skipped);
- *               zero it once after allocating. Calls that share a workspace
- *               must not overlap in time.
+ *               entry outside [0, num_pages) was met and its tokens skipped;
+ *               bit 1: a sequence's cu_seqlens_q rows were inconsistent and
+ *               the sequence was skipped, varlen calls only); zero it once
+ *               after allocating. Calls that share a workspace must not
+ *               overlap in time.
  *   stream      hipStream_t (NULL = default stream).
  * q, k_cache, v_cache and out must be 16-byte aligned. No input is written.
  */
@@ -144,9 +146,35 @@ int pkv_paged_decode_attention(const pkv_decode_params* p,
                                void* out, void* workspace, int64_t workspace_bytes,
                                void* stream);
 
-/* Which kernels the last successful pkv_paged_decode_attention call on this
- * thread launched, with the split plan, e.g.
- * "decode_valu d256 g6 + lse_merge splits=64 chunk=512 B=784". Copies at most
+/*
+ * Varlen multi-row call: sequence b has its own number of new query rows,
+ * n_b = cu_seqlens_q[b + 1] - cu_seqlens_q[b] in [0, q_len], in one batched
+ * call (batched speculative verify). The rows of all sequences are packed:
+ *   q            device bf16 [total_q, Hq, D], total_q = cu_seqlens_q[num_seqs];
+ *                sequence b's rows are cu_seqlens_q[b] .. cu_seqlens_q[b + 1].
+ *   cu_seqlens_q device int32 [num_seqs + 1], non-decreasing, cu_seqlens_q[0] = 0
+ *                and total_q <= num_seqs * q_len (the workspace's rows).
+ *   out          device [total_q, Hq, D], float32 or bf16.
+ * p->q_len is the largest n_b (a host-known bound, like max_seqlen_q of the
+ * vendor interface in "DCU page832 attention" §6); (Hq / Hkv) * q_len <= 128.
+ * Row i of sequence b sees the tokens j <= seq_lens[b] - n_b + i (the n_b new
+ * tokens are the last ones in the cache), as in the uniform call; seq_lens[b]
+ * must be >= n_b. All rows run on the MFMA kernel, whatever n_b is. The other
+ * arguments, the workspace (pkv_workspace_bytes with the same p) and the
+ * error word are as for pkv_paged_decode_attention; a sequence whose row
+ * range is inconsistent with the rules above is skipped (its out rows are not
+ * written) and sets bit 1 of the error word.
+ */
+int pkv_paged_varlen_attention(const pkv_decode_params* p,
+                               const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               const int32_t* cu_seqlens_q,
+                               void* out, void* workspace, int64_t workspace_bytes,
+                               void* stream);
+
+/* Which kernels the last successful pkv_paged_decode_attention (or
+ * pkv_paged_varlen_attention) call on this thread launched, with the split
+ * plan, e.g. "decode_valu d256 g6 q1 w512 + lse_merge splits=64 chunk=512 B=784". Copies at most
  * len-1 characters plus a terminator; returns the full length. */
 int pkv_last_variant(char* buf, int32_t len);
 

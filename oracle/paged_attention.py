@@ -157,6 +157,25 @@ def paged_attention_ref(q, k_cache, v_cache, block_table, seq_lens, block_size: 
     return out
 
 
+def paged_attention_varlen_ref(q_packed, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens,
+                               block_size: int, scale: float) -> np.ndarray:
+    """Varlen multi-row attention: sequence b owns query rows
+    q_packed[cu[b]:cu[b+1]] (n_b of them, [total_q, Hq, D] bf16 bits) and row i
+    sees tokens j <= L_b - n_b + i, exactly as a call with q_len = n_b on that
+    sequence alone (the vendor interface of the DCU page, §6, passes such rows
+    through cu_seqlens_q). Returns float64 [total_q, Hq, D]."""
+    q_packed = np.asarray(q_packed)
+    cu = [int(x) for x in np.asarray(cu_seqlens_q).tolist()]
+    out = np.zeros((q_packed.shape[0],) + q_packed.shape[1:], dtype=np.float64)
+    for b in range(len(cu) - 1):
+        lo, hi = cu[b], cu[b + 1]
+        if hi == lo:
+            continue
+        out[lo:hi] = paged_attention_ref(q_packed[None, lo:hi], k_cache, v_cache, block_table[b:b + 1],
+                                         np.asarray(seq_lens)[b:b + 1], block_size, scale)[0]
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Split mode: partial softmax statistics and their merge (split-KV paragraph of
 # the dual-Radeon page; Lektion 3 of the MI350P page).

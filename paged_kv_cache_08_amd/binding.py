@@ -65,6 +65,8 @@ _SIGNATURES = {
     "pkv_workspace_bytes": (ctypes.c_int64, [_P, ctypes.c_int32]),
     "pkv_device_cu_count": (ctypes.c_int, [_i32p]),
     "pkv_paged_decode_attention": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64, _vp]),
+    "pkv_paged_varlen_attention": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64,
+                                                  _vp]),
     "pkv_last_variant": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_int32]),
     "pkv_set_timing_events": (ctypes.c_int, [_vp, _vp]),
     "pkv_debug_token_offsets": (ctypes.c_int, [_P, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp]),
@@ -223,6 +225,42 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, block_siz
     return out
 
 
+def paged_varlen_attention(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, block_size: int,
+                           scale: float, *, max_q_len: int, max_seq_len: int, total_tokens: int = 0,
+                           num_splits: int = 0, out=None, out_dtype=None, workspace=None, stream=None):
+    """Varlen multi-row call: sequence b's query rows are q[cu_seqlens_q[b]:cu_seqlens_q[b+1]].
+
+    q: bf16 [total_q, Hq, D] packed rows (contiguous, on the GPU); cu_seqlens_q:
+    int32 [num_seqs + 1] on the GPU; max_q_len: the largest row count (host
+    bound); max_seq_len: host bound of seq_lens. Returns out [total_q, Hq, D].
+    """
+    torch = _torch()
+    assert q.is_cuda and q.dtype == torch.bfloat16 and q.is_contiguous() and q.dim() == 3
+    assert cu_seqlens_q.dtype == torch.int32 and cu_seqlens_q.is_contiguous()
+    assert block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
+    assert block_table.is_contiguous() and seq_lens.is_contiguous()
+    ns = seq_lens.shape[0]
+    assert cu_seqlens_q.shape[0] == ns + 1 and block_table.shape[0] == ns
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    odt = PKV_OUT_BF16 if out.dtype == torch.bfloat16 else PKV_OUT_F32
+    assert out.dtype in (torch.float32, torch.bfloat16) and out.is_contiguous() and out.shape == q.shape
+    shape4 = torch.empty((ns, int(max_q_len), q.shape[1], q.shape[2]), device="meta")
+    p = make_params(shape4, k_cache, v_cache, block_table, block_size, scale, max_seq_len=max_seq_len,
+                    num_splits=num_splits, total_tokens=total_tokens, out_dtype=odt)
+    need = workspace_bytes(p, 0)
+    if workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib().pkv_paged_varlen_attention(
+        ctypes.byref(p), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+        seq_lens.data_ptr(), cu_seqlens_q.data_ptr(), out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), stream)
+    check(rc, "pkv_paged_varlen_attention")
+    return out
+
+
 def debug_token_offsets(p: DecodeParams, block_table, seq_lens, kv_head: int):
     """Per-token K and V row offsets as the split kernel computes them ([num_seqs, max_seq_len] int64)."""
     torch = _torch()
@@ -257,20 +295,30 @@ class PreparedDecode:
     then only crosses into the C library (for tight loops and benchmarks).
 
     ``run(k_cache, v_cache)`` may swap in another pool with the same shape and
-    strides as the one given at construction."""
+    strides as the one given at construction. With ``cu_seqlens_q`` (int32 on
+    the GPU) and ``max_q_len`` the call is the varlen one on packed rows
+    q [total_q, Hq, D]."""
 
     def __init__(self, q, k_cache, v_cache, block_table, seq_lens, block_size: int, scale: float, *,
                  max_seq_len: int, total_tokens: int = 0, num_splits: int = 0, out=None, workspace=None,
-                 stream=None):
+                 stream=None, cu_seqlens_q=None, max_q_len: int | None = None):
         torch = _torch()
         assert q.is_cuda and q.dtype == torch.bfloat16 and q.is_contiguous()
         assert block_table.is_contiguous() and seq_lens.is_contiguous()
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
         odt = PKV_OUT_BF16 if out.dtype == torch.bfloat16 else PKV_OUT_F32
-        self.params = make_params(q, k_cache, v_cache, block_table, block_size, scale, max_seq_len=max_seq_len,
+        self.varlen = cu_seqlens_q is not None
+        if self.varlen:
+            assert q.dim() == 3 and cu_seqlens_q.dtype == torch.int32 and cu_seqlens_q.is_contiguous()
+            assert max_q_len is not None and max_q_len >= 1
+            shape = torch.empty((block_table.shape[0], max_q_len, q.shape[1], q.shape[2]), device="meta")
+        else:
+            shape = q
+        self.params = make_params(shape, k_cache, v_cache, block_table, block_size, scale, max_seq_len=max_seq_len,
                                   num_splits=num_splits, total_tokens=total_tokens, out_dtype=odt)
-        check(validate(self.params), "pkv_validate_params")
+        if not self.varlen:
+            check(validate(self.params), "pkv_validate_params")
         need = workspace_bytes(self.params, 0)
         if workspace is None:
             workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
@@ -280,26 +328,35 @@ class PreparedDecode:
         self.out, self.workspace = out, workspace
         self._shape = (tuple(k_cache.shape), tuple(k_cache.stride()), tuple(v_cache.stride()))
         self._keep = (q, k_cache, v_cache, block_table, seq_lens)
-        self._fn = lib().pkv_paged_decode_attention
+        self._keep = self._keep + (cu_seqlens_q,)
         self._pp = ctypes.byref(self.params)
         self._fixed = (q.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
                        workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
+        if self.varlen:
+            fn, cup, name = lib().pkv_paged_varlen_attention, cu_seqlens_q.data_ptr(), "pkv_paged_varlen_attention"
+
+            def call(kp, vp):
+                qp, tp, lp, op, wp, wn, st = self._fixed
+                return fn(self._pp, qp, kp, vp, tp, lp, cup, op, wp, wn, st)
+        else:
+            fn, name = lib().pkv_paged_decode_attention, "pkv_paged_decode_attention"
+
+            def call(kp, vp):
+                qp, tp, lp, op, wp, wn, st = self._fixed
+                return fn(self._pp, qp, kp, vp, tp, lp, op, wp, wn, st)
+        self._call, self._name = call, name
         self._k, self._v = k_cache.data_ptr(), v_cache.data_ptr()
 
     def run_ptrs(self, k_ptr: int, v_ptr: int) -> None:
         """Like run() with raw device pointers of a pool laid out like the original."""
-        qp, tp, lp, op, wp, wn, st = self._fixed
-        rc = self._fn(self._pp, qp, k_ptr, v_ptr, tp, lp, op, wp, wn, st)
+        rc = self._call(k_ptr, v_ptr)
         if rc != PKV_OK:
-            check(rc, "pkv_paged_decode_attention")
+            check(rc, self._name)
 
     def run(self, k_cache=None, v_cache=None):
         kp, vp = self._k, self._v
         if k_cache is not None:
             assert (tuple(k_cache.shape), tuple(k_cache.stride()), tuple(v_cache.stride())) == self._shape
             kp, vp = k_cache.data_ptr(), v_cache.data_ptr()
-        qp, tp, lp, op, wp, wn, st = self._fixed
-        rc = self._fn(self._pp, qp, kp, vp, tp, lp, op, wp, wn, st)
-        if rc != PKV_OK:
-            check(rc, "pkv_paged_decode_attention")
+        self.run_ptrs(kp, vp)
         return self.out

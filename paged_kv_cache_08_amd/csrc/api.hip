@@ -128,7 +128,13 @@ const char* pkv_strerror(int code) {
 
 const char* pkv_last_error(void) { return g_last_error.c_str(); }
 
-int pkv_validate_params(const pkv_decode_params* p) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the uniform and the varlen calls (all but the kernel's
+// limits on q_len and the group size).
+int validate_common(const pkv_decode_params* p) {
   if (!p) return fail(PKV_ERR_INVALID, "params is NULL");
   if (p->num_seqs < 1 || p->q_len < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1 ||
       p->block_size < 1 || p->max_pages_per_seq < 1 || p->num_pages < 1 || p->max_seq_len < 0 ||
@@ -136,13 +142,8 @@ int pkv_validate_params(const pkv_decode_params* p) {
     return fail(PKV_ERR_INVALID, "a size is out of range");
   if (p->num_q_heads % p->num_kv_heads != 0)
     return fail(PKV_ERR_INVALID, "num_q_heads is not a multiple of num_kv_heads");
-  const int group = p->num_q_heads / p->num_kv_heads;
   if (p->head_dim != 128 && p->head_dim != 256) return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 128 or 256");
   if (p->q_len > 16) return fail(PKV_ERR_UNSUPPORTED, "q_len above 16");
-  if (p->q_len == 1 && !pkv::decode_supported(p->head_dim, group))
-    return fail(PKV_ERR_UNSUPPORTED, "decode (q_len 1) needs at most 8 query heads per KV head");
-  if (p->q_len > 1 && !pkv::verify_supported(p->head_dim, group, p->q_len))
-    return fail(PKV_ERR_UNSUPPORTED, "multi-row calls need (Hq / Hkv) * q_len <= 128");
   if (p->max_seq_len > (1 << 30)) return fail(PKV_ERR_UNSUPPORTED, "max_seq_len above 2^30 tokens");
   if (int64_t(p->max_pages_per_seq) * p->block_size < p->max_seq_len)
     return fail(PKV_ERR_INVALID, "max_seq_len exceeds max_pages_per_seq * block_size");
@@ -159,8 +160,99 @@ int pkv_validate_params(const pkv_decode_params* p) {
   return PKV_OK;
 }
 
+int validate_varlen(const pkv_decode_params* p) {
+  int rc = validate_common(p);
+  if (rc) return rc;
+  if (!pkv::verify_supported(p->head_dim, p->num_q_heads / p->num_kv_heads, p->q_len))
+    return fail(PKV_ERR_UNSUPPORTED, "varlen calls need (Hq / Hkv) * max q_len <= 128");
+  return PKV_OK;
+}
+
+// Shapes that the uniform or the varlen call accepts (plan and workspace
+// queries serve both).
+int validate_any(const pkv_decode_params* p);
+
+// Plan, check the workspace and launch the split kernel (then the merge when
+// the plan has several splits). cu_q == nullptr: uniform call, q_len rows per
+// sequence (q_len 1 on the VALU decode kernel); else varlen rows on the MFMA
+// kernel.
+int launch_call(const pkv_decode_params* p, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_table, const int32_t* seq_lens, const int32_t* cu_q, void* out,
+                void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out || !workspace)
+    return fail(PKV_ERR_INVALID, "a device pointer is NULL");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return fail(PKV_ERR_INVALID, "q, k_cache, v_cache and out must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return fail(PKV_ERR_INVALID, "workspace must be 256-byte aligned");
+  int32_t cu = 0;
+  int rc = device_cu_count(&cu);
+  if (rc) return rc;
+  int32_t S = 0, chunk = 0;
+  plan(p, cu, &S, &chunk);
+  const int64_t need = workspace_for(p, S);
+  if (workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
+
+  pkv::DecodeArgs a = make_args(p, S, chunk);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_cache);
+  a.v = static_cast<const uint16_t*>(v_cache);
+  a.table = block_table;
+  a.seq_lens = seq_lens;
+  a.cu_q = cu_q;
+  a.out = out;
+  char* ws = static_cast<char*>(workspace);
+  const int64_t rows = int64_t(p->num_seqs) * p->q_len * p->num_q_heads;
+  a.err = reinterpret_cast<uint32_t*>(ws);
+  a.part_ml = reinterpret_cast<float*>(ws + pkv::kWsHeaderBytes);
+  a.part_acc = reinterpret_cast<float*>(ws + pkv::kWsHeaderBytes + align256(rows * S * 2 * 4));
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int group = p->num_q_heads / p->num_kv_heads;
+  hipError_t e;
+  const char* split_name;
+  int window;
+  if (p->q_len == 1 && !cu_q) {
+    e = pkv::launch_decode_split(a, p->head_dim, group, st, g_ev_start, g_ev_stop);
+    split_name = "decode_valu";
+    window = pkv::decode_window(chunk);
+  } else {
+    e = pkv::launch_verify_split(a, p->head_dim, group, st, g_ev_start, g_ev_stop);
+    split_name = cu_q ? "varlen_mfma" : "verify_mfma";
+    window = 64;   // 64-token K/V tiles, looped over the split
+  }
+  if (e != hipSuccess) return hip_fail(e, "split kernel launch");
+  if (S > 1) {
+    e = pkv::launch_lse_merge(a, p->head_dim, st);
+    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  }
+  g_last_variant = VariantInfo{split_name, p->head_dim, group, p->q_len, window, S, chunk, p->block_size};
+  return PKV_OK;
+}
+
+int validate_any(const pkv_decode_params* p) {
+  const int rc = pkv_validate_params(p);
+  return rc && validate_varlen(p) ? rc : PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_validate_params(const pkv_decode_params* p) {
+  int rc = validate_common(p);
+  if (rc) return rc;
+  const int group = p->num_q_heads / p->num_kv_heads;
+  if (p->q_len == 1 && !pkv::decode_supported(p->head_dim, group))
+    return fail(PKV_ERR_UNSUPPORTED, "decode (q_len 1) needs at most 8 query heads per KV head");
+  if (p->q_len > 1 && !pkv::verify_supported(p->head_dim, group, p->q_len))
+    return fail(PKV_ERR_UNSUPPORTED, "multi-row calls need (Hq / Hkv) * q_len <= 128");
+  return PKV_OK;
+}
+
 int pkv_plan_splits(const pkv_decode_params* p, int32_t cu_count, int32_t* num_splits, int32_t* chunk_tokens) {
-  int rc = pkv_validate_params(p);
+  int rc = validate_any(p);
   if (rc) return rc;
   if (cu_count < 1 || !num_splits || !chunk_tokens) return fail(PKV_ERR_INVALID, "bad cu_count or output pointer");
   return plan(p, cu_count, num_splits, chunk_tokens);
@@ -175,7 +267,7 @@ int pkv_plan_constants(int32_t* tile, int32_t* wg_per_cu, int32_t* min_tiles, in
 }
 
 int64_t pkv_workspace_bytes(const pkv_decode_params* p, int32_t cu_count) {
-  int rc = pkv_validate_params(p);
+  int rc = validate_any(p);
   if (rc) return rc;
   if (cu_count <= 0) {
     rc = device_cu_count(&cu_count);
@@ -196,55 +288,19 @@ int pkv_paged_decode_attention(const pkv_decode_params* p, const void* q, const 
                                void* out, void* workspace, int64_t workspace_bytes, void* stream) {
   int rc = pkv_validate_params(p);
   if (rc) return rc;
-  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out || !workspace)
-    return fail(PKV_ERR_INVALID, "a device pointer is NULL");
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
-    return fail(PKV_ERR_INVALID, "q, k_cache, v_cache and out must be 16-byte aligned");
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
-    return fail(PKV_ERR_INVALID, "workspace must be 256-byte aligned");
-  int32_t cu = 0;
-  rc = device_cu_count(&cu);
+  return launch_call(p, q, k_cache, v_cache, block_table, seq_lens, nullptr, out, workspace, workspace_bytes,
+                     stream);
+}
+
+int pkv_paged_varlen_attention(const pkv_decode_params* p, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                               const int32_t* cu_seqlens_q, void* out, void* workspace, int64_t workspace_bytes,
+                               void* stream) {
+  int rc = validate_varlen(p);
   if (rc) return rc;
-  int32_t S = 0, chunk = 0;
-  plan(p, cu, &S, &chunk);
-  const int64_t need = workspace_for(p, S);
-  if (workspace_bytes < need)
-    return fail(PKV_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes");
-
-  pkv::DecodeArgs a = make_args(p, S, chunk);
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k_cache);
-  a.v = static_cast<const uint16_t*>(v_cache);
-  a.table = block_table;
-  a.seq_lens = seq_lens;
-  a.out = out;
-  char* ws = static_cast<char*>(workspace);
-  const int64_t rows = int64_t(p->num_seqs) * p->q_len * p->num_q_heads;
-  a.err = reinterpret_cast<uint32_t*>(ws);
-  a.part_ml = reinterpret_cast<float*>(ws + pkv::kWsHeaderBytes);
-  a.part_acc = reinterpret_cast<float*>(ws + pkv::kWsHeaderBytes + align256(rows * S * 2 * 4));
-
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const int group = p->num_q_heads / p->num_kv_heads;
-  hipError_t e;
-  const char* split_name;
-  int window;
-  if (p->q_len == 1) {
-    e = pkv::launch_decode_split(a, p->head_dim, group, st, g_ev_start, g_ev_stop);
-    split_name = "decode_valu";
-    window = pkv::decode_window(chunk);
-  } else {
-    e = pkv::launch_verify_split(a, p->head_dim, group, st, g_ev_start, g_ev_stop);
-    split_name = "verify_mfma";
-    window = 64;   // 64-token K/V tiles, looped over the split
-  }
-  if (e != hipSuccess) return hip_fail(e, "split kernel launch");
-  if (S > 1) {
-    e = pkv::launch_lse_merge(a, p->head_dim, st);
-    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
-  }
-  g_last_variant = VariantInfo{split_name, p->head_dim, group, p->q_len, window, S, chunk, p->block_size};
-  return PKV_OK;
+  if (!cu_seqlens_q) return fail(PKV_ERR_INVALID, "cu_seqlens_q is NULL");
+  return launch_call(p, q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, out, workspace,
+                     workspace_bytes, stream);
 }
 
 int pkv_last_variant(char* buf, int32_t len) {

@@ -46,12 +46,14 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(DecodeArgs a) {
   __shared__ float part[4][64];
   const int cb = blockIdx.x, h = blockIdx.y;
   const int i = blockIdx.z % a.q_len, b = blockIdx.z / a.q_len;
+  const QRows qr = seq_q_rows(a, b);
+  if (i >= qr.n) return;          // no such row in a varlen batch
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int d = cb * 64 + lane;
   const SplitSpan sp = split_span(a, b, 0);
   if (sp.nsplit <= 1) return;    // written by the split kernel
   const int ns = sp.nsplit;
-  const int64_t prow = (int64_t(b) * a.q_len + i) * a.hq + h;
+  const int64_t prow = (int64_t(qr.base) + i) * a.hq + h;
   const float* ml = a.part_ml + prow * a.num_splits * 2;
   const float* ac = a.part_acc + prow * a.num_splits * D;
 
@@ -124,6 +126,64 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(DecodeArgs a) {
     store_out(a, prow * D + d, ((part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane])) * inv_den);
 }
 
+// The merge for plans of at most kFewSplits splits (short contexts, batched
+// verify): workgroup = (query row slot, 4 query heads), one wave per head, each
+// lane D / 64 columns, so the grid is not 64-column blocks times heads times
+// rows of tiny workgroups. Every lane reads its head's (m, l) pairs (the same
+// addresses across the wave), so the weights need no cross-lane step; the
+// accumulator loads are all issued first. Same rule as lse_merge_kernel:
+// M over the splits with l > 0, weights 2^(m_s - M), sums in split order.
+constexpr int kFewSplits = 8;
+
+template <int D>
+__global__ __launch_bounds__(256) void lse_merge_few_kernel(DecodeArgs a) {
+  constexpr int kCols = D / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = blockIdx.y * 4 + wave;
+  const int i = blockIdx.x % a.q_len, b = blockIdx.x / a.q_len;
+  if (h >= a.hq) return;
+  const QRows qr = seq_q_rows(a, b);
+  if (i >= qr.n) return;          // no such row in a varlen batch
+  const SplitSpan sp = split_span(a, b, 0);
+  if (sp.nsplit <= 1) return;    // written by the split kernel
+  const int ns = sp.nsplit;      // <= num_splits <= kFewSplits
+  const int64_t prow = (int64_t(qr.base) + i) * a.hq + h;
+  const float* ml = a.part_ml + prow * a.num_splits * 2;
+  const float* ac = a.part_acc + prow * a.num_splits * D;
+
+  float acc[kFewSplits][kCols];
+  float m[kFewSplits], l[kFewSplits];
+#pragma unroll
+  for (int s = 0; s < kFewSplits; ++s) {
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) acc[s][c] = s < ns ? ac[int64_t(s) * D + c * 64 + lane] : 0.0f;
+    const float2 v = s < ns ? reinterpret_cast<const float2*>(ml)[s] : make_float2(0.0f, 0.0f);
+    m[s] = v.y > 0.0f ? v.x : -INFINITY;   // a split with no visible token weighs 0
+    l[s] = v.y;
+  }
+  float M = m[0];
+#pragma unroll
+  for (int s = 1; s < kFewSplits; ++s) M = fmaxf(M, m[s]);
+  if (M == -INFINITY) {
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) store_out(a, prow * D + c * 64 + lane, 0.0f);
+    return;
+  }
+  float den = 0.0f, num[kCols];
+#pragma unroll
+  for (int c = 0; c < kCols; ++c) num[c] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < kFewSplits; ++s) {
+    const float f = fast_exp2(m[s] - M);   // 0 for empty and unused splits
+    den = fmaf(f, l[s], den);
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) num[c] = fmaf(f, acc[s][c], num[c]);
+  }
+  const float inv = 1.0f / den;
+#pragma unroll
+  for (int c = 0; c < kCols; ++c) store_out(a, prow * D + c * 64 + lane, num[c] * inv);
+}
+
 // Debug: offsets of every live token row, through the same split range,
 // table staging and token_row() the split kernel uses.
 __global__ __launch_bounds__(kThreads) void debug_offsets_kernel(DecodeArgs a, int g, int max_seq_len,
@@ -177,6 +237,16 @@ hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int group, hip
 }
 
 hipError_t launch_lse_merge(const DecodeArgs& a, int head_dim, hipStream_t st) {
+  if (a.num_splits <= kFewSplits) {
+    dim3 grid(a.q_len * a.num_seqs, (a.hq + 3) / 4);
+    if (head_dim == 256)
+      hipLaunchKernelGGL(lse_merge_few_kernel<256>, grid, dim3(256), 0, st, a);
+    else if (head_dim == 128)
+      hipLaunchKernelGGL(lse_merge_few_kernel<128>, grid, dim3(256), 0, st, a);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   dim3 grid(head_dim / 64, a.hq, a.q_len * a.num_seqs);
   if (head_dim == 256)
     hipLaunchKernelGGL(lse_merge_kernel<256>, grid, dim3(256), 0, st, a);

@@ -66,6 +66,10 @@ struct DecodeArgs {
   MagicDiv bdiv;            // division by block_size
   float scale_log2;         // scale * log2(e): scores kept in log2 units
   int32_t out_bf16;
+  // Varlen multi-row calls: cu_q[b] .. cu_q[b + 1] are sequence b's rows of the
+  // packed q / out ([total_q, Hq, D]); q_len is then the largest row count.
+  // nullptr for uniform calls (sequence b owns rows b * q_len .. + q_len).
+  const int32_t* cu_q;
 };
 
 // Launchers (decode_kernels.hip, decode_w*.hip, verify_kernels.hip). Return

@@ -75,6 +75,25 @@ __device__ __forceinline__ SplitSpan split_span(const DecodeArgs& a, int b, int 
   return r;
 }
 
+// Query rows of sequence b: rows [base, base + n) of the packed q and out.
+// Uniform calls: base = b * q_len, n = q_len. Varlen calls take them from
+// cu_q and check 0 <= cu_q[b] <= cu_q[b + 1] <= cu_q[num_seqs],
+// cu_q[b + 1] <= num_seqs * q_len (the workspace's rows) and n <= q_len; a
+// sequence that fails is skipped (n = 0, ok = false), so no row index leaves
+// the packed buffers or the workspace.
+struct QRows {
+  int base;
+  int n;
+  bool ok;
+};
+
+__device__ __forceinline__ QRows seq_q_rows(const DecodeArgs& a, int b) {
+  if (!a.cu_q) return {b * a.q_len, a.q_len, true};
+  const int lo = a.cu_q[b], hi = a.cu_q[b + 1], total = a.cu_q[a.num_seqs];
+  const bool ok = lo >= 0 && hi >= lo && hi - lo <= a.q_len && hi <= total && hi <= a.num_seqs * a.q_len;
+  return {ok ? lo : 0, ok ? hi - lo : 0, ok};
+}
+
 // Element offsets of one physical page's first row for KV head g, for K and
 // for V; k < 0 marks a table entry that is skipped.
 struct PageOffs {

@@ -1,5 +1,6 @@
-// Multi-row (speculative verify) paged attention for gfx950: q_len in [2, 16]
-// new query rows per sequence, each with its own causal bound, sharing one
+// Multi-row (speculative verify) paged attention for gfx950: up to 16 new
+// query rows per sequence (the same count for every sequence, or per sequence
+// through cu_seqlens_q), each with its own causal bound, sharing one
 // walk over the paged K/V. This is the case where q.k and p.v become small
 // dense contractions, so they run on MFMA.
 //
@@ -78,9 +79,14 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, ln = lane & 15;
-  const int q_len = a.q_len;
+  const QRows qr = seq_q_rows(a, b);
+  const int q_len = qr.n;                         // query rows of this sequence
   const int G = a.hq / a.hkv;
   const int R = G * q_len;                        // rows of this KV head (<= 128)
+  if (q_len == 0) {                               // no rows, or inconsistent cu_seqlens_q
+    if (!qr.ok && s == 0 && g == 0 && tid == 0 && a.err) atomicOr(a.err, 2u);
+    return;
+  }
   // The table slots do not depend on the sequence length: fetch them while
   // seq_lens is still in flight.
   const SplitPages pages = split_pages(a, s);
@@ -92,7 +98,7 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
     if (s == 0)   // empty sequence: zeros for every row of this KV head
       for (int i = tid; i < R * D; i += kVThreads) {
         const int f = i / D, d = i - f * D;
-        const int64_t prow = (int64_t(b) * q_len + f % q_len) * a.hq + int64_t(g) * G + f / q_len;
+        const int64_t prow = (int64_t(qr.base) + f % q_len) * a.hq + int64_t(g) * G + f / q_len;
         store_out(a, prow * D + d, 0.0f);
       }
     return;
@@ -109,7 +115,7 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
   // Q of row ln, as the B operand of S^T: k step kk holds d = 32 kk + 8 grp .. +8.
   uint4 qreg[kKSteps];
   {
-    const int64_t qoff = ((int64_t(b) * q_len + i_row) * a.hq + int64_t(g) * G + h_row) * D + 8 * grp;
+    const int64_t qoff = ((int64_t(qr.base) + i_row) * a.hq + int64_t(g) * G + h_row) * D + 8 * grp;
 #pragma unroll
     for (int kk = 0; kk < kKSteps; ++kk)
       qreg[kk] = (computes && row_valid) ? *reinterpret_cast<const uint4*>(a.q + qoff + 32 * kk)
@@ -252,7 +258,7 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
 
   if (!computes) return;
   // Rows 4 grp + r of O; their (max, sum) are held by lane 4 grp + r of each group.
-  const int64_t prow_base = (int64_t(b) * q_len) * a.hq + int64_t(g) * G;
+  const int64_t prow_base = int64_t(qr.base) * a.hq + int64_t(g) * G;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int src = 16 * grp + 4 * grp + r;
@@ -281,7 +287,7 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
 }  // namespace
 
 bool verify_supported(int head_dim, int group, int q_len) {
-  return (head_dim == 128 || head_dim == 256) && group >= 1 && q_len >= 2 && q_len <= 16 &&
+  return (head_dim == 128 || head_dim == 256) && group >= 1 && q_len >= 1 && q_len <= 16 &&
          group * q_len <= kVWaves * kRowsPerWave;
 }
 

@@ -236,6 +236,35 @@ def spec_verify(context: int = 32768, q_len: int = 16, **kw) -> DecodeCase:
     return make_case(1005, [context], q_len=q_len, block_size=784, **kw)
 
 
+def pack_varlen(case: DecodeCase, q_lens) -> tuple[np.ndarray, np.ndarray]:
+    """Packed query rows [total_q, Hq, D] and cu_seqlens_q [num_seqs + 1] for
+    per-sequence row counts q_lens (each <= case.q_len): sequence b keeps the
+    first q_lens[b] of its drawn rows."""
+    q_lens = [int(x) for x in q_lens]
+    assert len(q_lens) == case.num_seqs and all(0 <= n <= case.q_len for n in q_lens)
+    cu = np.zeros(len(q_lens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(q_lens)
+    rows = [case.q[b, :n] for b, n in enumerate(q_lens)]
+    q = np.concatenate(rows, axis=0) if rows else case.q[:0, 0]
+    return np.ascontiguousarray(q), cu
+
+
+def batched_verify(num_seqs: int = 32, max_rows: int = 5, lo: int = 512, hi: int = 2048,
+                   **kw) -> tuple[DecodeCase, np.ndarray, np.ndarray]:
+    """Batched speculative verify: num_seqs requests with 1..max_rows new rows
+    each (four drafted tokens give up to five positions), contexts log-uniform
+    in [lo, hi], 24/4/256, page 784, pages dealt round-robin. The row counts
+    continue the lengths stream. Returns (case, packed q, cu_seqlens_q)."""
+    seed = 1007
+    rng = streams(seed)["lengths"]
+    u = rng.uniform(math.log(lo), math.log(hi), size=num_seqs)
+    lens = np.clip(np.rint(np.exp(u)), lo, hi).astype(np.int32)
+    q_lens = rng.integers(1, max_rows + 1, size=num_seqs)
+    case = make_case(seed, lens, q_len=max_rows, block_size=784, interleave=True, **kw)
+    q, cu = pack_varlen(case, q_lens)
+    return case, q, cu
+
+
 def dense_control(context: int = 32768, **kw) -> DecodeCase:
     """Batch 1, q_len 1, 32 query heads, 8 KV heads, head_dim 128, page 16."""
     return make_case(1006, [context], num_q_heads=32, num_kv_heads=8, head_dim=128,

@@ -57,3 +57,24 @@ def assert_matches_oracle(gpu, ref, what=""):
     log(f"  {what}: max abs err {mx:.3e}, max rel err {rel:.3e}")
     assert mx <= ATOL, f"{what}: max abs err {mx} > {ATOL}"
     assert rel <= RTOL, f"{what}: max rel err {rel} > {RTOL}"
+
+
+def run_gpu_varlen(case, q_packed, cu, *, out=None, workspace=None, **kw):
+    """The varlen call through the C ABI on packed rows; returns (out as float64, workspace)."""
+    import torch
+    import paged_kv_cache_08_amd as P
+    _, k, v, table, lens = to_device(case)
+    q = bf16_tensor(q_packed)
+    cu_t = torch.from_numpy(np.ascontiguousarray(cu, dtype=np.int32)).cuda()
+    max_q = int(np.diff(cu).max(initial=1)) if kw.get("max_q_len") is None else kw.pop("max_q_len")
+    kw.pop("max_q_len", None)
+    if workspace is None:
+        p = P.make_params(torch.empty((case.num_seqs, max(max_q, 1), q.shape[1], q.shape[2]), device="meta"),
+                          k, v, table, case.block_size, case.scale, max_seq_len=case.max_seq_len,
+                          num_splits=kw.get("num_splits", 0))
+        workspace = torch.zeros(P.workspace_bytes(p, 0), dtype=torch.uint8, device="cuda")
+    got = P.paged_varlen_attention(q, k, v, table, lens, cu_t, case.block_size, case.scale,
+                                   max_q_len=max(max_q, 1), max_seq_len=case.max_seq_len, out=out,
+                                   workspace=workspace, **kw)
+    torch.cuda.synchronize()
+    return got.float().cpu().numpy().astype(np.float64), workspace

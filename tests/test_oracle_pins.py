@@ -435,3 +435,71 @@ def test_planted_mistakes_fail_the_pins(monkeypatch, name, attr, bad, q_len):
     monkeypatch.setattr(O, attr, bad)
     got = run_oracle(case)
     assert not np.allclose(got, ref, rtol=1e-6, atol=1e-8), name
+
+
+# ---------------------------------------------------------------------------
+# Varlen multi-row oracle (per-sequence row counts through cu_seqlens_q).
+# ---------------------------------------------------------------------------
+
+def brute_force_varlen(case: W.DecodeCase, q_packed, cu) -> np.ndarray:
+    """Dense attention over the logical rows, rows packed as cu says: row i of
+    sequence b (n_b rows) sees tokens 0 .. L_b - n_b + i."""
+    _, hq, d = q_packed.shape
+    hkv = case.logical_k[0].shape[1]
+    G = hq // hkv
+    sigma = float(np.float32(case.scale))
+    out = np.zeros(q_packed.shape)
+    for b in range(len(cu) - 1):
+        n = int(cu[b + 1] - cu[b])
+        L = int(case.seq_lens[b])
+        K, V = case.logical_k[b].tolist(), case.logical_v[b].tolist()
+        for i in range(n):
+            r = int(cu[b]) + i
+            pos = L - n + i
+            for h in range(hq):
+                qv = [_widen(x) for x in q_packed[r, h].tolist()]
+                s = [sigma * math.fsum(qv[e] * _widen(K[j][h // G][e]) for e in range(d)) for j in range(pos + 1)]
+                m = max(s)
+                ex = [math.exp(x - m) for x in s]
+                z = math.fsum(ex)
+                for e in range(d):
+                    out[r, h, e] = math.fsum(ex[j] * _widen(V[j][h // G][e]) for j in range(pos + 1)) / z
+    return out
+
+
+def test_varlen_oracle_matches_brute_force():
+    case = W.make_case(61, [9, 30, 4, 17], q_len=5, num_q_heads=6, num_kv_heads=2, head_dim=8,
+                       block_size=3, poison=False, interleave=True)
+    q, cu = W.pack_varlen(case, [3, 5, 0, 1])
+    assert cu.tolist() == [0, 3, 8, 8, 9] and q.shape == (9, 6, 8)
+    got = O.paged_attention_varlen_ref(q, cu, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                                       case.block_size, case.scale)
+    np.testing.assert_allclose(got, brute_force_varlen(case, q, cu), rtol=1e-12, atol=1e-13)
+
+
+def test_varlen_oracle_with_equal_rows_is_the_uniform_oracle():
+    case = W.make_case(62, [50, 12, 33], q_len=4, num_q_heads=6, num_kv_heads=2, head_dim=8,
+                       block_size=7, poison=True, interleave=True)
+    q, cu = W.pack_varlen(case, [4, 4, 4])
+    got = O.paged_attention_varlen_ref(q, cu, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                                       case.block_size, case.scale)
+    np.testing.assert_array_equal(got, run_oracle(case).reshape(got.shape))
+
+
+def test_varlen_single_row_sequences_are_decode_calls():
+    # n_b = 1 everywhere: each row is the q_len-1 decode of its sequence.
+    case = W.make_case(63, [20, 1, 7], q_len=3, num_q_heads=4, num_kv_heads=2, head_dim=4,
+                       block_size=5, poison=False)
+    q, cu = W.pack_varlen(case, [1, 1, 1])
+    got = O.paged_attention_varlen_ref(q, cu, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                                       case.block_size, case.scale)
+    dec = O.paged_attention_ref(case.q[:, :1], case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                                case.block_size, case.scale)
+    np.testing.assert_array_equal(got, dec[:, 0])
+
+
+def test_batched_verify_workload_shape():
+    case, q, cu = W.batched_verify(poison=False)
+    n = np.diff(cu)
+    assert case.num_seqs == 32 and n.min() >= 1 and n.max() <= 5 and q.shape[0] == cu[-1]
+    assert case.seq_lens.min() >= 512 and case.seq_lens.max() <= 2048
