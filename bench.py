@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--block-size", type=int, default=784)
     ap.add_argument("--pools", type=int, default=16)
     ap.add_argument("--splits", type=int, default=0, help="force a split count (0 = planner)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window: each query row sees its last W positions (0 = whole context)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--repeats", type=int, default=5, help="extra timed regions for spread statistics")
@@ -112,18 +114,18 @@ def traffic_from_profiles(kernel_src_hash: str, workload_key: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def oracle_call(case, varlen):
+def oracle_call(case, varlen, window):
     """The oracle's result for the benchmark input (pool 0)."""
     import oracle.paged_attention as O
     if varlen is not None:
         qp, cu = varlen
         return O.paged_attention_varlen_ref(qp, cu, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
-                                            case.block_size, case.scale)
+                                            case.block_size, case.scale, window)
     return O.paged_attention_ref(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
-                                 case.block_size, case.scale)
+                                 case.block_size, case.scale, window)
 
 
-def cpu_baseline(case, varlen, kv_bytes_per_call, seconds):
+def cpu_baseline(case, varlen, window, kv_bytes_per_call, seconds):
     """The oracle as it stands, on the host cores, over whole calls of the same
     workload until about `seconds` of CPU work has run."""
     try:
@@ -133,7 +135,7 @@ def cpu_baseline(case, varlen, kv_bytes_per_call, seconds):
         threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
     n, t0 = 0, time.perf_counter()
     while True:
-        oracle_call(case, varlen)
+        oracle_call(case, varlen, window)
         n += 1
         el = time.perf_counter() - t0
         if el >= seconds or n >= 1000:
@@ -183,11 +185,13 @@ def main():
     lens = torch.from_numpy(case.seq_lens).to(dev)
     pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(max(args.pools, 1) - 1)]
     total_tokens = int(case.seq_lens.sum())
-    kv_bytes = W.kv_read_bytes(case.seq_lens, case.k_cache.shape[2], case.k_cache.shape[3])
+    rows = [case.q_len] * case.num_seqs if varlen is None else np.diff(varlen[1])
+    kv_bytes = W.kv_read_bytes(case.seq_lens, case.k_cache.shape[2], case.k_cache.shape[3], window=args.window,
+                               rows=rows)
     stream = torch.cuda.current_stream(dev).cuda_stream
     call = P.PreparedDecode(q, k0, v0, table, lens, case.block_size, case.scale, max_seq_len=case.max_seq_len,
                             total_tokens=total_tokens, num_splits=args.splits, stream=stream,
-                            cu_seqlens_q=cu_t, max_q_len=max_q)
+                            cu_seqlens_q=cu_t, max_q_len=max_q, window=args.window)
     out = call.out
 
     ptrs = [(k.data_ptr(), v.data_ptr()) for k, v in pools]
@@ -260,7 +264,8 @@ def main():
             gcall = P.PreparedDecode(q, k0, v0, table, lens, case.block_size, case.scale,
                                      max_seq_len=case.max_seq_len, total_tokens=total_tokens,
                                      num_splits=args.splits, out=out, workspace=call.workspace,
-                                     stream=gstream.cuda_stream, cu_seqlens_q=cu_t, max_q_len=max_q)
+                                     stream=gstream.cuda_stream, cu_seqlens_q=cu_t, max_q_len=max_q,
+                                     window=args.window)
         torch.cuda.synchronize()
         with torch.cuda.graph(graph, stream=gstream):
             for i in range(args.steps):
@@ -285,7 +290,7 @@ def main():
     got = out.cpu().numpy().astype(np.float64)
     parity = None
     try:
-        ref = oracle_call(case, varlen)
+        ref = oracle_call(case, varlen, args.window)
         parity = float(np.abs(got - ref).max())
     except Exception as e:  # parity is reported, never required for the timing
         print(f"[bench] parity check skipped: {e}", file=sys.stderr)
@@ -294,12 +299,12 @@ def main():
     kern_gbs = kv_bytes / (kern_avg_us * 1e-6) / 1e9
     from paged_kv_cache_08_amd.profiling import kernel_source_hash
     src_hash = kernel_source_hash()
-    wl_key = f"{args.workload}:{args.context}:{case.block_size}"
+    wl_key = f"{args.workload}:{args.context}:{case.block_size}" + (f":w{args.window}" if args.window else "")
     traffic = traffic_from_profiles(src_hash, wl_key)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(case, varlen, kv_bytes, args.cpu_seconds)
+        cpu = cpu_baseline(case, varlen, args.window, kv_bytes, args.cpu_seconds)
 
     med = statistics.median(region_us)
     rec = {
@@ -320,6 +325,7 @@ def main():
             "batch": int(case.num_seqs),
             "query_rows": int(case.num_seqs * case.q_len if varlen is None else varlen[1][-1]),
             "context": int(case.max_seq_len),
+            "window": args.window,
             "block_size": int(case.block_size),
             "kv_pools_rotated": len(pools),
             "kv_bytes_per_step": kv_bytes,

@@ -17,6 +17,10 @@
  * For sequence b, query row i and query head h (G = Hq / Hkv, KV head h / G):
  *     out[b,i,h,:] = softmax_j( scale * q[b,i,h,:] . K_j ) V_j,
  *     j over tokens 0 .. seq_lens[b] - q_len + i   (bottom-right causal window)
+ * With a sliding window W > 0, row i sees only its last W of those tokens
+ * (j > seq_lens[b] - q_len + i - W): "如何在单张 RTX 3090 上让 Qwen3.5-27B
+ * token 生成速度提升 6 倍" restricts decode attention to the most recent
+ * 2,048 KV positions this way.
  *
  * Conventions shared by every entry point:
  *   - All pointers named *device* point to device memory on the current HIP
@@ -49,8 +53,8 @@ extern "C" {
 #define PKV_OUT_F32  0
 #define PKV_OUT_BF16 1
 
-/* Problem description. Layout is fixed: 10 x int32, 7 x int64, float, int32
- * (104 bytes, natural alignment). */
+/* Problem description. Layout is fixed: 10 x int32, 7 x int64, float, 3 x int32
+ * (112 bytes, natural alignment). */
 typedef struct pkv_decode_params {
   int32_t num_seqs;          /* sequences in the batch, >= 1 */
   int32_t q_len;             /* new query rows per sequence, 1..16 (1 = decode) */
@@ -72,6 +76,10 @@ typedef struct pkv_decode_params {
   int64_t v_stride_head;
   float   scale;             /* softmax scale applied to q . k (e.g. 1/sqrt(D)) */
   int32_t out_dtype;         /* PKV_OUT_F32 or PKV_OUT_BF16 */
+  int32_t window;            /* sliding window: the query row at position p sees only the
+                                tokens j with p - window < j <= p (the most recent `window`
+                                positions, its own included); 0 = the whole context */
+  int32_t reserved;          /* must be 0 */
 } pkv_decode_params;
 
 /* Library version string (static storage). */
@@ -92,16 +100,20 @@ const char* pkv_last_error(void);
 int pkv_validate_params(const pkv_decode_params* p);
 
 /* Host-only split plan (no HIP call). With T = 64-token tiles:
- *   n_tiles = ceil(max_seq_len / T);
+ *   span    = max_seq_len, or min(max_seq_len, window + q_len - 1) with a window;
+ *   n_tiles = ceil(span / T) (1 when span is 0);
  *   work    = total_tokens, or num_seqs * max_seq_len when total_tokens == 0;
+ *             with a window at most num_seqs * span;
  *   c       = max(min_tiles, ceil(Hkv * work / (cu_count * wg_per_cu * T))),
  *             or ceil(n_tiles / num_splits) when num_splits > 0;
  *   c       = clamp(c, 1, min(n_tiles, max_tiles));
  *   *num_splits = ceil(n_tiles / c); *chunk_tokens = c * T.
- * Sequence b then uses ceil(L_b / chunk) splits; split s covers tokens
- * [s * chunk, min((s + 1) * chunk, L_b)). A split never exceeds max_tiles * T
- * tokens (one unrolled window of the split kernel), so a requested num_splits
- * may be raised. cu_count must be >= 1. */
+ * Sequence b with n_b query rows sees tokens [lo_b, L_b), lo_b = 0, or
+ * max(0, L_b - n_b + 1 - window) with a window; it uses
+ * ceil((L_b - lo_b) / chunk) splits and split s covers
+ * [lo_b + s * chunk, min(lo_b + (s + 1) * chunk, L_b)). A split never exceeds
+ * max_tiles * T tokens (one unrolled window of the split kernel), so a
+ * requested num_splits may be raised. cu_count must be >= 1. */
 int pkv_plan_splits(const pkv_decode_params* p, int32_t cu_count,
                     int32_t* num_splits, int32_t* chunk_tokens);
 

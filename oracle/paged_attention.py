@@ -112,6 +112,13 @@ def last_visible(L: int, q_len: int, i: int) -> int:
     return L - q_len + i
 
 
+def first_visible(pos: int, window: int) -> int:
+    """First token a row whose last visible token is pos sees: 0, or with a
+    sliding window the start of its most recent `window` positions (the RTX
+    3090 page attends to the most recent 2,048 KV positions this way)."""
+    return max(0, pos - window + 1) if window > 0 else 0
+
+
 def _scaled_scores(keys: np.ndarray, qv: np.ndarray, sigma: float) -> np.ndarray:
     """score_j = sigma * dot(q, k_j) (the DCU page, §5)."""
     return sigma * (keys @ qv)
@@ -126,7 +133,7 @@ def _softmax_weighted_sum(scores: np.ndarray, values: np.ndarray) -> np.ndarray:
 
 
 def paged_attention_ref(q, k_cache, v_cache, block_table, seq_lens, block_size: int,
-                        scale: float) -> np.ndarray:
+                        scale: float, window: int = 0) -> np.ndarray:
     """fp64 paged attention for all sequences, query rows and query heads.
 
     q: uint16 bf16 bits [num_seqs, q_len, Hq, D]; k_cache / v_cache: uint16
@@ -149,16 +156,17 @@ def paged_attention_ref(q, k_cache, v_cache, block_table, seq_lens, block_size: 
         V = [gather_token_rows(v_cache, block_table[b], L, block_size, g) for g in range(hkv)]
         for i in range(q_len):
             pos = last_visible(L, q_len, i)
+            lo = first_visible(pos, window)
             for h in range(hq):
                 g = kv_head_of(h, G)
                 qv = bf16_bits_to_f64(q[b, i, h])
-                s = _scaled_scores(K[g][: pos + 1], qv, sigma)
-                out[b, i, h] = _softmax_weighted_sum(s, V[g][: pos + 1])
+                s = _scaled_scores(K[g][lo: pos + 1], qv, sigma)
+                out[b, i, h] = _softmax_weighted_sum(s, V[g][lo: pos + 1])
     return out
 
 
 def paged_attention_varlen_ref(q_packed, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens,
-                               block_size: int, scale: float) -> np.ndarray:
+                               block_size: int, scale: float, window: int = 0) -> np.ndarray:
     """Varlen multi-row attention: sequence b owns query rows
     q_packed[cu[b]:cu[b+1]] (n_b of them, [total_q, Hq, D] bf16 bits) and row i
     sees tokens j <= L_b - n_b + i, exactly as a call with q_len = n_b on that
@@ -172,7 +180,7 @@ def paged_attention_varlen_ref(q_packed, cu_seqlens_q, k_cache, v_cache, block_t
         if hi == lo:
             continue
         out[lo:hi] = paged_attention_ref(q_packed[None, lo:hi], k_cache, v_cache, block_table[b:b + 1],
-                                         np.asarray(seq_lens)[b:b + 1], block_size, scale)[0]
+                                         np.asarray(seq_lens)[b:b + 1], block_size, scale, window)[0]
     return out
 
 
@@ -206,7 +214,7 @@ def merge_partials_ref(parts) -> np.ndarray:
 
 
 def split_attention_ref(q, k_cache, v_cache, block_table, seq_lens, block_size: int,
-                        scale: float, ranges) -> np.ndarray:
+                        scale: float, ranges, window: int = 0) -> np.ndarray:
     """Same result as paged_attention_ref, evaluated split by split and merged.
 
     ranges[b] is a list of [begin, end) token ranges that partition [0, L_b).
@@ -225,17 +233,18 @@ def split_attention_ref(q, k_cache, v_cache, block_table, seq_lens, block_size: 
         V = [gather_token_rows(v_cache, block_table[b], L, block_size, g) for g in range(hkv)]
         for i in range(q_len):
             pos = last_visible(L, q_len, i)
+            first = first_visible(pos, window)
             for h in range(hq):
                 g = kv_head_of(h, G)
                 qv = bf16_bits_to_f64(q[b, i, h])
                 parts = []
                 for (lo, hi) in ranges[b]:
-                    hi_vis = min(hi, pos + 1)
-                    if hi_vis <= lo:
+                    lo_vis, hi_vis = max(lo, first), min(hi, pos + 1)
+                    if hi_vis <= lo_vis:
                         parts.append(partial_stats_ref(np.zeros(0), V[g][:0]))
                         continue
-                    s = _scaled_scores(K[g][lo:hi_vis], qv, sigma)
-                    parts.append(partial_stats_ref(s, V[g][lo:hi_vis]))
+                    s = _scaled_scores(K[g][lo_vis:hi_vis], qv, sigma)
+                    parts.append(partial_stats_ref(s, V[g][lo_vis:hi_vis]))
                 out[b, i, h] = merge_partials_ref(parts)
     return out
 
@@ -245,16 +254,22 @@ def split_attention_ref(q, k_cache, v_cache, block_table, seq_lens, block_size: 
 # plan this library defines, restated here in plain integers so the library's
 # planner can be checked against it exactly.
 #
-#   T          tile of logical tokens; split boundaries are multiples of T
-#   n_tiles    = ceil(max_seq_len / T)
-#   work       = total_tokens if given, else num_seqs * max_seq_len
+#   T          tile of logical tokens; splits are whole tiles from a sequence's
+#              first visible token
+#   span       = max_seq_len, or min(max_seq_len, window + q_len - 1) with a
+#              sliding window (the union of a sequence's rows' windows)
+#   n_tiles    = ceil(span / T)
+#   work       = total_tokens if given, else num_seqs * max_seq_len; with a
+#              window at most num_seqs * span
 #   c (tiles)  = ceil(Hkv * work / (cu_count * wg_per_cu * T)), at least min_tiles;
 #                a forced split count S_f instead gives c = ceil(n_tiles / S_f);
 #                then at most n_tiles and at most max_tiles (a split is one
 #                window of the split kernel)
 #   S          = ceil(n_tiles / c);   chunk = c * T tokens
-#   sequence b uses S_b = ceil(L_b / chunk) splits; split s covers
-#   [s * chunk, min((s + 1) * chunk, L_b)).
+#   sequence b with n_b query rows sees [lo_b, L_b), lo_b = 0, or
+#   max(0, L_b - n_b + 1 - window) with a window; it uses
+#   S_b = ceil((L_b - lo_b) / chunk) splits and split s covers
+#   [lo_b + s * chunk, min(lo_b + (s + 1) * chunk, L_b)).
 # ---------------------------------------------------------------------------
 
 def _cdiv(a: int, b: int) -> int:
@@ -264,27 +279,32 @@ def _cdiv(a: int, b: int) -> int:
 def split_plan_ref(num_seqs: int, num_kv_heads: int, max_seq_len: int, block_size: int,
                    cu_count: int, *, total_tokens: int = 0, forced_splits: int = 0,
                    tile: int = 64, wg_per_cu: int = 1, min_tiles: int = 1,
-                   max_tiles: int = 8) -> tuple[int, int]:
+                   max_tiles: int = 8, window: int = 0, q_len: int = 1) -> tuple[int, int]:
     """Return (S, chunk_tokens). block_size does not enter the plan."""
-    n_tiles = max(1, _cdiv(max_seq_len, tile))
+    span = min(max_seq_len, window + q_len - 1) if window > 0 else max_seq_len
+    n_tiles = max(1, _cdiv(span, tile))
     if forced_splits > 0:
         c = _cdiv(n_tiles, forced_splits)
     else:
         work = total_tokens if total_tokens > 0 else num_seqs * max_seq_len
+        if window > 0:
+            work = min(work, num_seqs * span)
         target = max(1, cu_count * wg_per_cu)
         c = max(min_tiles, _cdiv(num_kv_heads * work, target * tile))
     c = max(1, min(c, n_tiles, max_tiles))
     return _cdiv(n_tiles, c), c * tile
 
 
-def split_ranges_ref(seq_lens, num_splits: int, chunk: int) -> np.ndarray:
-    """[num_seqs, num_splits, 2] array of [begin, end); unused splits are [L, L)."""
+def split_ranges_ref(seq_lens, num_splits: int, chunk: int, window: int = 0, rows: int = 1) -> np.ndarray:
+    """[num_seqs, num_splits, 2] array of [begin, end); unused splits are [L, L).
+    With a window, sequence b's splits start at max(0, L - rows + 1 - window)."""
     seq_lens = [int(x) for x in np.asarray(seq_lens).tolist()]
     r = np.zeros((len(seq_lens), num_splits, 2), dtype=np.int32)
     for b, L in enumerate(seq_lens):
+        first = max(0, L - rows + 1 - window) if window > 0 else 0
         for s in range(num_splits):
-            lo = min(s * chunk, L)
-            hi = min((s + 1) * chunk, L)
+            lo = min(first + s * chunk, L)
+            hi = min(first + (s + 1) * chunk, L)
             r[b, s] = (lo, hi)
     return r
 

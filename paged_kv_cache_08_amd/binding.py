@@ -44,10 +44,12 @@ class DecodeParams(ctypes.Structure):
         ("v_stride_head", ctypes.c_int64),
         ("scale", ctypes.c_float),
         ("out_dtype", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
-assert ctypes.sizeof(DecodeParams) == 104
+assert ctypes.sizeof(DecodeParams) == 112
 
 _lock = threading.Lock()
 _lib = None
@@ -164,7 +166,8 @@ def _torch():
 
 
 def make_params(q, k_cache, v_cache, block_table, block_size: int, scale: float, *, max_seq_len: int,
-                num_splits: int = 0, total_tokens: int = 0, out_dtype: int = PKV_OUT_F32) -> DecodeParams:
+                num_splits: int = 0, total_tokens: int = 0, out_dtype: int = PKV_OUT_F32,
+                window: int = 0) -> DecodeParams:
     """Fill DecodeParams from tensor shapes and strides.
 
     q: [num_seqs, q_len, Hq, D]; k_cache / v_cache: [num_pages, B, Hkv, D] with
@@ -185,13 +188,15 @@ def make_params(q, k_cache, v_cache, block_table, block_size: int, scale: float,
     p.v_stride_page, p.v_stride_tok, p.v_stride_head = v_cache.stride(0), v_cache.stride(1), v_cache.stride(2)
     p.scale = float(scale)
     p.out_dtype = out_dtype
+    p.window = int(window)
     return p
 
 
 def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, block_size: int, scale: float, *,
                            max_seq_len: int | None = None, total_tokens: int = 0, num_splits: int = 0,
-                           out=None, out_dtype=None, workspace=None, stream=None):
-    """out[b,i,h,:] = softmax(scale * q[b,i,h,:] . K_j) V_j over the visible tokens of sequence b.
+                           out=None, out_dtype=None, workspace=None, stream=None, window: int = 0):
+    """out[b,i,h,:] = softmax(scale * q[b,i,h,:] . K_j) V_j over the visible tokens of sequence b
+    (with window > 0, only the last `window` of them for each row).
 
     q: bf16 [num_seqs, q_len, Hq, D] (contiguous, on the GPU); k_cache / v_cache:
     bf16 [num_pages, B, Hkv, D] (views of a combined [num_pages, 2, B, Hkv, D]
@@ -211,7 +216,7 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, block_siz
     odt = PKV_OUT_BF16 if out.dtype == torch.bfloat16 else PKV_OUT_F32
     assert out.dtype in (torch.float32, torch.bfloat16) and out.is_contiguous() and out.shape == q.shape
     p = make_params(q, k_cache, v_cache, block_table, block_size, scale, max_seq_len=max_seq_len,
-                    num_splits=num_splits, total_tokens=total_tokens, out_dtype=odt)
+                    num_splits=num_splits, total_tokens=total_tokens, out_dtype=odt, window=window)
     need = workspace_bytes(p, 0)
     if workspace is None:
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
@@ -227,7 +232,8 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, block_siz
 
 def paged_varlen_attention(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, block_size: int,
                            scale: float, *, max_q_len: int, max_seq_len: int, total_tokens: int = 0,
-                           num_splits: int = 0, out=None, out_dtype=None, workspace=None, stream=None):
+                           num_splits: int = 0, out=None, out_dtype=None, workspace=None, stream=None,
+                           window: int = 0):
     """Varlen multi-row call: sequence b's query rows are q[cu_seqlens_q[b]:cu_seqlens_q[b+1]].
 
     q: bf16 [total_q, Hq, D] packed rows (contiguous, on the GPU); cu_seqlens_q:
@@ -247,7 +253,7 @@ def paged_varlen_attention(q, k_cache, v_cache, block_table, seq_lens, cu_seqlen
     assert out.dtype in (torch.float32, torch.bfloat16) and out.is_contiguous() and out.shape == q.shape
     shape4 = torch.empty((ns, int(max_q_len), q.shape[1], q.shape[2]), device="meta")
     p = make_params(shape4, k_cache, v_cache, block_table, block_size, scale, max_seq_len=max_seq_len,
-                    num_splits=num_splits, total_tokens=total_tokens, out_dtype=odt)
+                    num_splits=num_splits, total_tokens=total_tokens, out_dtype=odt, window=window)
     need = workspace_bytes(p, 0)
     if workspace is None:
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
@@ -301,7 +307,7 @@ class PreparedDecode:
 
     def __init__(self, q, k_cache, v_cache, block_table, seq_lens, block_size: int, scale: float, *,
                  max_seq_len: int, total_tokens: int = 0, num_splits: int = 0, out=None, workspace=None,
-                 stream=None, cu_seqlens_q=None, max_q_len: int | None = None):
+                 stream=None, cu_seqlens_q=None, max_q_len: int | None = None, window: int = 0):
         torch = _torch()
         assert q.is_cuda and q.dtype == torch.bfloat16 and q.is_contiguous()
         assert block_table.is_contiguous() and seq_lens.is_contiguous()
@@ -316,7 +322,7 @@ class PreparedDecode:
         else:
             shape = q
         self.params = make_params(shape, k_cache, v_cache, block_table, block_size, scale, max_seq_len=max_seq_len,
-                                  num_splits=num_splits, total_tokens=total_tokens, out_dtype=odt)
+                                  num_splits=num_splits, total_tokens=total_tokens, out_dtype=odt, window=window)
         if not self.varlen:
             check(validate(self.params), "pkv_validate_params")
         need = workspace_bytes(self.params, 0)
@@ -332,26 +338,19 @@ class PreparedDecode:
         self._pp = ctypes.byref(self.params)
         self._fixed = (q.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
                        workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
-        if self.varlen:
-            fn, cup, name = lib().pkv_paged_varlen_attention, cu_seqlens_q.data_ptr(), "pkv_paged_varlen_attention"
-
-            def call(kp, vp):
-                qp, tp, lp, op, wp, wn, st = self._fixed
-                return fn(self._pp, qp, kp, vp, tp, lp, cup, op, wp, wn, st)
-        else:
-            fn, name = lib().pkv_paged_decode_attention, "pkv_paged_decode_attention"
-
-            def call(kp, vp):
-                qp, tp, lp, op, wp, wn, st = self._fixed
-                return fn(self._pp, qp, kp, vp, tp, lp, op, wp, wn, st)
-        self._call, self._name = call, name
+        self._cu = cu_seqlens_q.data_ptr() if self.varlen else None
+        self._fn = lib().pkv_paged_varlen_attention if self.varlen else lib().pkv_paged_decode_attention
         self._k, self._v = k_cache.data_ptr(), v_cache.data_ptr()
 
     def run_ptrs(self, k_ptr: int, v_ptr: int) -> None:
         """Like run() with raw device pointers of a pool laid out like the original."""
-        rc = self._call(k_ptr, v_ptr)
+        qp, tp, lp, op, wp, wn, st = self._fixed
+        if self._cu is None:
+            rc = self._fn(self._pp, qp, k_ptr, v_ptr, tp, lp, op, wp, wn, st)
+        else:
+            rc = self._fn(self._pp, qp, k_ptr, v_ptr, tp, lp, self._cu, op, wp, wn, st)
         if rc != PKV_OK:
-            check(rc, self._name)
+            check(rc, "pkv_paged_varlen_attention" if self.varlen else "pkv_paged_decode_attention")
 
     def run(self, k_cache=None, v_cache=None):
         kp, vp = self._k, self._v

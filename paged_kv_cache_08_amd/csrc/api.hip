@@ -41,15 +41,27 @@ int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
 bool mult8_pos(int64_t s) { return s > 0 && (s % 8) == 0; }
 
+static_assert(sizeof(pkv_decode_params) == 112, "pkv_decode_params layout");
+
+// Longest token range one sequence's splits must cover: the whole context,
+// or with a sliding window the union of its rows' windows (window + q_len - 1).
+int64_t plan_span(const pkv_decode_params* p) {
+  int64_t span = p->max_seq_len;
+  if (p->window > 0 && int64_t(p->window) + p->q_len - 1 < span) span = int64_t(p->window) + p->q_len - 1;
+  return span;
+}
+
 int plan(const pkv_decode_params* p, int32_t cu_count, int32_t* S, int32_t* chunk) {
   const int64_t T = pkv::kTile;
-  const int64_t n_tiles = p->max_seq_len > 0 ? cdiv64(p->max_seq_len, T) : 1;
+  const int64_t span = plan_span(p);
+  const int64_t n_tiles = span > 0 ? cdiv64(span, T) : 1;
   const int64_t cap = pkv::kMaxTiles;
   int64_t c;
   if (p->num_splits > 0) {
     c = cdiv64(n_tiles, p->num_splits);
   } else {
-    const int64_t work = p->total_tokens > 0 ? p->total_tokens : int64_t(p->num_seqs) * p->max_seq_len;
+    int64_t work = p->total_tokens > 0 ? p->total_tokens : int64_t(p->num_seqs) * p->max_seq_len;
+    if (p->window > 0 && int64_t(p->num_seqs) * span < work) work = int64_t(p->num_seqs) * span;
     int64_t target = int64_t(cu_count) * pkv::kWgPerCu;
     if (target < 1) target = 1;
     c = cdiv64(int64_t(p->num_kv_heads) * work, target * T);
@@ -106,6 +118,7 @@ pkv::DecodeArgs make_args(const pkv_decode_params* p, int32_t S, int32_t chunk) 
   a.bdiv = pkv::make_magic(uint32_t(p->block_size));
   a.scale_log2 = float(double(p->scale) * 1.4426950408889634);
   a.out_bf16 = p->out_dtype == PKV_OUT_BF16;
+  a.window = p->window;
   return a;
 }
 
@@ -113,7 +126,7 @@ pkv::DecodeArgs make_args(const pkv_decode_params* p, int32_t S, int32_t chunk) 
 
 extern "C" {
 
-const char* pkv_version(void) { return "pkv 0.1.0 gfx950"; }
+const char* pkv_version(void) { return "pkv 0.2.0 gfx950"; }
 
 const char* pkv_strerror(int code) {
   switch (code) {
@@ -138,8 +151,9 @@ int validate_common(const pkv_decode_params* p) {
   if (!p) return fail(PKV_ERR_INVALID, "params is NULL");
   if (p->num_seqs < 1 || p->q_len < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1 ||
       p->block_size < 1 || p->max_pages_per_seq < 1 || p->num_pages < 1 || p->max_seq_len < 0 ||
-      p->num_splits < 0 || p->total_tokens < 0)
+      p->num_splits < 0 || p->total_tokens < 0 || p->window < 0)
     return fail(PKV_ERR_INVALID, "a size is out of range");
+  if (p->reserved != 0) return fail(PKV_ERR_INVALID, "reserved must be 0");
   if (p->num_q_heads % p->num_kv_heads != 0)
     return fail(PKV_ERR_INVALID, "num_q_heads is not a multiple of num_kv_heads");
   if (p->head_dim != 128 && p->head_dim != 256) return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 128 or 256");

@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(DecodeArgs a) {
   if (i >= qr.n) return;          // no such row in a varlen batch
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int d = cb * 64 + lane;
-  const SplitSpan sp = split_span(a, b, 0);
+  const SplitSpan sp = split_span(a, b, 0, qr.n);
   if (sp.nsplit <= 1) return;    // written by the split kernel
   const int ns = sp.nsplit;
   const int64_t prow = (int64_t(qr.base) + i) * a.hq + h;
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void lse_merge_few_kernel(DecodeArgs a) {
   if (h >= a.hq) return;
   const QRows qr = seq_q_rows(a, b);
   if (i >= qr.n) return;          // no such row in a varlen batch
-  const SplitSpan sp = split_span(a, b, 0);
+  const SplitSpan sp = split_span(a, b, 0, qr.n);
   if (sp.nsplit <= 1) return;    // written by the split kernel
   const int ns = sp.nsplit;      // <= num_splits <= kFewSplits
   const int64_t prow = (int64_t(qr.base) + i) * a.hq + h;
@@ -190,11 +190,11 @@ __global__ __launch_bounds__(kThreads) void debug_offsets_kernel(DecodeArgs a, i
                                                                  int64_t* k_off, int64_t* v_off) {
   __shared__ PageOffs tbl[kTblSplit];
   const int s = blockIdx.x, b = blockIdx.y;
-  const SplitPages pages = split_pages(a, s);
+  const SplitSpan sp = split_span(a, b, s, a.q_len);
+  if (sp.begin >= sp.L) return;
+  const SplitPages pages = a.window == 0 ? split_pages(a, s) : span_pages(a, sp);
   const int p_first = pages.p_first;
   stage_table(a, b, g, p_first, pages.n, tbl);
-  const SplitSpan sp = split_span(a, b, s);
-  if (sp.begin >= sp.L) return;
   __syncthreads();
   const int t_end = min(sp.end, max_seq_len);
   for (int t = sp.begin + threadIdx.x; t < t_end; t += kThreads) {
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kThreads) void debug_offsets_kernel(DecodeArgs a, i
 __global__ void debug_ranges_kernel(DecodeArgs a, int32_t* ranges) {
   const int b = blockIdx.x;
   for (int s = threadIdx.x; s < a.num_splits; s += blockDim.x) {
-    const SplitSpan sp = split_span(a, b, s);
+    const SplitSpan sp = split_span(a, b, s, a.q_len);
     const int lo = min(sp.begin, sp.L);
     const int hi = max(lo, sp.end);
     ranges[(int64_t(b) * a.num_splits + s) * 2] = lo;

@@ -168,11 +168,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   const int lane = tid & 63, wave = tid >> 6;
   const int row = lane >> 4, col = lane & 15;
 
-  // The table slots and q do not depend on the sequence length: fetch them
-  // while seq_lens is still in flight.
-  const SplitPages pages = split_pages(a, s);
-  const int p_first = pages.p_first;
-  stage_table(a, b, g, p_first, pages.n, tbl);
+  // Without a sliding window the table slots and q do not depend on the
+  // sequence length: fetch them while seq_lens is still in flight.
+  SplitPages pages = split_pages(a, s);
+  if (a.window == 0) stage_table(a, b, g, pages.p_first, pages.n, tbl);
   // q of the group's G heads: lane col holds elements [k*128 + col*8, +8) of each head.
   uint4 qv[G][kCpl];
   {
@@ -184,12 +183,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
         qv[h][k] = *reinterpret_cast<const uint4*>(qp + h * D + k * 128);
   }
 
-  const SplitSpan sp = split_span(a, b, s);
+  const SplitSpan sp = split_span(a, b, s, 1);
   if (sp.begin >= sp.L) {
     if (s == 0)   // empty sequence: zeros
       for (int i = tid; i < G * D; i += kThreads) store_out(a, out_row0 + i, 0.0f);
     return;
   }
+  if (a.window > 0) {   // the split starts at the window's first token
+    pages = span_pages(a, sp);
+    stage_table(a, b, g, pages.p_first, pages.n, tbl);
+  }
+  const int p_first = pages.p_first;
   __syncthreads();
   flag_invalid_entries(a, tbl, int(magic_div(uint32_t(sp.end - 1), a.bdiv)) - p_first + 1);
 

@@ -70,6 +70,7 @@ struct DecodeArgs {
   // packed q / out ([total_q, Hq, D]); q_len is then the largest row count.
   // nullptr for uniform calls (sequence b owns rows b * q_len .. + q_len).
   const int32_t* cu_q;
+  int32_t window;           // sliding window in positions (0 = whole context)
 };
 
 // Launchers (decode_kernels.hip, decode_w*.hip, verify_kernels.hip). Return

@@ -44,34 +44,45 @@ __device__ __forceinline__ void store_out(const DecodeArgs& a, int64_t idx, floa
 }
 
 struct SplitSpan {
-  int L;        // live tokens of the sequence (clamped to what the table can map)
+  int L;        // live tokens of the sequence (clamped to what the table and the plan can map)
+  int lo;       // first token the sequence's query rows can see
   int begin;    // first token of the split
   int end;      // one past the last token
   int nsplit;   // splits this sequence uses
 };
 
-// Longest token range the launch can map: what the block table can address
-// and what the planned splits cover. A sequence length is clamped to it, so a
-// length above the host's max_seq_len can never index past the table, the
-// grid or the workspace.
-// (The host keeps max_seq_len <= 2^30, so the planned range fits an int.)
+// Longest token range the launch can map without a sliding window: what the
+// block table can address and what the planned splits cover. (The host keeps
+// max_seq_len <= 2^30, so the planned range fits an int.)
 __device__ __forceinline__ int planned_cap(const DecodeArgs& a) {
   const int64_t cap = int64_t(a.max_pages) * int64_t(a.bdiv.d);
   const int64_t planned = int64_t(a.num_splits) * a.chunk;
   return int(cap < planned ? cap : planned);
 }
 
-// Split s of sequence b: [s * chunk, min((s + 1) * chunk, L)), L clamped to
-// planned_cap().
-__device__ __forceinline__ SplitSpan split_span(const DecodeArgs& a, int b, int s) {
-  const int cap = planned_cap(a);
-  int L = a.seq_lens[b];
-  L = L < 0 ? 0 : (L > cap ? cap : L);
+// Tokens that sequence b's `rows` query rows can see: [lo, L), lo = 0, or with
+// a sliding window max(0, L - rows + 1 - window) (the union of the rows'
+// windows). Split s covers [lo + s * chunk, min(lo + (s + 1) * chunk, L)). L
+// is clamped to what the block table can map and [lo, L) to what the planned
+// splits cover, so a length above the host's max_seq_len can never index past
+// the table, the grid or the workspace.
+__device__ __forceinline__ SplitSpan split_span(const DecodeArgs& a, int b, int s, int rows) {
+  const int64_t table_cap = int64_t(a.max_pages) * int64_t(a.bdiv.d);
+  const int64_t planned = int64_t(a.num_splits) * a.chunk;
+  int64_t L = a.seq_lens[b];
+  L = L < 0 ? 0 : (L > table_cap ? table_cap : L);
+  int64_t lo = 0;
+  if (a.window > 0) {
+    lo = L - rows + 1 - a.window;
+    lo = lo < 0 ? 0 : lo;
+  }
+  if (L - lo > planned) L = lo + planned;
   SplitSpan r;
-  r.L = L;
-  r.begin = s * a.chunk;
+  r.L = int(L);
+  r.lo = int(lo);
+  r.begin = r.lo + s * a.chunk;
   r.end = min(r.begin + a.chunk, r.L);
-  r.nsplit = (r.L + a.chunk - 1) / a.chunk;
+  r.nsplit = (r.L - r.lo + a.chunk - 1) / a.chunk;
   return r;
 }
 
@@ -110,12 +121,22 @@ struct SplitPages {
   int n;   // 0: the split is empty for every sequence length
 };
 
+// Without a sliding window: the pages split s may touch follow from the plan
+// alone (the split starts at s * chunk for every sequence length).
 __device__ __forceinline__ SplitPages split_pages(const DecodeArgs& a, int s) {
   const int begin = s * a.chunk;
   const int end = min(begin + a.chunk, planned_cap(a));
   SplitPages r;
   r.p_first = int(magic_div(uint32_t(begin), a.bdiv));
   r.n = end > begin ? int(magic_div(uint32_t(end - 1), a.bdiv)) - r.p_first + 1 : 0;
+  return r;
+}
+
+// The pages of a split's real range [begin, end) (end > begin).
+__device__ __forceinline__ SplitPages span_pages(const DecodeArgs& a, const SplitSpan& sp) {
+  SplitPages r;
+  r.p_first = int(magic_div(uint32_t(sp.begin), a.bdiv));
+  r.n = int(magic_div(uint32_t(sp.end - 1), a.bdiv)) - r.p_first + 1;
   return r;
 }
 

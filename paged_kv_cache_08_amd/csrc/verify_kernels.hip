@@ -89,10 +89,9 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
   }
   // The table slots do not depend on the sequence length: fetch them while
   // seq_lens is still in flight.
-  const SplitPages pages = split_pages(a, s);
-  const int p_first = pages.p_first;
-  stage_table(a, b, g, p_first, pages.n, tbl);
-  const SplitSpan sp = split_span(a, b, s);
+  SplitPages pages = split_pages(a, s);
+  if (a.window == 0) stage_table(a, b, g, pages.p_first, pages.n, tbl);
+  const SplitSpan sp = split_span(a, b, s, q_len);
 
   if (sp.begin >= sp.L) {
     if (s == 0)   // empty sequence: zeros for every row of this KV head
@@ -103,6 +102,11 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
       }
     return;
   }
+  if (a.window > 0) {   // the split starts at the first token of the rows' windows
+    pages = span_pages(a, sp);
+    stage_table(a, b, g, pages.p_first, pages.n, tbl);
+  }
+  const int p_first = pages.p_first;
 
   // This lane's S^T row (row ln of the wave's block).
   const bool computes = wave * kRowsPerWave < R;  // uniform per wave
@@ -185,7 +189,7 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = t0 + tb * 16 + r;
-          const bool vis = row_valid && t < sp.end && t <= pos_row;
+          const bool vis = row_valid && t < sp.end && t <= pos_row && (a.window == 0 || t > pos_row - a.window);
           const float x = vis ? st[tb][r] * a.scale_log2 : -INFINITY;
           st[tb][r] = x;
           mt = fmaxf(mt, x);

@@ -271,6 +271,13 @@ def dense_control(context: int = 32768, **kw) -> DecodeCase:
                      block_size=16, **kw)
 
 
-def kv_read_bytes(seq_lens, num_kv_heads: int, head_dim: int, elem_bytes: int = 2) -> int:
-    """Algorithmic K+V bytes one decode call must read: every live token once."""
-    return int(2 * int(np.sum(np.asarray(seq_lens, dtype=np.int64))) * num_kv_heads * head_dim * elem_bytes)
+def kv_read_bytes(seq_lens, num_kv_heads: int, head_dim: int, elem_bytes: int = 2, *, window: int = 0,
+                  rows=None) -> int:
+    """Algorithmic K+V bytes one call must read: every token some query row of
+    its sequence sees, once. With a sliding window, sequence b's rows (rows[b],
+    default 1) see the last min(L_b, window + rows[b] - 1) tokens."""
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    if window > 0:
+        r = np.ones_like(lens) if rows is None else np.asarray(rows, dtype=np.int64)
+        lens = np.minimum(lens, window + r - 1)
+    return int(2 * int(lens.sum()) * num_kv_heads * head_dim * elem_bytes)

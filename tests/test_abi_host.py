@@ -63,6 +63,9 @@ def params(**kw):
     ({"num_q_heads": 48, "q_len": 11}, -2),  # 132 rows > 128
     ({"num_q_heads": 32, "q_len": 16}, 0),   # 8 x 16 = 128 rows
     ({"q_len": 17}, -2),
+    ({"window": 2048}, 0),
+    ({"window": -1}, -1),
+    ({"reserved": 1}, -1),
     ({"q_len": 0}, -1),
     ({"block_size": 0}, -1),
     ({"max_seq_len": 42 * 784 + 1}, -1),
@@ -104,6 +107,12 @@ PLAN = [
     dict(num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, max_pages_per_seq=2048,
          k_stride_page=16 * 8 * 128, k_stride_tok=8 * 128, k_stride_head=128,
          v_stride_page=16 * 8 * 128, v_stride_tok=8 * 128, v_stride_head=128),
+    dict(window=2048),
+    dict(window=1),
+    dict(window=100000),
+    dict(window=2048, q_len=16),
+    dict(window=500, num_splits=4),
+    dict(num_seqs=16, max_seq_len=32000, total_tokens=121000, max_pages_per_seq=41, window=2048),
 ]
 
 
@@ -113,7 +122,8 @@ def test_planner_matches_oracle_plan_exactly(kw, cu):
     p = params(**kw)
     got = P.plan_splits(p, cu)
     ref = O.split_plan_ref(p.num_seqs, p.num_kv_heads, p.max_seq_len, p.block_size, cu,
-                           total_tokens=p.total_tokens, forced_splits=p.num_splits)
+                           total_tokens=p.total_tokens, forced_splits=p.num_splits, window=p.window,
+                           q_len=p.q_len)
     assert got == ref
 
 

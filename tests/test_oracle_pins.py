@@ -503,3 +503,93 @@ def test_batched_verify_workload_shape():
     n = np.diff(cu)
     assert case.num_seqs == 32 and n.min() >= 1 and n.max() <= 5 and q.shape[0] == cu[-1]
     assert case.seq_lens.min() >= 512 and case.seq_lens.max() <= 2048
+
+
+# ---------------------------------------------------------------------------
+# Sliding window (each row sees only its most recent `window` positions).
+# ---------------------------------------------------------------------------
+
+def brute_force_window(case: W.DecodeCase, window: int) -> np.ndarray:
+    """Dense attention over the logical rows where row i of q_len sees tokens
+    max(0, p - window + 1) .. p, p = L - q_len + i."""
+    ns, ql, hq, d = case.q.shape
+    G = hq // case.logical_k[0].shape[1]
+    sigma = float(np.float32(case.scale))
+    out = np.zeros((ns, ql, hq, d))
+    for b in range(ns):
+        L = int(case.seq_lens[b])
+        K, V = case.logical_k[b].tolist(), case.logical_v[b].tolist()
+        for i in range(ql):
+            p = L - ql + i
+            toks = range(max(0, p - window + 1), p + 1)
+            for h in range(hq):
+                qv = [_widen(x) for x in case.q[b, i, h].tolist()]
+                s = [sigma * math.fsum(qv[e] * _widen(K[j][h // G][e]) for e in range(d)) for j in toks]
+                m = max(s)
+                ex = [math.exp(x - m) for x in s]
+                z = math.fsum(ex)
+                for e in range(d):
+                    out[b, i, h, e] = math.fsum(w * _widen(V[j][h // G][e]) for w, j in zip(ex, toks)) / z
+    return out
+
+
+@pytest.mark.parametrize("window,ql", [(1, 1), (5, 1), (7, 3), (16, 4), (100, 2)])
+def test_window_oracle_matches_brute_force(window, ql):
+    case = W.make_case(71, [40, 9, 23], q_len=ql, num_q_heads=6, num_kv_heads=2, head_dim=8,
+                       block_size=5, poison=True, interleave=True)
+    got = O.paged_attention_ref(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                                case.block_size, case.scale, window)
+    np.testing.assert_allclose(got, brute_force_window(case, window), rtol=1e-12, atol=1e-13)
+
+
+def test_window_covering_the_context_changes_nothing():
+    case = W.make_case(72, [40, 9], q_len=2, num_q_heads=4, num_kv_heads=2, head_dim=8, block_size=3)
+    for window in (41, 1000):
+        np.testing.assert_array_equal(
+            O.paged_attention_ref(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                                  case.block_size, case.scale, window), run_oracle(case))
+
+
+def test_window_one_returns_the_rows_own_value():
+    # A one-position window leaves only token p: the output is v_p exactly.
+    case = W.make_case(73, [12], q_len=3, num_q_heads=4, num_kv_heads=2, head_dim=8, block_size=5)
+    got = O.paged_attention_ref(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                                case.block_size, case.scale, 1)
+    for i in range(3):
+        p = 12 - 3 + i
+        for h in range(4):
+            np.testing.assert_array_equal(got[0, i, h], O.bf16_bits_to_f64(case.logical_v[0][p, h // 2]))
+
+
+@pytest.mark.parametrize("window", [3, 8, 30])
+def test_window_split_mode_agrees_with_direct(window):
+    case = W.make_case(74, [60, 17], q_len=3, num_q_heads=4, num_kv_heads=2, head_dim=8, block_size=7)
+    ref = O.paged_attention_ref(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                                case.block_size, case.scale, window)
+    for chunk in (4, 7, 64):
+        S = 64
+        r = O.split_ranges_ref(case.seq_lens, S, chunk, window=window, rows=3)
+        ranges = [[tuple(x) for x in r[b] if x[1] > x[0]] for b in range(case.num_seqs)]
+        got = O.split_attention_ref(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                                    case.block_size, case.scale, ranges, window)
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_window_split_ranges_cover_exactly_the_union_of_the_windows():
+    r = O.split_ranges_ref([100, 5, 0], 8, 16, window=20, rows=4)
+    # The 4 rows of sequence 0 end at tokens 96 .. 99; the first row's window
+    # starts at 96 - 20 + 1 = 77, the start of the union of the windows.
+    first = 77
+    assert r[0, 0].tolist() == [first, first + 16]
+    assert r[0, 1].tolist() == [first + 16, 100]
+    assert all(r[0, s].tolist() == [100, 100] for s in range(2, 8))
+    assert r[1, 0].tolist() == [0, 5] and r[2, 0].tolist() == [0, 0]
+
+
+def test_planted_window_off_by_one_fails_the_pin(monkeypatch):
+    case = W.make_case(75, [30], q_len=2, num_q_heads=4, num_kv_heads=2, head_dim=8, block_size=4, poison=False)
+    ref = brute_force_window(case, 6)
+    monkeypatch.setattr(O, "first_visible", lambda pos, window: max(0, pos - window))
+    got = O.paged_attention_ref(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                                case.block_size, case.scale, 6)
+    assert not np.allclose(got, ref, rtol=1e-6, atol=1e-8)
