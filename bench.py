@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--block-size", type=int, default=784)
     ap.add_argument("--pools", type=int, default=16)
     ap.add_argument("--splits", type=int, default=0, help="force a split count (0 = planner)")
+    ap.add_argument("--kv-dtype", default="bf16", choices=["bf16", "fp8"],
+                    help="K/V cache type: bf16, or OCP FP8 E4M3 codes with per-tensor scales")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window: each query row sees its last W positions (0 = whole context)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
@@ -79,23 +81,24 @@ class Hip:
 
 def make_workload(args):
     from paged_kv_cache_08_amd import workloads as W
+    kv = dict(kv_dtype="fp8_e4m3") if args.kv_dtype == "fp8" else {}
     if args.workload == "hybrid":
-        case = W.hybrid_long_context(args.context, block_size=args.block_size, poison=False)
+        case = W.hybrid_long_context(args.context, block_size=args.block_size, poison=False, **kv)
         name = (f"hybrid decode: batch 1, q_len 1, 24 q / 4 KV heads, head_dim 256, page {args.block_size}, "
                 f"context {args.context}, 5% of keys x4")
     elif args.workload == "dense":
-        case = W.dense_control(args.context, poison=False)
+        case = W.dense_control(args.context, poison=False, **kv)
         name = f"dense control: batch 1, q_len 1, 32 q / 8 KV heads, head_dim 128, page 16, context {args.context}"
     elif args.workload == "mixed":
-        case = W.mixed_batch(poison=False)
+        case = W.mixed_batch(poison=False, **kv)
         name = "mixed batch: 16 sequences, q_len 1, 24 q / 4 KV heads, head_dim 256, page 784, log-uniform 500-32000"
     elif args.workload == "varlen":
-        case, qp, cu = W.batched_verify(poison=False)
+        case, qp, cu = W.batched_verify(poison=False, **kv)
         name = ("batched speculative verify (varlen): 32 requests, 1..5 rows each, 24 q / 4 KV heads, "
                 "head_dim 256, page 784, contexts log-uniform 512..2048")
         return case, name, (qp, cu)
     else:
-        case = W.spec_verify(args.context, poison=False)
+        case = W.spec_verify(args.context, poison=False, **kv)
         name = (f"speculative verify: batch 1, q_len 16 causal rows, 24 q / 4 KV heads, head_dim 256, "
                 f"page 784, context {args.context}")
     return case, name, None
@@ -120,9 +123,10 @@ def oracle_call(case, varlen, window):
     if varlen is not None:
         qp, cu = varlen
         return O.paged_attention_varlen_ref(qp, cu, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
-                                            case.block_size, case.scale, window)
+                                            case.block_size, case.scale, window, case.kv_dtype, case.k_scale,
+                                            case.v_scale)
     return O.paged_attention_ref(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
-                                 case.block_size, case.scale, window)
+                                 case.block_size, case.scale, window, case.kv_dtype, case.k_scale, case.v_scale)
 
 
 def cpu_baseline(case, varlen, window, kv_bytes_per_call, seconds):
@@ -180,18 +184,24 @@ def main():
         q = bf16(varlen[0])
         cu_t = torch.from_numpy(varlen[1]).to(dev)
         max_q = int(np.diff(varlen[1]).max())
-    k0, v0 = bf16(case.k_cache), bf16(case.v_cache)
+    if case.kv_dtype == "fp8_e4m3":
+        k0 = torch.from_numpy(np.ascontiguousarray(case.k_cache)).to(dev)
+        v0 = torch.from_numpy(np.ascontiguousarray(case.v_cache)).to(dev)
+        scales = dict(k_scale=case.k_scale, v_scale=case.v_scale)
+    else:
+        k0, v0 = bf16(case.k_cache), bf16(case.v_cache)
+        scales = {}
     table = torch.from_numpy(case.block_table).to(dev)
     lens = torch.from_numpy(case.seq_lens).to(dev)
     pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(max(args.pools, 1) - 1)]
     total_tokens = int(case.seq_lens.sum())
     rows = [case.q_len] * case.num_seqs if varlen is None else np.diff(varlen[1])
-    kv_bytes = W.kv_read_bytes(case.seq_lens, case.k_cache.shape[2], case.k_cache.shape[3], window=args.window,
-                               rows=rows)
+    kv_bytes = W.kv_read_bytes(case.seq_lens, case.k_cache.shape[2], case.k_cache.shape[3],
+                               elem_bytes=case.k_cache.dtype.itemsize, window=args.window, rows=rows)
     stream = torch.cuda.current_stream(dev).cuda_stream
     call = P.PreparedDecode(q, k0, v0, table, lens, case.block_size, case.scale, max_seq_len=case.max_seq_len,
                             total_tokens=total_tokens, num_splits=args.splits, stream=stream,
-                            cu_seqlens_q=cu_t, max_q_len=max_q, window=args.window)
+                            cu_seqlens_q=cu_t, max_q_len=max_q, window=args.window, **scales)
     out = call.out
 
     ptrs = [(k.data_ptr(), v.data_ptr()) for k, v in pools]
@@ -265,7 +275,7 @@ def main():
                                      max_seq_len=case.max_seq_len, total_tokens=total_tokens,
                                      num_splits=args.splits, out=out, workspace=call.workspace,
                                      stream=gstream.cuda_stream, cu_seqlens_q=cu_t, max_q_len=max_q,
-                                     window=args.window)
+                                     window=args.window, **scales)
         torch.cuda.synchronize()
         with torch.cuda.graph(graph, stream=gstream):
             for i in range(args.steps):
@@ -299,7 +309,8 @@ def main():
     kern_gbs = kv_bytes / (kern_avg_us * 1e-6) / 1e9
     from paged_kv_cache_08_amd.profiling import kernel_source_hash
     src_hash = kernel_source_hash()
-    wl_key = f"{args.workload}:{args.context}:{case.block_size}" + (f":w{args.window}" if args.window else "")
+    wl_key = (f"{args.workload}:{args.context}:{case.block_size}" + (f":w{args.window}" if args.window else "")
+              + (":fp8" if args.kv_dtype == "fp8" else ""))
     traffic = traffic_from_profiles(src_hash, wl_key)
 
     cpu = None
@@ -318,7 +329,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if case.kv_dtype == "bf16" else "fp8",
         "data": "synthetic",
         "config": {
             "workload": wl_name,
@@ -326,6 +337,7 @@ def main():
             "query_rows": int(case.num_seqs * case.q_len if varlen is None else varlen[1][-1]),
             "context": int(case.max_seq_len),
             "window": args.window,
+            "kv_dtype": case.kv_dtype,
             "block_size": int(case.block_size),
             "kv_pools_rotated": len(pools),
             "kv_bytes_per_step": kv_bytes,

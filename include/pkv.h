@@ -53,8 +53,12 @@ extern "C" {
 #define PKV_OUT_F32  0
 #define PKV_OUT_BF16 1
 
-/* Problem description. Layout is fixed: 10 x int32, 7 x int64, float, 3 x int32
- * (112 bytes, natural alignment). */
+/* Element type of the K/V caches (pkv_decode_params.kv_dtype). */
+#define PKV_KV_BF16 0
+#define PKV_KV_FP8_E4M3 1   /* OCP FP8 E4M3 (E4M3FN) codes; value = decoded code * k_scale / v_scale */
+
+/* Problem description. Layout is fixed: 10 x int32, 7 x int64, float, 3 x int32,
+ * 2 x float (120 bytes, natural alignment). */
 typedef struct pkv_decode_params {
   int32_t num_seqs;          /* sequences in the batch, >= 1 */
   int32_t q_len;             /* new query rows per sequence, 1..16 (1 = decode) */
@@ -79,7 +83,10 @@ typedef struct pkv_decode_params {
   int32_t window;            /* sliding window: the query row at position p sees only the
                                 tokens j with p - window < j <= p (the most recent `window`
                                 positions, its own included); 0 = the whole context */
-  int32_t reserved;          /* must be 0 */
+  int32_t kv_dtype;          /* PKV_KV_BF16 or PKV_KV_FP8_E4M3 (one byte per element; strides
+                                then multiples of 16 elements) */
+  float   k_scale;           /* FP8 caches: K = decoded code * k_scale (per tensor, finite, > 0) */
+  float   v_scale;           /* FP8 caches: V = decoded code * v_scale; both ignored for bf16 */
 } pkv_decode_params;
 
 /* Library version string (static storage). */
@@ -132,7 +139,7 @@ int pkv_device_cu_count(int32_t* cu_count);
 /*
  * The decode-attention call.
  *   q           device bf16 [num_seqs, q_len, Hq, D], contiguous.
- *   k_cache     device bf16, row (page, token, kv_head) at
+ *   k_cache     device bf16 (or FP8 E4M3 codes, kv_dtype), row (page, token, kv_head) at
  *               page * k_stride_page + token * k_stride_tok + kv_head * k_stride_head;
  *               both [P, B, Hkv, D] and views of [P, 2, B, Hkv, D] fit.
  *   v_cache     device bf16, same with the v_* strides.

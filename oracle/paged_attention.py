@@ -60,6 +60,28 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
+def fp8_e4m3_to_f64(codes) -> np.ndarray:
+    """Exact value of OCP FP8 E4M3 (E4M3FN) codes: a sign bit, 4 exponent bits
+    with bias 7 and 3 mantissa bits; exponent 0 holds the subnormals
+    m / 8 * 2^-6; S.1111.111 is NaN and there is no infinity (largest 448)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    e, m = (c >> 3) & 0xF, c & 7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    val = np.where(c & 0x80, -mag, mag)
+    return np.where((e == 15) & (m == 7), np.nan, val)
+
+
+def kv_widen(kv_dtype: str, scale: float = 1.0):
+    """Element decoder of a K or V cache: bf16 bits, or FP8 E4M3 codes times
+    the per-tensor scale (as the float32 the kernel receives)."""
+    if kv_dtype == "bf16":
+        return bf16_bits_to_f64
+    if kv_dtype == "fp8_e4m3":
+        s = float(np.float32(scale))
+        return lambda codes: fp8_e4m3_to_f64(codes) * s
+    raise ValueError(f"unknown kv_dtype {kv_dtype!r}")
+
+
 # ---------------------------------------------------------------------------
 # Address translation ("DCU page832 attention", §1 and §5).
 # ---------------------------------------------------------------------------
@@ -87,13 +109,27 @@ def token_offsets_ref(block_table, seq_lens, block_size: int, stride_page: int,
     return out
 
 
-def gather_token_rows(cache, table_row, n_tokens: int, block_size: int, kv_head: int) -> np.ndarray:
+def gather_token_rows(cache, table_row, n_tokens: int, block_size: int, kv_head: int,
+                      widen=bf16_bits_to_f64) -> np.ndarray:
     """Rows cache[block_table[j // B], j % B, kv_head, :] for j < n_tokens, as fp64."""
     j = np.arange(n_tokens, dtype=np.int64)
     logical_page = j // block_size
     page_offset = j % block_size
     physical_page = np.asarray(table_row, dtype=np.int64)[logical_page]
-    return bf16_bits_to_f64(np.asarray(cache)[physical_page, page_offset, kv_head, :])
+    return widen(np.asarray(cache)[physical_page, page_offset, kv_head, :])
+
+
+def _gather_kv(k_cache, v_cache, table_row, L: int, block_size: int, hkv: int, kv_dtype: str,
+               k_scale: float, v_scale: float):
+    """K and V rows of every KV head of one sequence, decoded to fp64."""
+    if kv_dtype == "bf16":   # the plain call (the planted-mistake pins replace gather_token_rows)
+        K = [gather_token_rows(k_cache, table_row, L, block_size, g) for g in range(hkv)]
+        V = [gather_token_rows(v_cache, table_row, L, block_size, g) for g in range(hkv)]
+    else:
+        wk, wv = kv_widen(kv_dtype, k_scale), kv_widen(kv_dtype, v_scale)
+        K = [gather_token_rows(k_cache, table_row, L, block_size, g, wk) for g in range(hkv)]
+        V = [gather_token_rows(v_cache, table_row, L, block_size, g, wv) for g in range(hkv)]
+    return K, V
 
 
 # ---------------------------------------------------------------------------
@@ -133,7 +169,8 @@ def _softmax_weighted_sum(scores: np.ndarray, values: np.ndarray) -> np.ndarray:
 
 
 def paged_attention_ref(q, k_cache, v_cache, block_table, seq_lens, block_size: int,
-                        scale: float, window: int = 0) -> np.ndarray:
+                        scale: float, window: int = 0, kv_dtype: str = "bf16", k_scale: float = 1.0,
+                        v_scale: float = 1.0) -> np.ndarray:
     """fp64 paged attention for all sequences, query rows and query heads.
 
     q: uint16 bf16 bits [num_seqs, q_len, Hq, D]; k_cache / v_cache: uint16
@@ -152,8 +189,7 @@ def paged_attention_ref(q, k_cache, v_cache, block_table, seq_lens, block_size: 
         if L == 0:
             continue
         assert L >= q_len, "a sequence must hold at least its q_len new tokens"
-        K = [gather_token_rows(k_cache, block_table[b], L, block_size, g) for g in range(hkv)]
-        V = [gather_token_rows(v_cache, block_table[b], L, block_size, g) for g in range(hkv)]
+        K, V = _gather_kv(k_cache, v_cache, block_table[b], L, block_size, hkv, kv_dtype, k_scale, v_scale)
         for i in range(q_len):
             pos = last_visible(L, q_len, i)
             lo = first_visible(pos, window)
@@ -166,7 +202,8 @@ def paged_attention_ref(q, k_cache, v_cache, block_table, seq_lens, block_size: 
 
 
 def paged_attention_varlen_ref(q_packed, cu_seqlens_q, k_cache, v_cache, block_table, seq_lens,
-                               block_size: int, scale: float, window: int = 0) -> np.ndarray:
+                               block_size: int, scale: float, window: int = 0, kv_dtype: str = "bf16",
+                               k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
     """Varlen multi-row attention: sequence b owns query rows
     q_packed[cu[b]:cu[b+1]] (n_b of them, [total_q, Hq, D] bf16 bits) and row i
     sees tokens j <= L_b - n_b + i, exactly as a call with q_len = n_b on that
@@ -180,7 +217,8 @@ def paged_attention_varlen_ref(q_packed, cu_seqlens_q, k_cache, v_cache, block_t
         if hi == lo:
             continue
         out[lo:hi] = paged_attention_ref(q_packed[None, lo:hi], k_cache, v_cache, block_table[b:b + 1],
-                                         np.asarray(seq_lens)[b:b + 1], block_size, scale, window)[0]
+                                         np.asarray(seq_lens)[b:b + 1], block_size, scale, window, kv_dtype,
+                                         k_scale, v_scale)[0]
     return out
 
 
@@ -214,7 +252,8 @@ def merge_partials_ref(parts) -> np.ndarray:
 
 
 def split_attention_ref(q, k_cache, v_cache, block_table, seq_lens, block_size: int,
-                        scale: float, ranges, window: int = 0) -> np.ndarray:
+                        scale: float, ranges, window: int = 0, kv_dtype: str = "bf16", k_scale: float = 1.0,
+                        v_scale: float = 1.0) -> np.ndarray:
     """Same result as paged_attention_ref, evaluated split by split and merged.
 
     ranges[b] is a list of [begin, end) token ranges that partition [0, L_b).
@@ -229,8 +268,7 @@ def split_attention_ref(q, k_cache, v_cache, block_table, seq_lens, block_size: 
         L = int(seq_lens[b])
         if L == 0:
             continue
-        K = [gather_token_rows(k_cache, block_table[b], L, block_size, g) for g in range(hkv)]
-        V = [gather_token_rows(v_cache, block_table[b], L, block_size, g) for g in range(hkv)]
+        K, V = _gather_kv(k_cache, v_cache, block_table[b], L, block_size, hkv, kv_dtype, k_scale, v_scale)
         for i in range(q_len):
             pos = last_visible(L, q_len, i)
             first = first_visible(pos, window)

@@ -20,6 +20,8 @@ PKV_ERR_WORKSPACE = -3
 PKV_ERR_HIP = -4
 PKV_OUT_F32 = 0
 PKV_OUT_BF16 = 1
+PKV_KV_BF16 = 0
+PKV_KV_FP8_E4M3 = 1
 
 
 class DecodeParams(ctypes.Structure):
@@ -45,11 +47,13 @@ class DecodeParams(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("out_dtype", ctypes.c_int32),
         ("window", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
-assert ctypes.sizeof(DecodeParams) == 112
+assert ctypes.sizeof(DecodeParams) == 120
 
 _lock = threading.Lock()
 _lib = None
@@ -167,11 +171,13 @@ def _torch():
 
 def make_params(q, k_cache, v_cache, block_table, block_size: int, scale: float, *, max_seq_len: int,
                 num_splits: int = 0, total_tokens: int = 0, out_dtype: int = PKV_OUT_F32,
-                window: int = 0) -> DecodeParams:
+                window: int = 0, k_scale: float = 1.0, v_scale: float = 1.0) -> DecodeParams:
     """Fill DecodeParams from tensor shapes and strides.
 
     q: [num_seqs, q_len, Hq, D]; k_cache / v_cache: [num_pages, B, Hkv, D] with
-    unit stride on D; block_table: [num_seqs, max_pages]."""
+    unit stride on D, bf16, or one byte per element (FP8 E4M3 codes, as uint8 or
+    float8_e4m3fn) with per-tensor k_scale / v_scale; block_table:
+    [num_seqs, max_pages]."""
     ns, ql, hq, d = q.shape
     P, B, hkv, d2 = k_cache.shape
     assert d2 == d and tuple(v_cache.shape) == tuple(k_cache.shape) and B == block_size
@@ -189,12 +195,17 @@ def make_params(q, k_cache, v_cache, block_table, block_size: int, scale: float,
     p.scale = float(scale)
     p.out_dtype = out_dtype
     p.window = int(window)
+    fp8 = k_cache.element_size() == 1
+    assert v_cache.element_size() == k_cache.element_size()
+    p.kv_dtype = PKV_KV_FP8_E4M3 if fp8 else PKV_KV_BF16
+    p.k_scale, p.v_scale = (float(k_scale), float(v_scale)) if fp8 else (1.0, 1.0)
     return p
 
 
 def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, block_size: int, scale: float, *,
                            max_seq_len: int | None = None, total_tokens: int = 0, num_splits: int = 0,
-                           out=None, out_dtype=None, workspace=None, stream=None, window: int = 0):
+                           out=None, out_dtype=None, workspace=None, stream=None, window: int = 0,
+                           k_scale: float = 1.0, v_scale: float = 1.0):
     """out[b,i,h,:] = softmax(scale * q[b,i,h,:] . K_j) V_j over the visible tokens of sequence b
     (with window > 0, only the last `window` of them for each row).
 
@@ -206,7 +217,7 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, block_siz
     """
     torch = _torch()
     assert q.is_cuda and q.dtype == torch.bfloat16 and q.is_contiguous()
-    assert k_cache.dtype == torch.bfloat16 and v_cache.dtype == torch.bfloat16
+    assert k_cache.dtype in _KV_DTYPES() and v_cache.dtype == k_cache.dtype
     assert block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
     assert block_table.is_contiguous() and seq_lens.is_contiguous()
     if max_seq_len is None:
@@ -216,7 +227,8 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, block_siz
     odt = PKV_OUT_BF16 if out.dtype == torch.bfloat16 else PKV_OUT_F32
     assert out.dtype in (torch.float32, torch.bfloat16) and out.is_contiguous() and out.shape == q.shape
     p = make_params(q, k_cache, v_cache, block_table, block_size, scale, max_seq_len=max_seq_len,
-                    num_splits=num_splits, total_tokens=total_tokens, out_dtype=odt, window=window)
+                    num_splits=num_splits, total_tokens=total_tokens, out_dtype=odt, window=window,
+                    k_scale=k_scale, v_scale=v_scale)
     need = workspace_bytes(p, 0)
     if workspace is None:
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
@@ -230,10 +242,15 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, block_siz
     return out
 
 
+def _KV_DTYPES():
+    torch = _torch()
+    return (torch.bfloat16, torch.uint8, torch.float8_e4m3fn)
+
+
 def paged_varlen_attention(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, block_size: int,
                            scale: float, *, max_q_len: int, max_seq_len: int, total_tokens: int = 0,
                            num_splits: int = 0, out=None, out_dtype=None, workspace=None, stream=None,
-                           window: int = 0):
+                           window: int = 0, k_scale: float = 1.0, v_scale: float = 1.0):
     """Varlen multi-row call: sequence b's query rows are q[cu_seqlens_q[b]:cu_seqlens_q[b+1]].
 
     q: bf16 [total_q, Hq, D] packed rows (contiguous, on the GPU); cu_seqlens_q:
@@ -253,7 +270,8 @@ def paged_varlen_attention(q, k_cache, v_cache, block_table, seq_lens, cu_seqlen
     assert out.dtype in (torch.float32, torch.bfloat16) and out.is_contiguous() and out.shape == q.shape
     shape4 = torch.empty((ns, int(max_q_len), q.shape[1], q.shape[2]), device="meta")
     p = make_params(shape4, k_cache, v_cache, block_table, block_size, scale, max_seq_len=max_seq_len,
-                    num_splits=num_splits, total_tokens=total_tokens, out_dtype=odt, window=window)
+                    num_splits=num_splits, total_tokens=total_tokens, out_dtype=odt, window=window,
+                    k_scale=k_scale, v_scale=v_scale)
     need = workspace_bytes(p, 0)
     if workspace is None:
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
@@ -307,7 +325,8 @@ class PreparedDecode:
 
     def __init__(self, q, k_cache, v_cache, block_table, seq_lens, block_size: int, scale: float, *,
                  max_seq_len: int, total_tokens: int = 0, num_splits: int = 0, out=None, workspace=None,
-                 stream=None, cu_seqlens_q=None, max_q_len: int | None = None, window: int = 0):
+                 stream=None, cu_seqlens_q=None, max_q_len: int | None = None, window: int = 0,
+                 k_scale: float = 1.0, v_scale: float = 1.0):
         torch = _torch()
         assert q.is_cuda and q.dtype == torch.bfloat16 and q.is_contiguous()
         assert block_table.is_contiguous() and seq_lens.is_contiguous()
@@ -322,7 +341,8 @@ class PreparedDecode:
         else:
             shape = q
         self.params = make_params(shape, k_cache, v_cache, block_table, block_size, scale, max_seq_len=max_seq_len,
-                                  num_splits=num_splits, total_tokens=total_tokens, out_dtype=odt, window=window)
+                                  num_splits=num_splits, total_tokens=total_tokens, out_dtype=odt, window=window,
+                                  k_scale=k_scale, v_scale=v_scale)
         if not self.varlen:
             check(validate(self.params), "pkv_validate_params")
         need = workspace_bytes(self.params, 0)

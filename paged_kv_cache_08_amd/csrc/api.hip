@@ -41,7 +41,7 @@ int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
 bool mult8_pos(int64_t s) { return s > 0 && (s % 8) == 0; }
 
-static_assert(sizeof(pkv_decode_params) == 112, "pkv_decode_params layout");
+static_assert(sizeof(pkv_decode_params) == 120, "pkv_decode_params layout");
 
 // Longest token range one sequence's splits must cover: the whole context,
 // or with a sliding window the union of its rows' windows (window + q_len - 1).
@@ -116,7 +116,12 @@ pkv::DecodeArgs make_args(const pkv_decode_params* p, int32_t S, int32_t chunk) 
   a.chunk = chunk;
   a.num_splits = S;
   a.bdiv = pkv::make_magic(uint32_t(p->block_size));
-  a.scale_log2 = float(double(p->scale) * 1.4426950408889634);
+  const bool fp8 = p->kv_dtype == PKV_KV_FP8_E4M3;
+  // FP8 caches: K's per-tensor scale folds into the score scale, V's into the
+  // stored output (partials stay unscaled).
+  a.scale_log2 = float(double(p->scale) * (fp8 ? double(p->k_scale) : 1.0) * 1.4426950408889634);
+  a.out_scale = fp8 ? p->v_scale : 1.0f;
+  a.kv_fp8 = fp8;
   a.out_bf16 = p->out_dtype == PKV_OUT_BF16;
   a.window = p->window;
   return a;
@@ -153,7 +158,10 @@ int validate_common(const pkv_decode_params* p) {
       p->block_size < 1 || p->max_pages_per_seq < 1 || p->num_pages < 1 || p->max_seq_len < 0 ||
       p->num_splits < 0 || p->total_tokens < 0 || p->window < 0)
     return fail(PKV_ERR_INVALID, "a size is out of range");
-  if (p->reserved != 0) return fail(PKV_ERR_INVALID, "reserved must be 0");
+  if (p->kv_dtype != PKV_KV_BF16 && p->kv_dtype != PKV_KV_FP8_E4M3) return fail(PKV_ERR_INVALID, "unknown kv_dtype");
+  if (p->kv_dtype == PKV_KV_FP8_E4M3 &&
+      !(isfinite(p->k_scale) && p->k_scale > 0.0f && isfinite(p->v_scale) && p->v_scale > 0.0f))
+    return fail(PKV_ERR_INVALID, "FP8 caches need finite, positive k_scale and v_scale");
   if (p->num_q_heads % p->num_kv_heads != 0)
     return fail(PKV_ERR_INVALID, "num_q_heads is not a multiple of num_kv_heads");
   if (p->head_dim != 128 && p->head_dim != 256) return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 128 or 256");
@@ -164,6 +172,10 @@ int validate_common(const pkv_decode_params* p) {
   if (!mult8_pos(p->k_stride_page) || !mult8_pos(p->k_stride_tok) || !mult8_pos(p->k_stride_head) ||
       !mult8_pos(p->v_stride_page) || !mult8_pos(p->v_stride_tok) || !mult8_pos(p->v_stride_head))
     return fail(PKV_ERR_INVALID, "K/V strides must be positive multiples of 8 elements");
+  if (p->kv_dtype == PKV_KV_FP8_E4M3 &&
+      ((p->k_stride_page | p->k_stride_tok | p->k_stride_head | p->v_stride_page | p->v_stride_tok |
+        p->v_stride_head) & 15) != 0)
+    return fail(PKV_ERR_INVALID, "FP8 K/V strides must be multiples of 16 elements (16-byte rows)");
   if (p->block_size > (1 << 20)) return fail(PKV_ERR_UNSUPPORTED, "block_size above 2^20 tokens");
   if (int64_t(p->block_size) * p->k_stride_tok >= (int64_t(1) << 31) ||
       int64_t(p->block_size) * p->v_stride_tok >= (int64_t(1) << 31))

@@ -228,11 +228,12 @@ int decode_window(int chunk) {
 
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int group, hipStream_t st, hipEvent_t e0,
                                hipEvent_t e1) {
+  const bool fp8 = a.kv_fp8 != 0;
   switch (decode_window(a.chunk)) {
-    case 64: return launch_decode_split_w64(a, head_dim, group, st, e0, e1);
-    case 128: return launch_decode_split_w128(a, head_dim, group, st, e0, e1);
-    case 256: return launch_decode_split_w256(a, head_dim, group, st, e0, e1);
-    default: return launch_decode_split_w512(a, head_dim, group, st, e0, e1);
+    case 64: return (fp8 ? launch_decode_split_w64_fp8 : launch_decode_split_w64)(a, head_dim, group, st, e0, e1);
+    case 128: return (fp8 ? launch_decode_split_w128_fp8 : launch_decode_split_w128)(a, head_dim, group, st, e0, e1);
+    case 256: return (fp8 ? launch_decode_split_w256_fp8 : launch_decode_split_w256)(a, head_dim, group, st, e0, e1);
+    default: return (fp8 ? launch_decode_split_w512_fp8 : launch_decode_split_w512)(a, head_dim, group, st, e0, e1);
   }
 }
 

@@ -1,8 +1,9 @@
 // The single-query split kernel for gfx950 (wave64, CDNA4), templated on
 // head_dim D, group size G (query heads per KV head) and window NS (sub-steps
-// of 32 tokens; a split holds at most NS * 32 tokens). Each window size is
-// instantiated in its own source file (decode_w64.hip .. decode_w512.hip) so
-// the fully unrolled kernels compile in parallel.
+// of 32 tokens; a split holds at most NS * 32 tokens) and the cache type
+// (bf16 or FP8 E4M3). Each window size and cache type is instantiated in its
+// own source file (decode_w64.hip .. decode_w512_fp8.hip) so the fully
+// unrolled kernels compile in parallel.
 //
 // What is computed follows "DCU page832 attention" (luanjiahao.me): §1 and §5
 // for the address of a token row (logical page = t / B, offset = t % B,
@@ -147,10 +148,20 @@ __device__ __forceinline__ float reduce_scatter16(const float (&x)[G], int col) 
   return w + dpp_move<0xB1>(w);            // quad_perm [1,0,3,2]
 }
 
-template <int D, int G, int kSubSteps>
+// Head-dim element of lane column col's e-th element. bf16 caches: two
+// 16-byte pieces per 512-byte row, lane col holds [k * 128 + col * 8, +8) of
+// piece k. FP8 caches: lane col holds the kEpl contiguous elements
+// [col * kEpl, +kEpl) (one 16-byte load at D = 256).
+template <bool FP8, int kEpl>
+__device__ __forceinline__ int elem_d(int col, int e) {
+  return FP8 ? col * kEpl + e : (e / 8) * 128 + col * 8 + (e % 8);
+}
+
+template <int D, int G, int kSubSteps, bool FP8>
 __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a) {
   constexpr int kEpl = D / kLanesPerRow;   // head-dim elements per lane: 16 or 8
-  constexpr int kCpl = kEpl / 8;           // 16-byte chunks per lane: 2 or 1
+  constexpr int kCq = kEpl / 8;            // 16-byte pieces of q per lane: 2 or 1
+  constexpr int kCpl = FP8 ? 1 : kCq;      // 16-byte K/V loads per lane and row (FP8 at D = 128: 8 bytes)
   constexpr int kSteps = 2 * kSubSteps;    // K pass, then V pass
   constexpr int kRing = ring_depth(D, G);
   static_assert(kCpl >= 1 && kEpl % 8 == 0, "head_dim must be a multiple of 128");
@@ -172,16 +183,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   // sequence length: fetch them while seq_lens is still in flight.
   SplitPages pages = split_pages(a, s);
   if (a.window == 0) stage_table(a, b, g, pages.p_first, pages.n, tbl);
-  // q of the group's G heads: lane col holds elements [k*128 + col*8, +8) of each head.
-  uint4 qv[G][kCpl];
-  {
-    const uint16_t* qp = a.q + out_row0 + col * 8;
+  // q of the group's G heads, in the lane's element order (elem_d).
+  uint4 qv[G][kCq];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int k = 0; k < kCpl; ++k)
-        qv[h][k] = *reinterpret_cast<const uint4*>(qp + h * D + k * 128);
-  }
+    for (int k = 0; k < kCq; ++k)
+      qv[h][k] = *reinterpret_cast<const uint4*>(a.q + out_row0 + h * D + elem_d<FP8, kEpl>(col, 8 * k));
 
   const SplitSpan sp = split_span(a, b, s, 1);
   if (sp.begin >= sp.L) {
@@ -211,8 +219,23 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   uint32_t tix[kSubSteps];    // (table slot << 20) | in-page offset of that token; ~0u if masked
   float m_row = kMinit, l_row = 0.0f;
 
-  const uint16_t* const safe_row = a.q + out_row0 + col * 8;   // finite, in bounds
+  const uint16_t* const safe_row = a.q + out_row0 + col * 8;   // finite bf16, in bounds
   uint4 ring[kRing][kCpl];
+  // One lane's piece of a K or V row: bf16 kCpl 16-byte loads; FP8 kEpl bytes.
+  auto load_row = [&](const void* bf16_row, const uint8_t* fp8_row, uint4 (&buf)[kCpl]) {
+    if constexpr (FP8) {
+      if constexpr (kEpl == 16) {
+        buf[0] = *reinterpret_cast<const uint4*>(fp8_row);
+      } else {
+        const uint2 h = *reinterpret_cast<const uint2*>(fp8_row);
+        buf[0] = make_uint4(h.x, h.y, 0u, 0u);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kCpl; ++k)
+        buf[k] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(bf16_row) + k * 128);
+    }
+  };
 
   // K step j: locate the token, remember where it is (tix: bit 31 = masked,
   // bits 20..30 = table slot, bits 0..19 = in-page offset), load its K chunk.
@@ -227,35 +250,64 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
     const int64_t pk = tbl[slot].k;
     const bool ok = (t < sp.end) && pk >= 0;
     tix[j] = (ok ? 0u : 0x80000000u) | (uint32_t(slot) << 20) | uint32_t(off);
-    const uint16_t* real = a.k + (pk + int64_t(off * int32_t(a.k_st))) + col * 8;
-    const uint16_t* kp = ok ? real : safe_row;
-#pragma unroll
-    for (int k = 0; k < kCpl; ++k) buf[k] = *reinterpret_cast<const uint4*>(kp + k * 128);
+    const int64_t eo = pk + int64_t(off * int32_t(a.k_st)) + elem_d<FP8, kEpl>(col, 0);
+    if constexpr (FP8) {
+      const uint8_t* real = reinterpret_cast<const uint8_t*>(a.k) + eo;
+      load_row(nullptr, ok ? real : reinterpret_cast<const uint8_t*>(safe_row), buf);
+    } else {
+      load_row(ok ? a.k + eo : safe_row, nullptr, buf);
+    }
   };
   // V step j: the same token's V chunk (the slot of a masked row is still a
   // staged entry, so the LDS read is in range).
   auto fetch_v = [&](int j, uint4 (&buf)[kCpl]) {
     const uint32_t ti = tix[j];
     const int slot = int((ti >> 20) & 0x7ffu), off = int(ti & 0xfffffu);
-    const uint16_t* real = a.v + (tbl[slot].v + int64_t(off * int32_t(a.v_st))) + col * 8;
-    const uint16_t* vp = (ti & 0x80000000u) ? safe_row : real;
-#pragma unroll
-    for (int k = 0; k < kCpl; ++k) buf[k] = *reinterpret_cast<const uint4*>(vp + k * 128);
+    const bool ok = !(ti & 0x80000000u);
+    const int64_t eo = tbl[slot].v + int64_t(off * int32_t(a.v_st)) + elem_d<FP8, kEpl>(col, 0);
+    if constexpr (FP8) {
+      const uint8_t* real = reinterpret_cast<const uint8_t*>(a.v) + eo;
+      load_row(nullptr, ok ? real : reinterpret_cast<const uint8_t*>(safe_row), buf);
+    } else {
+      load_row(ok ? a.v + eo : safe_row, nullptr, buf);
+    }
   };
   // q.k of the G heads; lanes 2h, 2h+1 keep head h's score.
   auto consume_k = [&](int j, const uint4 (&kk)[kCpl]) {
     float dq[G];
+    if constexpr (FP8) {
+      // Each 32-bit word holds 4 FP8 codes: two exact bf16 pairs, elements
+      // 4w .. 4w + 3 of the lane, i.e. q words 2w and 2w + 1.
+      constexpr int kWords = kEpl / 4;
+      const uint32_t w4[4] = {kk[0].x, kk[0].y, kk[0].z, kk[0].w};
+      uint32_t kb[2 * kWords];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float d0 = 0.0f;
-#pragma unroll
-      for (int k = 0; k < kCpl; ++k) {
-        d0 = dot2_bf16(qv[h][k].x, kk[k].x, d0);
-        d0 = dot2_bf16(qv[h][k].y, kk[k].y, d0);
-        d0 = dot2_bf16(qv[h][k].z, kk[k].z, d0);
-        d0 = dot2_bf16(qv[h][k].w, kk[k].w, d0);
+      for (int w = 0; w < kWords; ++w) {
+        kb[2 * w] = fp8x2_to_bf16x2<false>(w4[w]);
+        kb[2 * w + 1] = fp8x2_to_bf16x2<true>(w4[w]);
       }
-      dq[h] = d0;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const uint32_t qw[8] = {qv[h][0].x, qv[h][0].y, qv[h][0].z, qv[h][0].w,
+                                qv[h][kCq - 1].x, qv[h][kCq - 1].y, qv[h][kCq - 1].z, qv[h][kCq - 1].w};
+        float d0 = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 2 * kWords; ++m) d0 = dot2_bf16(qw[m], kb[m], d0);
+        dq[h] = d0;
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float d0 = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kCpl; ++k) {
+          d0 = dot2_bf16(qv[h][k].x, kk[k].x, d0);
+          d0 = dot2_bf16(qv[h][k].y, kk[k].y, d0);
+          d0 = dot2_bf16(qv[h][k].z, kk[k].z, d0);
+          d0 = dot2_bf16(qv[h][k].w, kk[k].w, d0);
+        }
+        dq[h] = d0;
+      }
     }
     const float r = reduce_scatter16<G>(dq, col) * a.scale_log2;
     sc[j] = (tix[j] & 0x80000000u) ? -INFINITY : r;
@@ -266,17 +318,35 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
     l_row += pl;
     float p[G];
     head_bcast<G>(pl, p);
+    if constexpr (FP8) {
+      // A masked row read the q row's bytes, which may decode to NaN, and
+      // 0 * NaN is NaN: its codes are replaced by zeros.
+      const bool ok = !(tix[j] & 0x80000000u);
+      constexpr int kWords = kEpl / 4;
+      const uint32_t w4[4] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w};
 #pragma unroll
-    for (int k = 0; k < kCpl; ++k) {
-      const uint32_t w4[4] = {vv[k].x, vv[k].y, vv[k].z, vv[k].w};
+      for (int w = 0; w < kWords; ++w) {
+        const uint32_t word = ok ? w4[w] : 0u;
+        const float2 lo = fp8x2_to_f32x2<false>(word), hi = fp8x2_to_f32x2<true>(word);
+        const float v4[4] = {lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float v0 = bf16_lo(w4[w]), v1 = bf16_hi(w4[w]);
-        const int e = k * 8 + w * 2;
+        for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          acc[h][e] = fmaf(p[h], v0, acc[h][e]);
-          acc[h][e + 1] = fmaf(p[h], v1, acc[h][e + 1]);
+          for (int h = 0; h < G; ++h) acc[h][4 * w + c] = fmaf(p[h], v4[c], acc[h][4 * w + c]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kCpl; ++k) {
+        const uint32_t w4[4] = {vv[k].x, vv[k].y, vv[k].z, vv[k].w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float v0 = bf16_lo(w4[w]), v1 = bf16_hi(w4[w]);
+          const int e = k * 8 + w * 2;
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            acc[h][e] = fmaf(p[h], v0, acc[h][e]);
+            acc[h][e + 1] = fmaf(p[h], v1, acc[h][e + 1]);
+          }
         }
       }
     }
@@ -355,8 +425,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
     for (int e = 0; e < kE4; ++e) part[h][e] *= f;
   }
   {
-    const int e0 = row * kE4;                             // within one 8-element chunk
-    const int d0 = (e0 / 8) * 128 + col * 8 + (e0 % 8);
+    const int d0 = elem_d<FP8, kEpl>(col, row * kE4);     // kE4 contiguous elements
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float* dst = &mrg_acc[wave][h][d0];
@@ -399,38 +468,39 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   }
 }
 
-template <int D, int G, int NS>
-hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+template <int D, int G, int NS, bool FP8>
+hipError_t launch_decode_k(const DecodeArgs& a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   dim3 grid(a.num_splits, a.hkv, a.num_seqs);
   if (e0 && e1)
-    hipExtLaunchKernelGGL((decode_split_kernel<D, G, NS>), grid, dim3(kThreads), 0, st, e0, e1, 0, a);
+    hipExtLaunchKernelGGL((decode_split_kernel<D, G, NS, FP8>), grid, dim3(kThreads), 0, st, e0, e1, 0, a);
   else
-    hipLaunchKernelGGL((decode_split_kernel<D, G, NS>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, G, NS, FP8>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
-template <int D, int NS>
+template <int D, int NS, bool FP8>
 hipError_t launch_decode_d(const DecodeArgs& a, int group, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   switch (group) {
-    case 1: return launch_decode_t<D, 1, NS>(a, st, e0, e1);
-    case 2: return launch_decode_t<D, 2, NS>(a, st, e0, e1);
-    case 3: return launch_decode_t<D, 3, NS>(a, st, e0, e1);
-    case 4: return launch_decode_t<D, 4, NS>(a, st, e0, e1);
-    case 5: return launch_decode_t<D, 5, NS>(a, st, e0, e1);
-    case 6: return launch_decode_t<D, 6, NS>(a, st, e0, e1);
-    case 7: return launch_decode_t<D, 7, NS>(a, st, e0, e1);
-    case 8: return launch_decode_t<D, 8, NS>(a, st, e0, e1);
+    case 1: return launch_decode_k<D, 1, NS, FP8>(a, st, e0, e1);
+    case 2: return launch_decode_k<D, 2, NS, FP8>(a, st, e0, e1);
+    case 3: return launch_decode_k<D, 3, NS, FP8>(a, st, e0, e1);
+    case 4: return launch_decode_k<D, 4, NS, FP8>(a, st, e0, e1);
+    case 5: return launch_decode_k<D, 5, NS, FP8>(a, st, e0, e1);
+    case 6: return launch_decode_k<D, 6, NS, FP8>(a, st, e0, e1);
+    case 7: return launch_decode_k<D, 7, NS, FP8>(a, st, e0, e1);
+    case 8: return launch_decode_k<D, 8, NS, FP8>(a, st, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }
 
-// Launch the split kernel with a window of NS sub-steps (a.chunk <= NS * 32).
-template <int NS>
+// Launch the split kernel with a window of NS sub-steps (a.chunk <= NS * 32)
+// for bf16 (FP8 = false) or FP8 caches.
+template <int NS, bool FP8>
 hipError_t launch_decode_window(const DecodeArgs& a, int head_dim, int group, hipStream_t st, hipEvent_t e0,
                                 hipEvent_t e1) {
-  if (a.chunk > NS * kStep) return hipErrorInvalidValue;
-  if (head_dim == 256) return launch_decode_d<256, NS>(a, group, st, e0, e1);
-  if (head_dim == 128) return launch_decode_d<128, NS>(a, group, st, e0, e1);
+  if (a.chunk > NS * kStep || bool(a.kv_fp8) != FP8) return hipErrorInvalidValue;
+  if (head_dim == 256) return launch_decode_d<256, NS, FP8>(a, group, st, e0, e1);
+  if (head_dim == 128) return launch_decode_d<128, NS, FP8>(a, group, st, e0, e1);
   return hipErrorInvalidValue;
 }
 

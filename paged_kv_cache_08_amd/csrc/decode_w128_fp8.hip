@@ -1,0 +1,11 @@
+// Split kernels with a 128-token window (4 sub-steps of 32 tokens), FP8 E4M3 caches.
+#include "decode_split.h"
+
+namespace pkv {
+
+hipError_t launch_decode_split_w128_fp8(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
+                                        hipEvent_t e0, hipEvent_t e1) {
+  return launch_decode_window<4, true>(a, head_dim, group, st, e0, e1);
+}
+
+}  // namespace pkv

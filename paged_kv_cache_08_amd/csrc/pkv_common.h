@@ -50,8 +50,8 @@ __host__ __device__ inline uint32_t magic_div(uint32_t n, const MagicDiv& md) {
 // Everything a split / merge kernel needs, passed by value.
 struct DecodeArgs {
   const uint16_t* q;        // bf16 [num_seqs, q_len, hq, D]
-  const uint16_t* k;        // bf16 paged K
-  const uint16_t* v;        // bf16 paged V
+  const uint16_t* k;        // paged K: bf16, or FP8 codes addressed bytewise (kv_fp8)
+  const uint16_t* v;        // paged V, the same
   const int32_t* table;     // [num_seqs, max_pages]
   const int32_t* seq_lens;  // [num_seqs]
   void* out;                // [num_seqs, q_len, hq, D] f32 or bf16
@@ -71,6 +71,8 @@ struct DecodeArgs {
   // nullptr for uniform calls (sequence b owns rows b * q_len .. + q_len).
   const int32_t* cu_q;
   int32_t window;           // sliding window in positions (0 = whole context)
+  int32_t kv_fp8;           // K/V caches hold FP8 E4M3 codes (else bf16)
+  float out_scale;          // applied to every stored output (the FP8 V scale, else 1)
 };
 
 // Launchers (decode_kernels.hip, decode_w*.hip, verify_kernels.hip). Return
@@ -83,12 +85,20 @@ hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int group, hip
                                hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_decode_split_w64(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
                                    hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_decode_split_w64_fp8(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
+                                       hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_decode_split_w128(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
                                     hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_decode_split_w128_fp8(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
+                                        hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_decode_split_w256(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
                                     hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_decode_split_w256_fp8(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
+                                        hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_decode_split_w512(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
                                     hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_decode_split_w512_fp8(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
+                                        hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_verify_split(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
                                hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_lse_merge(const DecodeArgs& a, int head_dim, hipStream_t st);

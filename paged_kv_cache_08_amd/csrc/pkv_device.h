@@ -29,6 +29,18 @@ __device__ __forceinline__ float dpp_move(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Two OCP FP8 E4M3 codes of a 32-bit word (bytes 0, 1, or 2, 3 when hi) as an
+// exact bf16 pair, or as two floats (low byte first); one instruction each.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+template <bool HI>
+__device__ __forceinline__ float2 fp8x2_to_f32x2(uint32_t w) {
+  const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, HI);
+  return make_float2(f[0], f[1]);
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40);   // quiet NaN
@@ -37,6 +49,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 __device__ __forceinline__ void store_out(const DecodeArgs& a, int64_t idx, float x) {
+  x *= a.out_scale;
   if (a.out_bf16)
     static_cast<uint16_t*>(a.out)[idx] = f32_to_bf16_rne(x);
   else

@@ -12,7 +12,8 @@
 //
 // Workgroup = one split (<= 512 tokens) of one (sequence, KV head), 8 waves.
 //   * All 8 waves stage 64-token K and V tiles into LDS (double buffered, rows
-//     padded to 528 bytes) with 16-byte loads through the block table.
+//     padded to 528 bytes) with 16-byte loads through the block table; FP8
+//     caches are decoded to bf16 (exactly) on the way into LDS.
 //   * Wave w owns query rows f = 16w .. 16w + 15 of the flattened
 //     (head, position) list, head-major (f = h_local * q_len + i); waves past
 //     the last row only stage tiles.
@@ -64,10 +65,11 @@ __device__ __forceinline__ uint32_t bf16_pair(float x, float y) {
 // rescale of O.
 constexpr float kLazyMax = 8.0f;
 
-template <int D>
+template <int D, bool FP8>
 __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a) {
   constexpr int kPitch = D * 2 + 16;              // LDS bytes per token row (padded)
-  constexpr int kChunks = D * 2 / 16;             // 16-byte chunks per row
+  constexpr int kElems = FP8 ? 16 : 8;            // elements per 16-byte chunk of a cache row
+  constexpr int kChunks = D / kElems;             // 16-byte chunks per row
   constexpr int kLoads = kVTile * kChunks / kVThreads;   // K (and V) chunks per thread per tile
   constexpr int kKSteps = D / 32;                 // 32-wide k steps of q.k
   constexpr int kDBlocks = D / 16;                // 16-column blocks of O
@@ -135,6 +137,7 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
 
   // Tile staging: thread tid moves chunks c = tid + kVThreads * k of K and V.
   u32x4_t stk[kLoads], stv[kLoads];   // native vectors: kept in registers
+  bool okt[kLoads];                   // FP8: the chunk belongs to a live token
   auto load_tile = [&](int tile) __attribute__((always_inline)) {
     static_for<0, kLoads>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
@@ -144,19 +147,48 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
       const int tc = min(t, sp.end - 1);
       int64_t ko, vo;
       const bool ok = token_row(a, tbl, p_first, tc, ko, vo) && t < sp.end;
-      const uint16_t* kp = ok ? a.k + ko + piece * 8 : a.q;   // masked rows read q (finite)
-      const uint16_t* vp = ok ? a.v + vo + piece * 8 : a.q;
-      stk[k] = *reinterpret_cast<const u32x4_t*>(kp);
-      stv[k] = *reinterpret_cast<const u32x4_t*>(vp);
+      okt[k] = ok;
+      if constexpr (FP8) {   // element offsets are byte offsets
+        const uint8_t* kp = ok ? reinterpret_cast<const uint8_t*>(a.k) + ko + piece * 16
+                               : reinterpret_cast<const uint8_t*>(a.q);
+        const uint8_t* vp = ok ? reinterpret_cast<const uint8_t*>(a.v) + vo + piece * 16
+                               : reinterpret_cast<const uint8_t*>(a.q);
+        stk[k] = *reinterpret_cast<const u32x4_t*>(kp);
+        stv[k] = *reinterpret_cast<const u32x4_t*>(vp);
+      } else {
+        const uint16_t* kp = ok ? a.k + ko + piece * 8 : a.q;   // masked rows read q (finite)
+        const uint16_t* vp = ok ? a.v + vo + piece * 8 : a.q;
+        stk[k] = *reinterpret_cast<const u32x4_t*>(kp);
+        stv[k] = *reinterpret_cast<const u32x4_t*>(vp);
+      }
     });
+  };
+  // FP8: 16 codes -> 16 exact bf16 values (32 bytes); a masked chunk read the
+  // q row, whose bytes may decode to NaN, so it becomes zeros.
+  auto fp8_to_bf16 = [&](const u32x4_t& w, bool ok, u32x4_t& lo, u32x4_t& hi) __attribute__((always_inline)) {
+    const uint32_t x[4] = {ok ? w[0] : 0u, ok ? w[1] : 0u, ok ? w[2] : 0u, ok ? w[3] : 0u};
+    lo = u32x4_t{fp8x2_to_bf16x2<false>(x[0]), fp8x2_to_bf16x2<true>(x[0]),
+                 fp8x2_to_bf16x2<false>(x[1]), fp8x2_to_bf16x2<true>(x[1])};
+    hi = u32x4_t{fp8x2_to_bf16x2<false>(x[2]), fp8x2_to_bf16x2<true>(x[2]),
+                 fp8x2_to_bf16x2<false>(x[3]), fp8x2_to_bf16x2<true>(x[3])};
   };
   auto store_tile = [&](int buf) __attribute__((always_inline)) {
     static_for<0, kLoads>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
       const int c = tid + kVThreads * k;
       const int tt = c / kChunks, piece = c - tt * kChunks;
-      *reinterpret_cast<u32x4_t*>(&kv[buf][0][tt * kPitch + piece * 16]) = stk[k];
-      *reinterpret_cast<u32x4_t*>(&kv[buf][1][tt * kPitch + piece * 16]) = stv[k];
+      if constexpr (FP8) {
+        u32x4_t lo, hi;
+        fp8_to_bf16(stk[k], okt[k], lo, hi);
+        *reinterpret_cast<u32x4_t*>(&kv[buf][0][tt * kPitch + piece * 32]) = lo;
+        *reinterpret_cast<u32x4_t*>(&kv[buf][0][tt * kPitch + piece * 32 + 16]) = hi;
+        fp8_to_bf16(stv[k], okt[k], lo, hi);
+        *reinterpret_cast<u32x4_t*>(&kv[buf][1][tt * kPitch + piece * 32]) = lo;
+        *reinterpret_cast<u32x4_t*>(&kv[buf][1][tt * kPitch + piece * 32 + 16]) = hi;
+      } else {
+        *reinterpret_cast<u32x4_t*>(&kv[buf][0][tt * kPitch + piece * 16]) = stk[k];
+        *reinterpret_cast<u32x4_t*>(&kv[buf][1][tt * kPitch + piece * 16]) = stv[k];
+      }
     });
   };
 
@@ -288,6 +320,15 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
   }
 }
 
+template <int D, bool FP8>
+hipError_t launch_verify_k(const DecodeArgs& a, dim3 grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  if (e0 && e1)
+    hipExtLaunchKernelGGL((verify_split_kernel<D, FP8>), grid, dim3(kVThreads), 0, st, e0, e1, 0, a);
+  else
+    hipLaunchKernelGGL((verify_split_kernel<D, FP8>), grid, dim3(kVThreads), 0, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool verify_supported(int head_dim, int group, int q_len) {
@@ -299,15 +340,9 @@ hipError_t launch_verify_split(const DecodeArgs& a, int head_dim, int group, hip
                                hipEvent_t e1) {
   if (!verify_supported(head_dim, group, a.q_len)) return hipErrorInvalidValue;
   dim3 grid(a.num_splits, a.hkv, a.num_seqs);
-  const bool timed = e0 && e1;
-  if (head_dim == 256) {
-    if (timed) hipExtLaunchKernelGGL(verify_split_kernel<256>, grid, dim3(kVThreads), 0, st, e0, e1, 0, a);
-    else hipLaunchKernelGGL(verify_split_kernel<256>, grid, dim3(kVThreads), 0, st, a);
-  } else {
-    if (timed) hipExtLaunchKernelGGL(verify_split_kernel<128>, grid, dim3(kVThreads), 0, st, e0, e1, 0, a);
-    else hipLaunchKernelGGL(verify_split_kernel<128>, grid, dim3(kVThreads), 0, st, a);
-  }
-  return hipGetLastError();
+  if (head_dim == 256)
+    return a.kv_fp8 ? launch_verify_k<256, true>(a, grid, st, e0, e1) : launch_verify_k<256, false>(a, grid, st, e0, e1);
+  return a.kv_fp8 ? launch_verify_k<128, true>(a, grid, st, e0, e1) : launch_verify_k<128, false>(a, grid, st, e0, e1);
 }
 
 }  // namespace pkv

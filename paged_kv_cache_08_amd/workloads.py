@@ -27,6 +27,7 @@ from typing import Sequence
 import numpy as np
 
 BF16_NAN = np.uint16(0x7FC0)
+FP8_NAN = np.uint8(0x7F)      # OCP FP8 E4M3 NaN code
 STREAMS = ("q", "k", "v", "mask", "pages", "lengths")
 
 
@@ -83,6 +84,9 @@ class DecodeCase:
     logical_v: list
     kv_pool: np.ndarray | None = None   # combined [num_pages, 2, B, Hkv, D] when requested
     meta: dict = dataclasses.field(default_factory=dict)
+    kv_dtype: str = "bf16"   # "bf16" (uint16 bits) or "fp8_e4m3" (uint8 codes; value = decoded * scale)
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     @property
     def num_seqs(self) -> int:
@@ -137,6 +141,7 @@ def make_case(
     combined: bool = False,
     interleave: bool = False,
     extra_table_cols: int = 0,
+    kv_dtype: str = "bf16",
 ) -> DecodeCase:
     """Build one paged decode input.
 
@@ -144,8 +149,12 @@ def make_case(
     (token, KV head) key rows of each sequence by ``boost`` (a power of two, so
     exact in bf16); this gives the peaked softmax of the long-context workloads.
     With ``poison`` every slot that no sequence owns (unused pages and the tail
-    of each last page) holds bf16 NaN, and table entries past a sequence's pages
+    of each last page) holds NaN, and table entries past a sequence's pages
     are -1, so any read outside the live range shows up in the output.
+
+    ``kv_dtype="fp8_e4m3"`` quantises the bf16 K and V draws to OCP FP8 E4M3
+    codes with one scale per tensor, amax / 448 as float32 (round to nearest
+    even, by torch's float8_e4m3fn conversion).
     """
     seq_lens = [int(x) for x in seq_lens]
     ns, hq, hkv, d, bs = len(seq_lens), num_q_heads, num_kv_heads, head_dim, block_size
@@ -169,6 +178,12 @@ def make_case(
         logical_k.append(k)
         logical_v.append(v)
 
+    k_scale = v_scale = 1.0
+    if kv_dtype == "fp8_e4m3":
+        logical_k, k_scale = _quantize_fp8(logical_k)
+        logical_v, v_scale = _quantize_fp8(logical_v)
+    elif kv_dtype != "bf16":
+        raise ValueError(f"unknown kv_dtype {kv_dtype!r}")
     n_pages = [-(-L // bs) for L in seq_lens]
     total = sum(n_pages)
     if pool_pages is None:
@@ -179,8 +194,12 @@ def make_case(
 
     max_pages = max(max(n_pages, default=0), 1) + extra_table_cols
     table = np.full((ns, max_pages), -1, dtype=np.int32)
-    fill = BF16_NAN if poison else np.uint16(0)
-    pool = np.full((pool_pages, 2, bs, hkv, d), fill, dtype=np.uint16)
+    fp8 = kv_dtype == "fp8_e4m3"
+    if fp8:
+        fill = FP8_NAN if poison else np.uint8(0)
+    else:
+        fill = BF16_NAN if poison else np.uint16(0)
+    pool = np.full((pool_pages, 2, bs, hkv, d), fill, dtype=np.uint8 if fp8 else np.uint16)
     for b, L in enumerate(seq_lens):
         table[b, : n_pages[b]] = pages[b]
         # Fill page by page: logical page p holds tokens [p*bs, min((p+1)*bs, L)).
@@ -204,7 +223,19 @@ def make_case(
         meta=dict(seed=seed, q_len=q_len, hq=hq, hkv=hkv, d=d, block_size=bs,
                   pool_pages=pool_pages, boost_frac=boost_frac, poison=poison,
                   combined=combined, interleave=interleave),
+        kv_dtype=kv_dtype, k_scale=k_scale, v_scale=v_scale,
     )
+
+
+def _quantize_fp8(rows: list) -> tuple[list, float]:
+    """bf16 bit arrays -> OCP FP8 E4M3 codes with one float32 scale, amax / 448."""
+    import torch
+    vals = [(np.asarray(r, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32) for r in rows]
+    amax = max((float(np.abs(v).max()) for v in vals if v.size), default=0.0)
+    scale = float(np.float32(amax / 448.0)) if amax > 0 else 1.0
+    codes = [torch.from_numpy(np.ascontiguousarray(v / np.float32(scale))).to(torch.float8_e4m3fn)
+             .view(torch.uint8).numpy().copy() for v in vals]
+    return codes, scale
 
 
 # ---------------------------------------------------------------------------

@@ -42,7 +42,8 @@ def params(**kw):
     base = dict(num_seqs=1, q_len=1, num_q_heads=24, num_kv_heads=4, head_dim=256, block_size=784,
                 max_pages_per_seq=42, max_seq_len=32768, num_pages=53, num_splits=0, total_tokens=0,
                 k_stride_page=784 * 4 * 256, k_stride_tok=4 * 256, k_stride_head=256,
-                v_stride_page=784 * 4 * 256, v_stride_tok=4 * 256, v_stride_head=256, scale=0.0625, out_dtype=0)
+                v_stride_page=784 * 4 * 256, v_stride_tok=4 * 256, v_stride_head=256, scale=0.0625, out_dtype=0,
+                window=0, kv_dtype=0, k_scale=1.0, v_scale=1.0)
     base.update(kw)
     for k, v in base.items():
         setattr(p, k, v)
@@ -65,7 +66,12 @@ def params(**kw):
     ({"q_len": 17}, -2),
     ({"window": 2048}, 0),
     ({"window": -1}, -1),
-    ({"reserved": 1}, -1),
+    ({"kv_dtype": 2}, -1),
+    ({"kv_dtype": 1, "k_scale": 0.01, "v_scale": 0.02}, 0),
+    ({"kv_dtype": 1, "k_scale": 0.0, "v_scale": 0.02}, -1),
+    ({"kv_dtype": 1, "k_scale": 0.01, "v_scale": float("inf")}, -1),
+    ({"kv_dtype": 1, "k_scale": 0.01, "v_scale": 0.02, "k_stride_head": 264}, -1),   # 8 but not 16 elements
+    ({"kv_dtype": 0, "k_stride_head": 264}, 0),
     ({"q_len": 0}, -1),
     ({"block_size": 0}, -1),
     ({"max_seq_len": 42 * 784 + 1}, -1),

@@ -593,3 +593,92 @@ def test_planted_window_off_by_one_fails_the_pin(monkeypatch):
     got = O.paged_attention_ref(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
                                 case.block_size, case.scale, 6)
     assert not np.allclose(got, ref, rtol=1e-6, atol=1e-8)
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 K/V caches (codes times a per-tensor scale).
+# ---------------------------------------------------------------------------
+
+def _torch_fp8_values():
+    import torch
+    return torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_fp8_decoder_matches_torch_for_every_code():
+    got, ref = O.fp8_e4m3_to_f64(np.arange(256)), _torch_fp8_values()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+
+
+def test_fp8_decoder_closed_forms():
+    v = O.fp8_e4m3_to_f64(np.array([0x00, 0x01, 0x07, 0x08, 0x38, 0x78, 0x7E, 0x80, 0xB8, 0x7F, 0xFF]))
+    assert v[0] == 0.0 and v[1] == 2.0 ** -9 and v[2] == 7 * 2.0 ** -9 and v[3] == 2.0 ** -6
+    assert v[4] == 1.0 and v[5] == 256.0 and v[6] == 448.0
+    assert v[7] == 0.0 and np.signbit(v[7]) and v[8] == -1.0
+    assert np.isnan(v[9]) and np.isnan(v[10])
+
+
+def _fp8_case(seed=81, lens=(40, 13), ql=2, bs=5, **kw):
+    return W.make_case(seed, list(lens), q_len=ql, num_q_heads=6, num_kv_heads=2, head_dim=8, block_size=bs,
+                       kv_dtype="fp8_e4m3", interleave=True, **kw)
+
+
+def _fp8_oracle(case, **kw):
+    return O.paged_attention_ref(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                                 case.block_size, case.scale, kv_dtype="fp8_e4m3", k_scale=case.k_scale,
+                                 v_scale=case.v_scale, **kw)
+
+
+def test_fp8_attention_is_bf16_attention_of_the_decoded_values():
+    # With power-of-two scales every decoded value times its scale is a bf16
+    # number; the FP8 path must then equal the bf16 path bit for bit.
+    case = _fp8_case(poison=True)
+    case.k_scale, case.v_scale = 2.0 ** -5, 2.0 ** 3
+    to_bf16 = lambda codes, s: W.f32_to_bf16_bits_np((np.nan_to_num(O.fp8_e4m3_to_f64(codes)) * s)
+                                                     .astype(np.float32))
+    kb, vb = to_bf16(case.k_cache, case.k_scale), to_bf16(case.v_cache, case.v_scale)
+    assert np.array_equal(O.bf16_bits_to_f64(kb)[np.isfinite(O.fp8_e4m3_to_f64(case.k_cache))],
+                          (O.fp8_e4m3_to_f64(case.k_cache) * case.k_scale)[np.isfinite(O.fp8_e4m3_to_f64(case.k_cache))])
+    ref = O.paged_attention_ref(case.q, kb, vb, case.block_table, case.seq_lens, case.block_size, case.scale)
+    np.testing.assert_array_equal(_fp8_oracle(case), ref)
+
+
+def test_fp8_attention_matches_brute_force():
+    case = _fp8_case(poison=False)
+    vals = _torch_fp8_values()
+    ns, ql, hq, d = case.q.shape
+    G = hq // 2
+    sigma = float(np.float32(case.scale))
+    ks, vs = float(np.float32(case.k_scale)), float(np.float32(case.v_scale))
+    out = np.zeros(case.q.shape)
+    for b in range(ns):
+        L = int(case.seq_lens[b])
+        K, V = case.logical_k[b].tolist(), case.logical_v[b].tolist()
+        for i in range(ql):
+            for h in range(hq):
+                qv = [_widen(x) for x in case.q[b, i, h].tolist()]
+                s = [sigma * math.fsum(qv[e] * vals[K[j][h // G][e]] * ks for e in range(d))
+                     for j in range(L - ql + i + 1)]
+                m = max(s)
+                ex = [math.exp(x - m) for x in s]
+                z = math.fsum(ex)
+                for e in range(d):
+                    out[b, i, h, e] = math.fsum(w * vals[V[j][h // G][e]] * vs for j, w in enumerate(ex)) / z
+    np.testing.assert_allclose(_fp8_oracle(case), out, rtol=1e-12, atol=1e-13)
+
+
+_fp8_true = O.fp8_e4m3_to_f64
+
+
+@pytest.mark.parametrize("name,attr,bad", [
+    ("exponent bias 8", "fp8_e4m3_to_f64", lambda c: _fp8_true(c) / 2.0),
+    ("scale ignored", "kv_widen", lambda kv_dtype, scale=1.0: _fp8_true),
+])
+def test_planted_fp8_mistakes_fail_the_pins(monkeypatch, name, attr, bad):
+    case = _fp8_case(poison=False)
+    ref = _fp8_oracle(case)
+    monkeypatch.setattr(O, attr, bad)
+    got = _fp8_oracle(case)
+    assert not np.allclose(got, ref, rtol=1e-6, atol=1e-8), name
