@@ -22,20 +22,27 @@ Sources (page titles as they appear on the pages):
   * "Qwen3.8 auf MI350P betreiben", Lektion 3: several verify rows share one
     K/V walk, each row keeps its own causal mask, and partial softmax
     statistics are merged.
+  * "如何在单张 RTX 3090 上让 Qwen3.5-27B token 生成速度提升 6 倍": decode
+    attention over the most recent 2,048 KV positions only (sliding window),
+    and a quantised KV cache (here OCP FP8 E4M3 with per-tensor scales).
 
 What is computed (the plain definition; split-KV is an exact re-association of
 it, so the oracle evaluates the definition directly):
     for sequence b, query row i, query head h:
         g   = h // G                        (G = Hq / Hkv, consecutive groups)
         pos = L_b - q_len + i               (bottom-right causal alignment)
-        s_j = sigma * sum_d q[b,i,h,d] * K_j[d]     for j in [0, pos]
+        lo  = 0, or max(0, pos - W + 1) with a sliding window W
+        s_j = sigma * sum_d q[b,i,h,d] * K_j[d]     for j in [lo, pos]
         out = sum_j exp(s_j - max s) V_j / sum_j exp(s_j - max s)
-with K_j, V_j read through the block table, bf16 widened exactly to fp64, and
-sigma = float64(float32(scale)), the value the kernel receives.
+with K_j, V_j read through the block table and widened exactly to fp64 (bf16
+bits, or FP8 E4M3 codes decoded from the OCP definition times the float32
+per-tensor scale), and sigma = float64(float32(scale)), the value the kernel
+receives. Varlen calls apply this to each sequence's own rows (q_len = n_b).
 
 Readings where the pages are silent (each also listed in the design notes):
 GQA head h uses KV head h // G; a sequence with L = 0 yields zeros; the
-multi-row causal window is bottom-right aligned (row i sees j <= L - q_len + i).
+multi-row causal window is bottom-right aligned (row i sees j <= L - q_len + i);
+a sliding window counts positions and includes the row's own token.
 
 Parity pins: every function here is checked by ``tests/test_oracle_pins.py``
 against brute force, closed forms, invariants, a library routine, and the
@@ -48,9 +55,10 @@ import math
 import numpy as np
 
 __all__ = [
-    "bf16_bits_to_f64", "page_of", "token_offsets_ref", "gather_token_rows",
-    "paged_attention_ref", "partial_stats_ref", "merge_partials_ref",
-    "split_attention_ref", "split_plan_ref", "split_ranges_ref", "kv_bytes_ref",
+    "bf16_bits_to_f64", "fp8_e4m3_to_f64", "kv_widen", "page_of", "token_offsets_ref", "gather_token_rows",
+    "kv_head_of", "last_visible", "first_visible", "paged_attention_ref", "paged_attention_varlen_ref",
+    "partial_stats_ref", "merge_partials_ref", "split_attention_ref", "split_plan_ref", "split_ranges_ref",
+    "kv_bytes_ref",
 ]
 
 
