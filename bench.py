@@ -25,7 +25,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn µs/step and KV-read GB/s (% of HBM peak) at 32K ctx, batch 1"
+METRIC_PREFILL = "chunked-prefill attention TFLOP/s (4 * head_dim flops per row, head and visible token)"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, MI355X
 
 
 def parse():
@@ -33,8 +35,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="hybrid", choices=["hybrid", "dense", "mixed", "verify", "varlen"])
-    ap.add_argument("--context", type=int, default=32768)
+    ap.add_argument("--workload", default="hybrid", choices=["hybrid", "dense", "mixed", "verify", "varlen", "prefill"])
+    ap.add_argument("--context", type=int, default=None,
+                    help="tokens in the cache (default 32768; 8192 for prefill)")
+    ap.add_argument("--chunk", type=int, default=4096, help="prefill: new query rows of the chunk")
     ap.add_argument("--block-size", type=int, default=784)
     ap.add_argument("--pools", type=int, default=16)
     ap.add_argument("--splits", type=int, default=0, help="force a split count (0 = planner)")
@@ -49,7 +53,10 @@ def parse():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before timing, copy this many MiB once (a kernel of known traffic, used to "
                          "scale rocprofv3 FETCH_SIZE / WRITE_SIZE)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.context is None:
+        args.context = 8192 if args.workload == "prefill" else 32768
+    return args
 
 
 class Hip:
@@ -92,6 +99,11 @@ def make_workload(args):
     elif args.workload == "mixed":
         case = W.mixed_batch(poison=False, **kv)
         name = "mixed batch: 16 sequences, q_len 1, 24 q / 4 KV heads, head_dim 256, page 784, log-uniform 500-32000"
+    elif args.workload == "prefill":
+        case, qp, cu = W.chunked_prefill(args.chunk, args.context, block_size=args.block_size, poison=False, **kv)
+        name = (f"chunked prefill: one chunk of {args.chunk} new rows on a {args.context}-token cache, "
+                f"24 q / 4 KV heads, head_dim 256, page {args.block_size}")
+        return case, name, (qp, cu)
     elif args.workload == "varlen":
         case, qp, cu = W.batched_verify(poison=False, **kv)
         name = ("batched speculative verify (varlen): 32 requests, 1..5 rows each, 24 q / 4 KV heads, "
@@ -129,14 +141,66 @@ def oracle_call(case, varlen, window):
                                  case.block_size, case.scale, window, case.kv_dtype, case.k_scale, case.v_scale)
 
 
+def oracle_rows(case, varlen, rows, window):
+    """The oracle's result for rows of sequence 0 of a packed call, one by one:
+    row i of n new rows sees the first L - n + i + 1 tokens, a one-row call on
+    that prefix. Returns [len(rows), Hq, D]."""
+    import numpy as np
+    import oracle.paged_attention as O
+    qp, cu = varlen
+    n, L = int(cu[1] - cu[0]), int(case.seq_lens[0])
+    out = []
+    for i in rows:
+        out.append(O.paged_attention_ref(qp[None, i:i + 1], case.k_cache, case.v_cache, case.block_table[:1],
+                                         np.array([L - n + i + 1]), case.block_size, case.scale, window,
+                                         case.kv_dtype, case.k_scale, case.v_scale)[0, 0])
+    return np.stack(out)
+
+
+def cpu_baseline_rows(case, varlen, window, seconds):
+    """Prefill: the oracle over a seeded sample of the chunk's rows (a whole
+    call is minutes of CPU work), reported as attention TFLOP/s."""
+    import numpy as np
+    from paged_kv_cache_08_amd import workloads as W
+    threads = _blas_threads()
+    n = int(varlen[1][1])
+    order = np.random.default_rng(3).permutation(n)
+    flops, done, t0 = 0, 0, time.perf_counter()
+    L = int(case.seq_lens[0])
+    while done < n:
+        i = int(order[done])
+        oracle_rows(case, varlen, [i], window)
+        vis = L - n + i + 1 if window <= 0 else min(L - n + i + 1, window)
+        flops += 4 * case.q.shape[3] * case.q.shape[2] * vis
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {
+        "value": round(flops / el / 1e12, 6),
+        "unit": "TFLOP/s",
+        "us_per_row": round(el / done * 1e6, 1),
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} random rows of the {n}-row chunk (all {case.q.shape[2]} heads), one-row oracle calls "
+                  f"on their causal prefixes (fp64 NumPy, BLAS threads={threads}), {el:.1f} s",
+        "host_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return int(os.environ.get("OMP_NUM_THREADS", "1"))
+
+
 def cpu_baseline(case, varlen, window, kv_bytes_per_call, seconds):
     """The oracle as it stands, on the host cores, over whole calls of the same
     workload until about `seconds` of CPU work has run."""
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    threads = _blas_threads()
     n, t0 = 0, time.perf_counter()
     while True:
         oracle_call(case, varlen, window)
@@ -173,6 +237,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     case, wl_name, varlen = make_workload(args)
+    prefill = args.workload == "prefill"
     print(f"[bench] workload: {wl_name}", file=sys.stderr, flush=True)
 
     def bf16(a):
@@ -198,10 +263,11 @@ def main():
     rows = [case.q_len] * case.num_seqs if varlen is None else np.diff(varlen[1])
     kv_bytes = W.kv_read_bytes(case.seq_lens, case.k_cache.shape[2], case.k_cache.shape[3],
                                elem_bytes=case.k_cache.dtype.itemsize, window=args.window, rows=rows)
+    flops = W.attention_flops(case.seq_lens, rows, case.q.shape[2], case.q.shape[3], window=args.window)
     stream = torch.cuda.current_stream(dev).cuda_stream
     call = P.PreparedDecode(q, k0, v0, table, lens, case.block_size, case.scale, max_seq_len=case.max_seq_len,
                             total_tokens=total_tokens, num_splits=args.splits, stream=stream,
-                            cu_seqlens_q=cu_t, max_q_len=max_q, window=args.window, **scales)
+                            cu_seqlens_q=cu_t, max_q_len=max_q, window=args.window, prefill=prefill, **scales)
     out = call.out
 
     ptrs = [(k.data_ptr(), v.data_ptr()) for k, v in pools]
@@ -275,7 +341,7 @@ def main():
                                      max_seq_len=case.max_seq_len, total_tokens=total_tokens,
                                      num_splits=args.splits, out=out, workspace=call.workspace,
                                      stream=gstream.cuda_stream, cu_seqlens_q=cu_t, max_q_len=max_q,
-                                     window=args.window, **scales)
+                                     window=args.window, prefill=prefill, **scales)
         torch.cuda.synchronize()
         with torch.cuda.graph(graph, stream=gstream):
             for i in range(args.steps):
@@ -300,8 +366,12 @@ def main():
     got = out.cpu().numpy().astype(np.float64)
     parity = None
     try:
-        ref = oracle_call(case, varlen, args.window)
-        parity = float(np.abs(got - ref).max())
+        if prefill:   # sampled rows: a whole oracle call is minutes of CPU work
+            sample = [0, 1, 2047, int(varlen[1][1]) - 1]
+            parity = float(np.abs(got[sample] - oracle_rows(case, varlen, sample, args.window)).max())
+        else:
+            ref = oracle_call(case, varlen, args.window)
+            parity = float(np.abs(got - ref).max())
     except Exception as e:  # parity is reported, never required for the timing
         print(f"[bench] parity check skipped: {e}", file=sys.stderr)
 
@@ -309,19 +379,37 @@ def main():
     kern_gbs = kv_bytes / (kern_avg_us * 1e-6) / 1e9
     from paged_kv_cache_08_amd.profiling import kernel_source_hash
     src_hash = kernel_source_hash()
-    wl_key = (f"{args.workload}:{args.context}:{case.block_size}" + (f":w{args.window}" if args.window else "")
+    wl_key = (f"{args.workload}:{args.context}:{case.block_size}" + (f":q{args.chunk}" if prefill else "")
+              + (f":w{args.window}" if args.window else "")
               + (":fp8" if args.kv_dtype == "fp8" else ""))
     traffic = traffic_from_profiles(src_hash, wl_key)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(case, varlen, args.window, kv_bytes, args.cpu_seconds)
+        if prefill:
+            cpu = cpu_baseline_rows(case, varlen, args.window, args.cpu_seconds)
+        else:
+            cpu = cpu_baseline(case, varlen, args.window, kv_bytes, args.cpu_seconds)
+
+    if prefill:   # a dense contraction: priced against the bf16 MFMA peak
+        tflops = flops / (ms_per_step * 1e-3) / 1e12
+        kern_tflops = flops / (kern_avg_us * 1e-6) / 1e12
+        value, unit = round(tflops, 2), "TFLOP/s"
+        roof = {"bound": "mfma", "kernel": "verify_split_kernel (prefill blocks)", "achieved": round(kern_tflops, 2),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    else:
+        value, unit = round(gbs, 1), "GB/s"
+        roof = {"bound": "hbm",
+                "kernel": "verify_split_kernel" if (case.q_len > 1 or varlen is not None) else "decode_split_kernel",
+                "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(kern_gbs / HBM_PEAK_GBS, 4)}
+    roof.update({"traffic": traffic, "kernel_us_avg": round(kern_avg_us, 2), "kernel_us_min": round(min(kern_us), 2)})
 
     med = statistics.median(region_us)
     rec = {
-        "metric": METRIC,
-        "value": round(gbs, 1),
-        "unit": "GB/s",
+        "metric": METRIC_PREFILL if prefill else METRIC,
+        "value": value,
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -341,6 +429,7 @@ def main():
             "block_size": int(case.block_size),
             "kv_pools_rotated": len(pools),
             "kv_bytes_per_step": kv_bytes,
+            "flops_per_step": flops,
             "variant": variant,
         },
         "us_per_step": round(ms_per_step * 1e3, 2),
@@ -348,17 +437,7 @@ def main():
         "us_per_step_regions": {"median": round(med, 2), "min": round(min(region_us), 2),
                                 "max": round(max(region_us), 2),
                                 "range_pct": round(100.0 * (max(region_us) - min(region_us)) / med, 2)},
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "verify_split_kernel" if (case.q_len > 1 or varlen is not None) else "decode_split_kernel",
-            "achieved": round(kern_gbs, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "kernel_us_avg": round(kern_avg_us, 2),
-            "kernel_us_min": round(min(kern_us), 2),
-        },
+        "roofline": roof,
         "graph_us_per_step": None if graph_us is None else round(graph_us, 2),
         "graph_gbs": None if graph_us is None else round(kv_bytes / (graph_us * 1e-6) / 1e9, 1),
         "cpu_baseline": cpu,

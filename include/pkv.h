@@ -46,7 +46,7 @@ extern "C" {
 
 #define PKV_OK               0
 #define PKV_ERR_INVALID     -1  /* null pointer, bad size, Hq % Hkv != 0, stride or alignment error */
-#define PKV_ERR_UNSUPPORTED -2  /* head_dim not 128/256, q_len not in [1,16], too many query rows per KV head, ... */
+#define PKV_ERR_UNSUPPORTED -2  /* head_dim not 128/256, q_len out of range, too many query rows per KV head, ... */
 #define PKV_ERR_WORKSPACE   -3  /* workspace smaller than pkv_workspace_bytes() */
 #define PKV_ERR_HIP         -4  /* a HIP runtime call or launch failed */
 
@@ -61,7 +61,7 @@ extern "C" {
  * 2 x float (120 bytes, natural alignment). */
 typedef struct pkv_decode_params {
   int32_t num_seqs;          /* sequences in the batch, >= 1 */
-  int32_t q_len;             /* new query rows per sequence, 1..16 (1 = decode) */
+  int32_t q_len;             /* new query rows per sequence, 1..16 (1 = decode; prefill: up to 2^24) */
   int32_t num_q_heads;       /* Hq */
   int32_t num_kv_heads;      /* Hkv; Hq % Hkv == 0; Hq / Hkv <= 8 when q_len == 1,
                                 (Hq / Hkv) * q_len <= 128 when q_len > 1 */
@@ -191,10 +191,41 @@ int pkv_paged_varlen_attention(const pkv_decode_params* p,
                                void* out, void* workspace, int64_t workspace_bytes,
                                void* stream);
 
-/* Which kernels the last successful pkv_paged_decode_attention (or
- * pkv_paged_varlen_attention) call on this thread launched, with the split
- * plan, e.g. "decode_valu d256 g6 q1 w512 + lse_merge splits=64 chunk=512 B=784". Copies at most
- * len-1 characters plus a terminator; returns the full length. */
+/* Workspace bytes of a prefill call: the error word's header only. */
+#define PKV_PREFILL_WORKSPACE_BYTES 256
+
+/*
+ * Chunked-prefill call: sequence b appends n_b = cu_seqlens_q[b + 1] -
+ * cu_seqlens_q[b] new tokens (a chunk of a long prompt, whose K/V rows the
+ * caller has already written into the paged cache) and each new row attends
+ * causally to everything before it, the cached prefix included. "DCU page832
+ * attention" §6 serves prompts in chunks of 4096 query rows plus a shorter
+ * tail chunk (1 < q <= 4096) with full causal attention over the paged
+ * context; this call takes any chunk length. Arguments, packing and the
+ * causal rule are those of pkv_paged_varlen_attention, except:
+ *   - p->q_len (the largest n_b) may be up to 2^24 and num_seqs * q_len at
+ *     most 2^31 - 1; Hq / Hkv <= 128;
+ *   - the rows of a sequence are cut into blocks of floor(128 / (Hq / Hkv))
+ *     positions; each block runs as one workgroup per KV head over its whole
+ *     visible range (no split and no merge), so the output is written
+ *     directly and the workspace holds only the error word: it must be
+ *     >= PKV_PREFILL_WORKSPACE_BYTES bytes and 256-byte aligned;
+ *   - num_splits and total_tokens are ignored.
+ * A block-table entry outside [0, num_pages) sets bit 0 of the error word and
+ * its tokens are skipped; inconsistent cu_seqlens_q rows set bit 1.
+ */
+int pkv_paged_prefill_attention(const pkv_decode_params* p,
+                                const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, const int32_t* seq_lens,
+                                const int32_t* cu_seqlens_q,
+                                void* out, void* workspace, int64_t workspace_bytes,
+                                void* stream);
+
+/* Which kernels the last successful attention call on this thread launched,
+ * with the split plan, e.g. "decode_valu d256 g6 q1 w512 + lse_merge
+ * splits=64 chunk=512 B=784" (for prefill, w is the query positions per
+ * workgroup). Copies at most len-1 characters plus a terminator; returns the
+ * full length. */
 int pkv_last_variant(char* buf, int32_t len);
 
 /* Profiling hook: when both are non-NULL, later calls on this thread launch

@@ -19,6 +19,7 @@ PKV_ERR_UNSUPPORTED = -2
 PKV_ERR_WORKSPACE = -3
 PKV_ERR_HIP = -4
 PKV_OUT_F32 = 0
+PKV_PREFILL_WORKSPACE_BYTES = 256   # prefill calls: the error-word header only
 PKV_OUT_BF16 = 1
 PKV_KV_BF16 = 0
 PKV_KV_FP8_E4M3 = 1
@@ -73,6 +74,8 @@ _SIGNATURES = {
     "pkv_paged_decode_attention": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64, _vp]),
     "pkv_paged_varlen_attention": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64,
                                                   _vp]),
+    "pkv_paged_prefill_attention": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64,
+                                                   _vp]),
     "pkv_last_variant": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_int32]),
     "pkv_set_timing_events": (ctypes.c_int, [_vp, _vp]),
     "pkv_debug_token_offsets": (ctypes.c_int, [_P, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp]),
@@ -285,6 +288,40 @@ def paged_varlen_attention(q, k_cache, v_cache, block_table, seq_lens, cu_seqlen
     return out
 
 
+def paged_prefill_attention(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, block_size: int,
+                            scale: float, *, max_q_len: int, max_seq_len: int, out=None, out_dtype=None,
+                            workspace=None, stream=None, window: int = 0, k_scale: float = 1.0,
+                            v_scale: float = 1.0):
+    """Chunked prefill: like paged_varlen_attention (packed rows q [total_q, Hq, D],
+    cu_seqlens_q, causal rows ending at seq_lens[b]) for any number of new rows
+    per sequence; one pass per block of query positions, no split workspace
+    (the workspace holds only the 256-byte error-word header)."""
+    torch = _torch()
+    assert q.is_cuda and q.dtype == torch.bfloat16 and q.is_contiguous() and q.dim() == 3
+    assert cu_seqlens_q.dtype == torch.int32 and cu_seqlens_q.is_contiguous()
+    assert block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
+    assert block_table.is_contiguous() and seq_lens.is_contiguous()
+    ns = seq_lens.shape[0]
+    assert cu_seqlens_q.shape[0] == ns + 1 and block_table.shape[0] == ns
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+    odt = PKV_OUT_BF16 if out.dtype == torch.bfloat16 else PKV_OUT_F32
+    assert out.dtype in (torch.float32, torch.bfloat16) and out.is_contiguous() and out.shape == q.shape
+    shape4 = torch.empty((ns, int(max_q_len), q.shape[1], q.shape[2]), device="meta")
+    p = make_params(shape4, k_cache, v_cache, block_table, block_size, scale, max_seq_len=max_seq_len,
+                    out_dtype=odt, window=window, k_scale=k_scale, v_scale=v_scale)
+    if workspace is None:
+        workspace = torch.zeros(PKV_PREFILL_WORKSPACE_BYTES, dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib().pkv_paged_prefill_attention(
+        ctypes.byref(p), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+        seq_lens.data_ptr(), cu_seqlens_q.data_ptr(), out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), stream)
+    check(rc, "pkv_paged_prefill_attention")
+    return out
+
+
 def debug_token_offsets(p: DecodeParams, block_table, seq_lens, kv_head: int):
     """Per-token K and V row offsets as the split kernel computes them ([num_seqs, max_seq_len] int64)."""
     torch = _torch()
@@ -321,12 +358,13 @@ class PreparedDecode:
     ``run(k_cache, v_cache)`` may swap in another pool with the same shape and
     strides as the one given at construction. With ``cu_seqlens_q`` (int32 on
     the GPU) and ``max_q_len`` the call is the varlen one on packed rows
-    q [total_q, Hq, D]."""
+    q [total_q, Hq, D]; ``prefill=True`` makes it the chunked-prefill call on
+    the same packed rows."""
 
     def __init__(self, q, k_cache, v_cache, block_table, seq_lens, block_size: int, scale: float, *,
                  max_seq_len: int, total_tokens: int = 0, num_splits: int = 0, out=None, workspace=None,
                  stream=None, cu_seqlens_q=None, max_q_len: int | None = None, window: int = 0,
-                 k_scale: float = 1.0, v_scale: float = 1.0):
+                 k_scale: float = 1.0, v_scale: float = 1.0, prefill: bool = False):
         torch = _torch()
         assert q.is_cuda and q.dtype == torch.bfloat16 and q.is_contiguous()
         assert block_table.is_contiguous() and seq_lens.is_contiguous()
@@ -334,6 +372,7 @@ class PreparedDecode:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
         odt = PKV_OUT_BF16 if out.dtype == torch.bfloat16 else PKV_OUT_F32
         self.varlen = cu_seqlens_q is not None
+        assert self.varlen or not prefill, "prefill calls take packed rows and cu_seqlens_q"
         if self.varlen:
             assert q.dim() == 3 and cu_seqlens_q.dtype == torch.int32 and cu_seqlens_q.is_contiguous()
             assert max_q_len is not None and max_q_len >= 1
@@ -345,7 +384,7 @@ class PreparedDecode:
                                   k_scale=k_scale, v_scale=v_scale)
         if not self.varlen:
             check(validate(self.params), "pkv_validate_params")
-        need = workspace_bytes(self.params, 0)
+        need = PKV_PREFILL_WORKSPACE_BYTES if prefill else workspace_bytes(self.params, 0)
         if workspace is None:
             workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
         assert workspace.numel() * workspace.element_size() >= need
@@ -359,7 +398,9 @@ class PreparedDecode:
         self._fixed = (q.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
                        workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
         self._cu = cu_seqlens_q.data_ptr() if self.varlen else None
-        self._fn = lib().pkv_paged_varlen_attention if self.varlen else lib().pkv_paged_decode_attention
+        self._name = ("pkv_paged_prefill_attention" if prefill else
+                      "pkv_paged_varlen_attention" if self.varlen else "pkv_paged_decode_attention")
+        self._fn = getattr(lib(), self._name)
         self._k, self._v = k_cache.data_ptr(), v_cache.data_ptr()
 
     def run_ptrs(self, k_ptr: int, v_ptr: int) -> None:
@@ -370,7 +411,7 @@ class PreparedDecode:
         else:
             rc = self._fn(self._pp, qp, k_ptr, v_ptr, tp, lp, self._cu, op, wp, wn, st)
         if rc != PKV_OK:
-            check(rc, "pkv_paged_varlen_attention" if self.varlen else "pkv_paged_decode_attention")
+            check(rc, self._name)
 
     def run(self, k_cache=None, v_cache=None):
         kp, vp = self._k, self._v

@@ -150,9 +150,12 @@ const char* pkv_last_error(void) { return g_last_error.c_str(); }
 
 namespace {
 
-// Checks shared by the uniform and the varlen calls (all but the kernel's
-// limits on q_len and the group size).
-int validate_common(const pkv_decode_params* p) {
+// Query rows per sequence a prefill call accepts.
+constexpr int32_t kMaxPrefillRows = 1 << 24;
+
+// Checks shared by every call (all but the kernels' limits on the group size);
+// max_q_len is 16 for the decode and varlen calls.
+int validate_common(const pkv_decode_params* p, int32_t max_q_len = 16) {
   if (!p) return fail(PKV_ERR_INVALID, "params is NULL");
   if (p->num_seqs < 1 || p->q_len < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1 ||
       p->block_size < 1 || p->max_pages_per_seq < 1 || p->num_pages < 1 || p->max_seq_len < 0 ||
@@ -165,7 +168,8 @@ int validate_common(const pkv_decode_params* p) {
   if (p->num_q_heads % p->num_kv_heads != 0)
     return fail(PKV_ERR_INVALID, "num_q_heads is not a multiple of num_kv_heads");
   if (p->head_dim != 128 && p->head_dim != 256) return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 128 or 256");
-  if (p->q_len > 16) return fail(PKV_ERR_UNSUPPORTED, "q_len above 16");
+  if (p->q_len > max_q_len)
+    return fail(PKV_ERR_UNSUPPORTED, "q_len above " + std::to_string(max_q_len));
   if (p->max_seq_len > (1 << 30)) return fail(PKV_ERR_UNSUPPORTED, "max_seq_len above 2^30 tokens");
   if (int64_t(p->max_pages_per_seq) * p->block_size < p->max_seq_len)
     return fail(PKV_ERR_INVALID, "max_seq_len exceeds max_pages_per_seq * block_size");
@@ -191,6 +195,20 @@ int validate_varlen(const pkv_decode_params* p) {
   if (rc) return rc;
   if (!pkv::verify_supported(p->head_dim, p->num_q_heads / p->num_kv_heads, p->q_len))
     return fail(PKV_ERR_UNSUPPORTED, "varlen calls need (Hq / Hkv) * max q_len <= 128");
+  return PKV_OK;
+}
+
+// Query positions per prefill workgroup: as many as fill the MFMA kernel's
+// 128 rows with all query heads of one KV head.
+int32_t prefill_rows(const pkv_decode_params* p) { return 128 / (p->num_q_heads / p->num_kv_heads); }
+
+int validate_prefill(const pkv_decode_params* p) {
+  int rc = validate_common(p, kMaxPrefillRows);
+  if (rc) return rc;
+  if (p->num_q_heads / p->num_kv_heads > 128)
+    return fail(PKV_ERR_UNSUPPORTED, "prefill calls need Hq / Hkv <= 128");
+  if (int64_t(p->num_seqs) * p->q_len > (int64_t(1) << 31) - 1)
+    return fail(PKV_ERR_UNSUPPORTED, "num_seqs * q_len above 2^31 - 1 rows");
   return PKV_OK;
 }
 
@@ -327,6 +345,38 @@ int pkv_paged_varlen_attention(const pkv_decode_params* p, const void* q, const 
   if (!cu_seqlens_q) return fail(PKV_ERR_INVALID, "cu_seqlens_q is NULL");
   return launch_call(p, q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, out, workspace,
                      workspace_bytes, stream);
+}
+
+int pkv_paged_prefill_attention(const pkv_decode_params* p, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                                const int32_t* cu_seqlens_q, void* out, void* workspace, int64_t workspace_bytes,
+                                void* stream) {
+  int rc = validate_prefill(p);
+  if (rc) return rc;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !cu_seqlens_q || !out || !workspace)
+    return fail(PKV_ERR_INVALID, "a device pointer is NULL");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return fail(PKV_ERR_INVALID, "q, k_cache, v_cache and out must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return fail(PKV_ERR_INVALID, "workspace must be 256-byte aligned");
+  if (workspace_bytes < PKV_PREFILL_WORKSPACE_BYTES)
+    return fail(PKV_ERR_WORKSPACE,
+                "workspace needs " + std::to_string(PKV_PREFILL_WORKSPACE_BYTES) + " bytes");
+  pkv::DecodeArgs a = make_args(p, 1, 0);
+  a.pf_rows = prefill_rows(p);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_cache);
+  a.v = static_cast<const uint16_t*>(v_cache);
+  a.table = block_table;
+  a.seq_lens = seq_lens;
+  a.cu_q = cu_seqlens_q;
+  a.out = out;
+  a.err = static_cast<uint32_t*>(workspace);
+  const int group = p->num_q_heads / p->num_kv_heads;
+  hipError_t e = pkv::launch_prefill(a, p->head_dim, group, static_cast<hipStream_t>(stream), g_ev_start, g_ev_stop);
+  if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
+  g_last_variant = VariantInfo{"prefill_mfma", p->head_dim, group, p->q_len, a.pf_rows, 1, 0, p->block_size};
+  return PKV_OK;
 }
 
 int pkv_last_variant(char* buf, int32_t len) {

@@ -73,6 +73,7 @@ struct DecodeArgs {
   int32_t window;           // sliding window in positions (0 = whole context)
   int32_t kv_fp8;           // K/V caches hold FP8 E4M3 codes (else bf16)
   float out_scale;          // applied to every stored output (the FP8 V scale, else 1)
+  int32_t pf_rows;          // prefill calls: query positions per workgroup block (else 0)
 };
 
 // Launchers (decode_kernels.hip, decode_w*.hip, verify_kernels.hip). Return
@@ -101,6 +102,10 @@ hipError_t launch_decode_split_w512_fp8(const DecodeArgs& a, int head_dim, int g
                                         hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_verify_split(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
                                hipEvent_t ev_start, hipEvent_t ev_stop);
+// Prefill: blocks of a.pf_rows query positions per workgroup, each over its
+// whole visible range in one pass (no split, no merge; output written directly).
+hipError_t launch_prefill(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
+                          hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_lse_merge(const DecodeArgs& a, int head_dim, hipStream_t st);
 hipError_t launch_debug_offsets(const DecodeArgs& a, int kv_head, int max_seq_len,
                                 int64_t* k_off, int64_t* v_off, hipStream_t st);

@@ -114,7 +114,8 @@ struct QRows {
 __device__ __forceinline__ QRows seq_q_rows(const DecodeArgs& a, int b) {
   if (!a.cu_q) return {b * a.q_len, a.q_len, true};
   const int lo = a.cu_q[b], hi = a.cu_q[b + 1], total = a.cu_q[a.num_seqs];
-  const bool ok = lo >= 0 && hi >= lo && hi - lo <= a.q_len && hi <= total && hi <= a.num_seqs * a.q_len;
+  const bool ok = lo >= 0 && hi >= lo && hi - lo <= a.q_len && hi <= total &&
+                  int64_t(hi) <= int64_t(a.num_seqs) * a.q_len;
   return {ok ? lo : 0, ok ? hi - lo : 0, ok};
 }
 
@@ -182,6 +183,47 @@ __device__ __forceinline__ void flag_invalid_entries(const DecodeArgs& a, const 
   if (!a.err) return;
   for (int i = threadIdx.x; i < n; i += blockDim.x)
     if (tbl[i].k < 0) atomicOr(a.err, 1u);
+}
+
+// Prefill block: query positions [p0, p0 + rows) of a sequence with n new
+// rows (of L tokens) see tokens up to L - n + p0 + rows - 1; the block is one
+// span [lo, that + 1) (lo from the window), in a single split.
+__device__ __forceinline__ SplitSpan prefill_span(const DecodeArgs& a, int b, int n, int p0, int rows) {
+  const int64_t table_cap = int64_t(a.max_pages) * int64_t(a.bdiv.d);
+  int64_t L = a.seq_lens[b];
+  L = L < 0 ? 0 : (L > table_cap ? table_cap : L);
+  int64_t end = L - n + p0 + rows;
+  end = end < 0 ? 0 : end;
+  int64_t lo = 0;
+  if (a.window > 0) {
+    lo = end - rows + 1 - a.window;
+    lo = lo < 0 ? 0 : lo;
+  }
+  SplitSpan r;
+  r.L = int(end);
+  r.lo = int(lo);
+  r.begin = r.lo;
+  r.end = r.L;
+  r.nsplit = 1;
+  return r;
+}
+
+// Element offsets of token t's K and V rows read straight from the block
+// table (no LDS staging); false if its entry is outside [0, num_pages), which
+// also sets bit 0 of the workspace error word.
+__device__ __forceinline__ bool token_row_global(const DecodeArgs& a, int b, int g, int t, int64_t& ko,
+                                                 int64_t& vo) {
+  const uint32_t pg = magic_div(uint32_t(t), a.bdiv);
+  const int off = t - int(pg * a.bdiv.d);
+  const int e = a.table[int64_t(b) * a.max_pages + pg];
+  if (uint32_t(e) >= uint32_t(a.num_pages)) {
+    if (a.err) atomicOr(a.err, 1u);
+    ko = vo = 0;
+    return false;
+  }
+  ko = int64_t(e) * a.k_sp + int64_t(g) * a.k_sh + int64_t(off * int32_t(a.k_st));
+  vo = int64_t(e) * a.v_sp + int64_t(g) * a.v_sh + int64_t(off * int32_t(a.v_st));
+  return true;
 }
 
 // Element offsets of token t's K and V rows; false if its page entry is

@@ -65,7 +65,11 @@ __device__ __forceinline__ uint32_t bf16_pair(float x, float y) {
 // rescale of O.
 constexpr float kLazyMax = 8.0f;
 
-template <int D, bool FP8>
+// PF (prefill): blockIdx.x is a block of a.pf_rows query positions instead
+// of a KV split; the block covers its whole visible range in one pass and
+// reads block-table entries from global memory (the range can exceed what the
+// LDS table holds).
+template <int D, bool FP8, bool PF>
 __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a) {
   constexpr int kPitch = D * 2 + 16;              // LDS bytes per token row (padded)
   constexpr int kElems = FP8 ? 16 : 8;            // elements per 16-byte chunk of a cache row
@@ -77,34 +81,43 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
 
   __shared__ __attribute__((aligned(16))) uint8_t kv[2][2][kVTile * kPitch];
   __shared__ PageOffs tbl[kMaxChunk + 2];
+  __shared__ __attribute__((aligned(4))) uint8_t tok_ok[2][kVTile];   // token's table entry valid
 
-  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int s = PF ? 0 : blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, ln = lane & 15;
   const QRows qr = seq_q_rows(a, b);
-  const int q_len = qr.n;                         // query rows of this sequence
+  const int p0 = PF ? blockIdx.x * a.pf_rows : 0;          // first query position of the block
+  const int q_len = PF ? min(a.pf_rows, qr.n - p0) : qr.n;   // query rows of this workgroup
+  const int row_base = qr.base + p0;
   const int G = a.hq / a.hkv;
   const int R = G * q_len;                        // rows of this KV head (<= 128)
-  if (q_len == 0) {                               // no rows, or inconsistent cu_seqlens_q
-    if (!qr.ok && s == 0 && g == 0 && tid == 0 && a.err) atomicOr(a.err, 2u);
+  if (q_len <= 0) {                               // no rows, or inconsistent cu_seqlens_q
+    if (!qr.ok && blockIdx.x == 0 && g == 0 && tid == 0 && a.err) atomicOr(a.err, 2u);
     return;
   }
-  // The table slots do not depend on the sequence length: fetch them while
-  // seq_lens is still in flight.
-  SplitPages pages = split_pages(a, s);
-  if (a.window == 0) stage_table(a, b, g, pages.p_first, pages.n, tbl);
-  const SplitSpan sp = split_span(a, b, s, q_len);
+  SplitPages pages{0, 0};
+  SplitSpan sp;
+  if constexpr (PF) {
+    sp = prefill_span(a, b, qr.n, p0, q_len);
+  } else {
+    // The table slots do not depend on the sequence length: fetch them while
+    // seq_lens is still in flight.
+    pages = split_pages(a, s);
+    if (a.window == 0) stage_table(a, b, g, pages.p_first, pages.n, tbl);
+    sp = split_span(a, b, s, q_len);
+  }
 
   if (sp.begin >= sp.L) {
     if (s == 0)   // empty sequence: zeros for every row of this KV head
       for (int i = tid; i < R * D; i += kVThreads) {
         const int f = i / D, d = i - f * D;
-        const int64_t prow = (int64_t(qr.base) + f % q_len) * a.hq + int64_t(g) * G + f / q_len;
+        const int64_t prow = (int64_t(row_base) + f % q_len) * a.hq + int64_t(g) * G + f / q_len;
         store_out(a, prow * D + d, 0.0f);
       }
     return;
   }
-  if (a.window > 0) {   // the split starts at the first token of the rows' windows
+  if (!PF && a.window > 0) {   // the split starts at the first token of the rows' windows
     pages = span_pages(a, sp);
     stage_table(a, b, g, pages.p_first, pages.n, tbl);
   }
@@ -121,14 +134,14 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
   // Q of row ln, as the B operand of S^T: k step kk holds d = 32 kk + 8 grp .. +8.
   uint4 qreg[kKSteps];
   {
-    const int64_t qoff = ((int64_t(qr.base) + i_row) * a.hq + int64_t(g) * G + h_row) * D + 8 * grp;
+    const int64_t qoff = ((int64_t(row_base) + i_row) * a.hq + int64_t(g) * G + h_row) * D + 8 * grp;
 #pragma unroll
     for (int kk = 0; kk < kKSteps; ++kk)
       qreg[kk] = (computes && row_valid) ? *reinterpret_cast<const uint4*>(a.q + qoff + 32 * kk)
                                          : make_uint4(0, 0, 0, 0);
   }
   __syncthreads();   // table staged
-  flag_invalid_entries(a, tbl, int(magic_div(uint32_t(sp.end - 1), a.bdiv)) - p_first + 1);
+  if constexpr (!PF) flag_invalid_entries(a, tbl, int(magic_div(uint32_t(sp.end - 1), a.bdiv)) - p_first + 1);
 
   float4_t o[kDBlocks];
 #pragma unroll
@@ -146,7 +159,11 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
       const int t = sp.begin + tile * kVTile + tt;
       const int tc = min(t, sp.end - 1);
       int64_t ko, vo;
-      const bool ok = token_row(a, tbl, p_first, tc, ko, vo) && t < sp.end;
+      bool ok;
+      if constexpr (PF)
+        ok = token_row_global(a, b, g, tc, ko, vo) && t < sp.end;
+      else
+        ok = token_row(a, tbl, p_first, tc, ko, vo) && t < sp.end;
       okt[k] = ok;
       if constexpr (FP8) {   // element offsets are byte offsets
         const uint8_t* kp = ok ? reinterpret_cast<const uint8_t*>(a.k) + ko + piece * 16
@@ -177,6 +194,7 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
       constexpr int k = decltype(kc)::value;
       const int c = tid + kVThreads * k;
       const int tt = c / kChunks, piece = c - tt * kChunks;
+      if (piece == 0) tok_ok[buf][tt] = okt[k];
       if constexpr (FP8) {
         u32x4_t lo, hi;
         fp8_to_bf16(stk[k], okt[k], lo, hi);
@@ -213,19 +231,22 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
           st[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr), as_bf16x8(qreg[kk]), st[tb], 0, 0, 0);
         }
       }
-      // Scale, causal / range mask, tile max of row ln.
+      // Scale, causal / range / skipped-page mask, tile max of row ln.
       const int t0 = sp.begin + tile * kVTile + 4 * grp;
       float mt = -INFINITY;
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
+      for (int tb = 0; tb < 4; ++tb) {
+        const uint32_t okw = *reinterpret_cast<const uint32_t*>(&tok_ok[buf][tb * 16 + 4 * grp]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = t0 + tb * 16 + r;
-          const bool vis = row_valid && t < sp.end && t <= pos_row && (a.window == 0 || t > pos_row - a.window);
+          const bool vis = row_valid && ((okw >> (8 * r)) & 0xffu) != 0 && t <= pos_row &&
+                           (a.window == 0 || t > pos_row - a.window);
           const float x = vis ? st[tb][r] * a.scale_log2 : -INFINITY;
           st[tb][r] = x;
           mt = fmaxf(mt, x);
         }
+      }
       mt = fmaxf(mt, __shfl_xor(mt, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
       const float m_new = mt > m_run + kLazyMax ? mt : m_run;
@@ -294,7 +315,7 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
 
   if (!computes) return;
   // Rows 4 grp + r of O; their (max, sum) are held by lane 4 grp + r of each group.
-  const int64_t prow_base = int64_t(qr.base) * a.hq + int64_t(g) * G;
+  const int64_t prow_base = int64_t(row_base) * a.hq + int64_t(g) * G;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int src = 16 * grp + 4 * grp + r;
@@ -320,13 +341,23 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
   }
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool PF>
 hipError_t launch_verify_k(const DecodeArgs& a, dim3 grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   if (e0 && e1)
-    hipExtLaunchKernelGGL((verify_split_kernel<D, FP8>), grid, dim3(kVThreads), 0, st, e0, e1, 0, a);
+    hipExtLaunchKernelGGL((verify_split_kernel<D, FP8, PF>), grid, dim3(kVThreads), 0, st, e0, e1, 0, a);
   else
-    hipLaunchKernelGGL((verify_split_kernel<D, FP8>), grid, dim3(kVThreads), 0, st, a);
+    hipLaunchKernelGGL((verify_split_kernel<D, FP8, PF>), grid, dim3(kVThreads), 0, st, a);
   return hipGetLastError();
+}
+
+template <bool PF>
+hipError_t launch_verify_any(const DecodeArgs& a, int head_dim, dim3 grid, hipStream_t st, hipEvent_t e0,
+                             hipEvent_t e1) {
+  if (head_dim == 256)
+    return a.kv_fp8 ? launch_verify_k<256, true, PF>(a, grid, st, e0, e1)
+                    : launch_verify_k<256, false, PF>(a, grid, st, e0, e1);
+  return a.kv_fp8 ? launch_verify_k<128, true, PF>(a, grid, st, e0, e1)
+                  : launch_verify_k<128, false, PF>(a, grid, st, e0, e1);
 }
 
 }  // namespace
@@ -340,9 +371,17 @@ hipError_t launch_verify_split(const DecodeArgs& a, int head_dim, int group, hip
                                hipEvent_t e1) {
   if (!verify_supported(head_dim, group, a.q_len)) return hipErrorInvalidValue;
   dim3 grid(a.num_splits, a.hkv, a.num_seqs);
-  if (head_dim == 256)
-    return a.kv_fp8 ? launch_verify_k<256, true>(a, grid, st, e0, e1) : launch_verify_k<256, false>(a, grid, st, e0, e1);
-  return a.kv_fp8 ? launch_verify_k<128, true>(a, grid, st, e0, e1) : launch_verify_k<128, false>(a, grid, st, e0, e1);
+  return launch_verify_any<false>(a, head_dim, grid, st, e0, e1);
+}
+
+hipError_t launch_prefill(const DecodeArgs& a, int head_dim, int group, hipStream_t st, hipEvent_t e0,
+                          hipEvent_t e1) {
+  // A block holds pf_rows positions of all `group` heads: at most 128 MFMA rows.
+  if ((head_dim != 128 && head_dim != 256) || group < 1 || a.pf_rows < 1 ||
+      group * a.pf_rows > kVWaves * kRowsPerWave)
+    return hipErrorInvalidValue;
+  dim3 grid((a.q_len + a.pf_rows - 1) / a.pf_rows, a.hkv, a.num_seqs);
+  return launch_verify_any<true>(a, head_dim, grid, st, e0, e1);
 }
 
 }  // namespace pkv

@@ -296,6 +296,32 @@ def batched_verify(num_seqs: int = 32, max_rows: int = 5, lo: int = 512, hi: int
     return case, q, cu
 
 
+def chunked_prefill(chunk: int = 4096, context: int = 8192, block_size: int = 784,
+                    **kw) -> tuple[DecodeCase, np.ndarray, np.ndarray]:
+    """One prompt chunk: `chunk` new query rows whose K/V are the last `chunk`
+    tokens of a `context`-token cache (the earlier tokens are the prefix that
+    previous chunks left), 24/4/256, page 784. The default is the second
+    4096-row chunk of an 8192-token prompt. Returns (case, packed q, cu_seqlens_q)."""
+    case = make_case(1011, [context], q_len=chunk, block_size=block_size, boost_frac=0.05, **kw)
+    q, cu = pack_varlen(case, [chunk])
+    return case, q, cu
+
+
+def attention_flops(seq_lens, q_lens, num_q_heads: int, head_dim: int, *, window: int = 0) -> int:
+    """Algorithmic flops of a causal multi-row call: 4 * D per (query row, query
+    head, visible token), i.e. 2 * D for q.k and 2 * D for p.v. Row i of a
+    sequence with n new rows and L tokens sees L - n + i + 1 tokens (at most
+    `window` of them with a sliding window)."""
+    total = 0
+    for L, n in zip(np.asarray(seq_lens, dtype=np.int64).tolist(), np.asarray(q_lens, dtype=np.int64).tolist()):
+        vis = np.arange(L - n + 1, L + 1, dtype=np.int64)
+        vis = np.maximum(vis, 0)
+        if window > 0:
+            vis = np.minimum(vis, window)
+        total += int(vis.sum())
+    return int(4 * head_dim * num_q_heads * total)
+
+
 def dense_control(context: int = 32768, **kw) -> DecodeCase:
     """Batch 1, q_len 1, 32 query heads, 8 KV heads, head_dim 128, page 16."""
     return make_case(1006, [context], num_q_heads=32, num_kv_heads=8, head_dim=128,

@@ -97,3 +97,26 @@ def run_gpu_varlen(case, q_packed, cu, *, out=None, workspace=None, **kw):
                                    workspace=workspace, **kv_kwargs(case), **kw)
     torch.cuda.synchronize()
     return got.float().cpu().numpy().astype(np.float64), workspace
+
+
+def ref_without_tokens(case, b, q_rows, rows, drop):
+    """fp64 attention of rows `rows` (indices into q_rows [n, Hq, D], the n new
+    rows of sequence b) over their causal prefixes with the tokens in the
+    boolean mask `drop` removed (a bf16 case; skipped-page checks)."""
+    import oracle.paged_attention as O
+    n, hq = q_rows.shape[0], q_rows.shape[1]
+    hkv = case.k_cache.shape[2]
+    G = hq // hkv
+    L = int(case.seq_lens[b])
+    sig = float(np.float32(case.scale))
+    out = np.zeros((len(rows), hq, q_rows.shape[2]))
+    for r, i in enumerate(rows):
+        pos = L - n + i
+        keep = ~np.asarray(drop[:pos + 1])
+        for h in range(hq):
+            K = O.bf16_bits_to_f64(case.logical_k[b][:pos + 1][keep, h // G])
+            V = O.bf16_bits_to_f64(case.logical_v[b][:pos + 1][keep, h // G])
+            s = sig * (K @ O.bf16_bits_to_f64(q_rows[i, h]))
+            e = np.exp(s - s.max())
+            out[r, h] = e @ V / e.sum()
+    return out

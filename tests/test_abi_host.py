@@ -11,6 +11,7 @@ import pytest
 import oracle.paged_attention as O
 import paged_kv_cache_08_amd as P
 from paged_kv_cache_08_amd import binding as Bn
+from paged_kv_cache_08_amd import workloads as W
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "pkv.h")
 
@@ -87,6 +88,45 @@ def params(**kw):
 ])
 def test_validation_codes(kw, code):
     assert P.validate(params(**kw)) == code
+
+
+def _prefill(p, ws_bytes=256, ptr=0):
+    """The prefill entry with fake device pointers: argument checks run on the
+    host before anything touches the device, so only error codes are tested."""
+    f = P.lib().pkv_paged_prefill_attention
+    import ctypes
+    a = ptr or None
+    return f(ctypes.byref(p), a, a, a, a, a, a, a, a, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({"q_len": 4096}, -1),                      # valid shape: stops at the NULL pointers
+    ({"q_len": 1 << 24, "num_seqs": 2}, -1),
+    ({"q_len": (1 << 24) + 1}, -2),
+    ({"q_len": 1 << 24, "num_seqs": 200}, -2),  # above 2^31 - 1 rows
+    ({"q_len": 0}, -1),
+    ({"num_q_heads": 128, "num_kv_heads": 1, "q_len": 300}, -1),   # group 128: one position per block
+    ({"num_q_heads": 129, "num_kv_heads": 1, "q_len": 300}, -2),
+    ({"q_len": 4096, "window": 2048}, -1),
+    ({"q_len": 4096, "head_dim": 64}, -2),
+    ({"q_len": 4096, "kv_dtype": 1, "k_scale": -1.0, "v_scale": 1.0}, -1),
+])
+def test_prefill_validation_codes(kw, code):
+    assert _prefill(params(**kw)) == code
+
+
+def test_prefill_workspace_is_the_header():
+    # 256-byte-aligned fake pointers pass the pointer checks; a workspace below
+    # the header size is refused before any launch.
+    assert P.binding.PKV_PREFILL_WORKSPACE_BYTES == 256
+    assert _prefill(params(q_len=4096), ws_bytes=255, ptr=1 << 20) == -3
+
+
+def test_attention_flops_counts_visible_tokens():
+    # rows of a 3-row chunk ending at L = 5 see 3, 4, 5 tokens; with window 4: 3, 4, 4
+    assert W.attention_flops([5], [3], 2, 8) == 4 * 8 * 2 * 12
+    assert W.attention_flops([5], [3], 2, 8, window=4) == 4 * 8 * 2 * 11
+    assert W.attention_flops([5, 7], [0, 1], 1, 1) == 4 * 7
 
 
 def test_plan_constants_are_the_documented_ones():

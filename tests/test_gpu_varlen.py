@@ -1,12 +1,14 @@
 """GPU parity of the varlen multi-row call (per-sequence query rows through
 cu_seqlens_q, batched speculative verify) against the fp64 oracle, through the
 C ABI."""
+import dataclasses
+
 import numpy as np
 import pytest
 
 import oracle.paged_attention as O
 from paged_kv_cache_08_amd import workloads as W
-from tests.gpu_helpers import assert_matches_oracle, log, run_gpu, run_gpu_varlen
+from tests.gpu_helpers import assert_matches_oracle, log, ref_without_tokens, run_gpu, run_gpu_varlen
 
 pytestmark = pytest.mark.gpu
 
@@ -84,3 +86,22 @@ def test_inconsistent_row_counts_are_flagged_and_skipped():
     assert_matches_oracle(got[8:10], ref[8:10], "seq 2")
     assert np.all(got[3:8] == 7.0)
     assert bool(torch.all(full[q.shape[0]:] == 7.0))
+
+
+def test_invalid_table_entry_is_skipped_and_flagged():
+    import torch
+    import paged_kv_cache_08_amd as P
+    # Sequence 1's page 2 (tokens 32..47, page 16) points outside the pool:
+    # bit 0 is set, sequence 1's rows skip those tokens, sequence 0 is untouched.
+    log("case: varlen rows [3, 4], lengths [300, 90], page 16, one out-of-range entry")
+    case = W.make_case(979, [300, 90], q_len=4, block_size=16, poison=False)
+    q, cu = W.pack_varlen(case, [3, 4])
+    bad = case.block_table.copy()
+    bad[1, 2] = case.num_pages + 1
+    case_bad = dataclasses.replace(case, block_table=bad)
+    got, ws = run_gpu_varlen(case_bad, q, cu)
+    assert P.read_error_word(ws) & 1
+    assert_matches_oracle(got[:3], oracle_varlen(case, q, cu)[:3], "sequence 0")
+    drop = np.zeros(90, bool)
+    drop[32:48] = True
+    assert_matches_oracle(got[3:], ref_without_tokens(case, 1, q[3:], [0, 1, 2, 3], drop), "sequence 1 without page 2")

@@ -5,7 +5,7 @@ import pytest
 
 import oracle.paged_attention as O
 from paged_kv_cache_08_amd import workloads as W
-from tests.gpu_helpers import assert_matches_oracle, log, run_gpu
+from tests.gpu_helpers import assert_matches_oracle, log, ref_without_tokens, run_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -102,3 +102,25 @@ def test_late_dominant_keys_move_the_softmax_reference(ql):
         case.k_cache[page, off] = W.f32_to_bf16_bits(rows.view(np.float32) * np.float32(16.0))
     assert_matches_oracle(run_gpu(case, num_splits=1), oracle_out(case), f"late keys q{ql}")
     assert_matches_oracle(run_gpu(case), oracle_out(case), f"late keys q{ql} planned")
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_invalid_table_entry_is_skipped_and_flagged(splits):
+    import torch
+    import paged_kv_cache_08_amd as P
+    # Page 8 (tokens 128..143) points outside the pool: bit 0 of the error word
+    # is set and every row attends to all of its tokens but those 16.
+    log(f"case: verify q8 on 200 tokens, page 16, one out-of-range entry, {splits} splits")
+    case = W.make_case(960 + splits, [200], q_len=8, block_size=16, poison=False)
+    q, k, v, table, lens = to_device(case)
+    table[0, 8] = case.num_pages + 3
+    p = P.make_params(q, k, v, table, 16, case.scale, max_seq_len=200, num_splits=splits)
+    ws = torch.zeros(P.workspace_bytes(p, 0), dtype=torch.uint8, device="cuda")
+    out = P.paged_decode_attention(q, k, v, table, lens, 16, case.scale, max_seq_len=200, num_splits=splits,
+                                   workspace=ws)
+    torch.cuda.synchronize()
+    assert P.read_error_word(ws) & 1
+    drop = np.zeros(200, bool)
+    drop[128:144] = True
+    ref = ref_without_tokens(case, 0, case.q[0], list(range(8)), drop)
+    assert_matches_oracle(out[0].cpu().numpy().astype(np.float64), ref, f"verify without page 8 S={splits}")
