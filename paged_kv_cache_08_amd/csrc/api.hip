@@ -209,6 +209,9 @@ int validate_prefill(const pkv_decode_params* p) {
     return fail(PKV_ERR_UNSUPPORTED, "prefill calls need Hq / Hkv <= 128");
   if (int64_t(p->num_seqs) * p->q_len > (int64_t(1) << 31) - 1)
     return fail(PKV_ERR_UNSUPPORTED, "num_seqs * q_len above 2^31 - 1 rows");
+  const int32_t pf = prefill_rows(p);
+  if ((int64_t(p->q_len) + pf - 1) / pf * p->num_kv_heads * p->num_seqs > (int64_t(1) << 31) - 1)
+    return fail(PKV_ERR_UNSUPPORTED, "more than 2^31 - 1 prefill blocks");
   return PKV_OK;
 }
 

@@ -208,24 +208,6 @@ __device__ __forceinline__ SplitSpan prefill_span(const DecodeArgs& a, int b, in
   return r;
 }
 
-// Element offsets of token t's K and V rows read straight from the block
-// table (no LDS staging); false if its entry is outside [0, num_pages), which
-// also sets bit 0 of the workspace error word.
-__device__ __forceinline__ bool token_row_global(const DecodeArgs& a, int b, int g, int t, int64_t& ko,
-                                                 int64_t& vo) {
-  const uint32_t pg = magic_div(uint32_t(t), a.bdiv);
-  const int off = t - int(pg * a.bdiv.d);
-  const int e = a.table[int64_t(b) * a.max_pages + pg];
-  if (uint32_t(e) >= uint32_t(a.num_pages)) {
-    if (a.err) atomicOr(a.err, 1u);
-    ko = vo = 0;
-    return false;
-  }
-  ko = int64_t(e) * a.k_sp + int64_t(g) * a.k_sh + int64_t(off * int32_t(a.k_st));
-  vo = int64_t(e) * a.v_sp + int64_t(g) * a.v_sh + int64_t(off * int32_t(a.v_st));
-  return true;
-}
-
 // Element offsets of token t's K and V rows; false if its page entry is
 // invalid. The in-page part off * stride_tok fits 32 bits (checked on the host).
 __device__ __forceinline__ bool token_row(const DecodeArgs& a, const PageOffs* tbl, int p_first, int t,

@@ -12,7 +12,7 @@
 //
 // Workgroup = one split (<= 512 tokens) of one (sequence, KV head), 8 waves.
 //   * All 8 waves stage 64-token K and V tiles into LDS (double buffered, rows
-//     padded to 528 bytes) with 16-byte loads through the block table; FP8
+//     padded to 544 bytes for D = 256) with 16-byte loads through the block table; FP8
 //     caches are decoded to bf16 (exactly) on the way into LDS.
 //   * Wave w owns query rows f = 16w .. 16w + 15 of the flattened
 //     (head, position) list, head-major (f = h_local * q_len + i); waves past
@@ -65,13 +65,33 @@ __device__ __forceinline__ uint32_t bf16_pair(float x, float y) {
 // rescale of O.
 constexpr float kLazyMax = 8.0f;
 
-// PF (prefill): blockIdx.x is a block of a.pf_rows query positions instead
-// of a KV split; the block covers its whole visible range in one pass and
-// reads block-table entries from global memory (the range can exceed what the
-// LDS table holds).
+// Stand-in 16-byte chunks for tokens a tile must not count (past its range,
+// or behind an invalid table entry): keys are NaN (bf16 NaN pairs; FP8 E4M3FN
+// NaN codes), so such a token's score is NaN and the score filter drops it,
+// and values are zero, so nothing reaches O.
+__device__ __attribute__((aligned(16))) const uint32_t kMaskedKey[2][4] = {
+    {0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u}, {0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu}};
+__device__ __attribute__((aligned(16))) const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
+
+// Padding of an LDS token row: for D = 256, 32 bytes shift consecutive rows
+// by 8 banks, which suits the transposed V reads (4 lanes x 8 bytes per row)
+// better than 16 (measured: about 5% on prefill blocks, neutral on verify).
+// D = 128 keeps 16 so that two workgroups still fit in one CU's LDS.
+template <int D>
+constexpr int kRowPad = D >= 256 ? 32 : 16;
+
+// PF (prefill): the workgroup is a block of a.pf_rows query positions of one
+// (sequence, KV head) stream instead of a KV split, and covers its whole
+// visible range in one pass. The 1-D grid lists blocks largest first (the
+// last positions see the most tokens), each rank interleaved over all
+// streams: with workgroups dealt round-robin to the 8 XCDs, the blocks of one
+// stream stay on the same XCDs (shared L2) when the stream count divides 8
+// or 8 divides it, and every XCD gets a balanced share. Token offsets come
+// from the block table in global memory, one lane per token, staged in LDS
+// two tiles ahead (the range can exceed what the LDS table holds).
 template <int D, bool FP8, bool PF>
 __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a) {
-  constexpr int kPitch = D * 2 + 16;              // LDS bytes per token row (padded)
+  constexpr int kPitch = D * 2 + kRowPad<D>;         // LDS bytes per token row (padded)
   constexpr int kElems = FP8 ? 16 : 8;            // elements per 16-byte chunk of a cache row
   constexpr int kChunks = D / kElems;             // 16-byte chunks per row
   constexpr int kLoads = kVTile * kChunks / kVThreads;   // K (and V) chunks per thread per tile
@@ -80,20 +100,34 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
   static_assert(kLoads >= 1 && kVTile * kChunks % kVThreads == 0, "tile must split evenly");
 
   __shared__ __attribute__((aligned(16))) uint8_t kv[2][2][kVTile * kPitch];
-  __shared__ PageOffs tbl[kMaxChunk + 2];
-  __shared__ __attribute__((aligned(4))) uint8_t tok_ok[2][kVTile];   // token's table entry valid
+  __shared__ PageOffs tbl[PF ? 1 : kMaxChunk + 2];   // PF reads the table from global memory
+  // PF: K and V offsets of a tile's tokens (-1: none), a ring of 3 tiles: the
+  // tile being computed (its skipped-page mask), the one being loaded and the
+  // one being staged.
+  __shared__ __attribute__((aligned(16))) int64_t toff[PF ? 3 : 1][kVTile][2];
 
-  const int s = PF ? 0 : blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  int p0 = 0;                                     // PF: first query position of the block
+  bool lead = s == 0;                             // reports inconsistent rows of the stream
+  if constexpr (PF) {
+    const int streams = a.hkv * a.num_seqs;
+    const int rank = int(blockIdx.x) / streams, stream = int(blockIdx.x) - rank * streams;
+    const int nblk = (a.q_len + a.pf_rows - 1) / a.pf_rows;
+    g = stream % a.hkv;
+    b = stream / a.hkv;
+    s = 0;
+    p0 = (nblk - 1 - rank) * a.pf_rows;
+    lead = rank == 0;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 4, ln = lane & 15;
   const QRows qr = seq_q_rows(a, b);
-  const int p0 = PF ? blockIdx.x * a.pf_rows : 0;          // first query position of the block
   const int q_len = PF ? min(a.pf_rows, qr.n - p0) : qr.n;   // query rows of this workgroup
   const int row_base = qr.base + p0;
   const int G = a.hq / a.hkv;
   const int R = G * q_len;                        // rows of this KV head (<= 128)
   if (q_len <= 0) {                               // no rows, or inconsistent cu_seqlens_q
-    if (!qr.ok && blockIdx.x == 0 && g == 0 && tid == 0 && a.err) atomicOr(a.err, 2u);
+    if (!qr.ok && lead && g == 0 && tid == 0 && a.err) atomicOr(a.err, 2u);
     return;
   }
   SplitPages pages{0, 0};
@@ -150,7 +184,6 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
 
   // Tile staging: thread tid moves chunks c = tid + kVThreads * k of K and V.
   u32x4_t stk[kLoads], stv[kLoads];   // native vectors: kept in registers
-  bool okt[kLoads];                   // FP8: the chunk belongs to a live token
   auto load_tile = [&](int tile) __attribute__((always_inline)) {
     static_for<0, kLoads>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
@@ -160,30 +193,29 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
       const int tc = min(t, sp.end - 1);
       int64_t ko, vo;
       bool ok;
-      if constexpr (PF)
-        ok = token_row_global(a, b, g, tc, ko, vo) && t < sp.end;
-      else
-        ok = token_row(a, tbl, p_first, tc, ko, vo) && t < sp.end;
-      okt[k] = ok;
-      if constexpr (FP8) {   // element offsets are byte offsets
-        const uint8_t* kp = ok ? reinterpret_cast<const uint8_t*>(a.k) + ko + piece * 16
-                               : reinterpret_cast<const uint8_t*>(a.q);
-        const uint8_t* vp = ok ? reinterpret_cast<const uint8_t*>(a.v) + vo + piece * 16
-                               : reinterpret_cast<const uint8_t*>(a.q);
-        stk[k] = *reinterpret_cast<const u32x4_t*>(kp);
-        stv[k] = *reinterpret_cast<const u32x4_t*>(vp);
+      if constexpr (PF) {
+        const int64_t* to = toff[tile % 3][tt];
+        ko = to[0];
+        vo = to[1];
+        ok = ko >= 0;
+        (void)tc;
       } else {
-        const uint16_t* kp = ok ? a.k + ko + piece * 8 : a.q;   // masked rows read q (finite)
-        const uint16_t* vp = ok ? a.v + vo + piece * 8 : a.q;
-        stk[k] = *reinterpret_cast<const u32x4_t*>(kp);
-        stv[k] = *reinterpret_cast<const u32x4_t*>(vp);
+        ok = token_row(a, tbl, p_first, tc, ko, vo) && t < sp.end;
       }
+      // Tokens that must not count read the stand-in chunks (NaN keys, zero values).
+      // (Element offsets are byte offsets for FP8 caches.)
+      const uint8_t* kb = reinterpret_cast<const uint8_t*>(a.k) + (FP8 ? ko : 2 * ko);
+      const uint8_t* vb = reinterpret_cast<const uint8_t*>(a.v) + (FP8 ? vo : 2 * vo);
+      const u32x4_t* kp = ok ? reinterpret_cast<const u32x4_t*>(kb) + piece
+                             : reinterpret_cast<const u32x4_t*>(kMaskedKey[FP8 ? 1 : 0]);
+      const u32x4_t* vp = ok ? reinterpret_cast<const u32x4_t*>(vb) + piece
+                             : reinterpret_cast<const u32x4_t*>(kZeroChunk);
+      stk[k] = *kp;
+      stv[k] = *vp;
     });
   };
-  // FP8: 16 codes -> 16 exact bf16 values (32 bytes); a masked chunk read the
-  // q row, whose bytes may decode to NaN, so it becomes zeros.
-  auto fp8_to_bf16 = [&](const u32x4_t& w, bool ok, u32x4_t& lo, u32x4_t& hi) __attribute__((always_inline)) {
-    const uint32_t x[4] = {ok ? w[0] : 0u, ok ? w[1] : 0u, ok ? w[2] : 0u, ok ? w[3] : 0u};
+  // FP8: 16 codes -> 16 exact bf16 values (32 bytes).
+  auto fp8_to_bf16 = [&](const u32x4_t& x, u32x4_t& lo, u32x4_t& hi) __attribute__((always_inline)) {
     lo = u32x4_t{fp8x2_to_bf16x2<false>(x[0]), fp8x2_to_bf16x2<true>(x[0]),
                  fp8x2_to_bf16x2<false>(x[1]), fp8x2_to_bf16x2<true>(x[1])};
     hi = u32x4_t{fp8x2_to_bf16x2<false>(x[2]), fp8x2_to_bf16x2<true>(x[2]),
@@ -194,13 +226,12 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
       constexpr int k = decltype(kc)::value;
       const int c = tid + kVThreads * k;
       const int tt = c / kChunks, piece = c - tt * kChunks;
-      if (piece == 0) tok_ok[buf][tt] = okt[k];
       if constexpr (FP8) {
         u32x4_t lo, hi;
-        fp8_to_bf16(stk[k], okt[k], lo, hi);
+        fp8_to_bf16(stk[k], lo, hi);
         *reinterpret_cast<u32x4_t*>(&kv[buf][0][tt * kPitch + piece * 32]) = lo;
         *reinterpret_cast<u32x4_t*>(&kv[buf][0][tt * kPitch + piece * 32 + 16]) = hi;
-        fp8_to_bf16(stv[k], okt[k], lo, hi);
+        fp8_to_bf16(stv[k], lo, hi);
         *reinterpret_cast<u32x4_t*>(&kv[buf][1][tt * kPitch + piece * 32]) = lo;
         *reinterpret_cast<u32x4_t*>(&kv[buf][1][tt * kPitch + piece * 32 + 16]) = hi;
       } else {
@@ -210,13 +241,53 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
     });
   };
 
+  // PF token offsets: lane `tid` (wave 0) fetches the table entry of token
+  // tid of a tile early and writes the offsets after the tile's compute, so
+  // its wait on the entry does not also wait on that tile's K/V loads.
+  int pf_entry = 0;
+  bool pf_bad = false;                            // an entry outside [0, num_pages) was met
+  auto fetch_entry = [&](int tile) __attribute__((always_inline)) {
+    if constexpr (PF) {
+      const int t = sp.begin + tile * kVTile + tid;
+      if (tid < kVTile && t < sp.end)
+        pf_entry = a.table[int64_t(b) * a.max_pages + magic_div(uint32_t(t), a.bdiv)];
+    }
+  };
+  auto commit_offsets = [&](int tile) __attribute__((always_inline)) {
+    if constexpr (PF) {
+      if (tid < kVTile) {
+        const int t = sp.begin + tile * kVTile + tid;
+        int64_t ko = -1, vo = -1;
+        if (t < sp.end) {
+          const int off = t - int(magic_div(uint32_t(t), a.bdiv) * a.bdiv.d);
+          if (uint32_t(pf_entry) < uint32_t(a.num_pages)) {
+            ko = int64_t(pf_entry) * a.k_sp + int64_t(g) * a.k_sh + int64_t(off * int32_t(a.k_st));
+            vo = int64_t(pf_entry) * a.v_sp + int64_t(g) * a.v_sh + int64_t(off * int32_t(a.v_st));
+          } else {
+            pf_bad = true;
+          }
+        }
+        toff[tile % 3][tid][0] = ko;
+        toff[tile % 3][tid][1] = vo;
+      }
+    }
+  };
+
   const int n_tiles = (sp.end - sp.begin + kVTile - 1) / kVTile;
+  if constexpr (PF) {
+    fetch_entry(0);
+    commit_offsets(0);
+    fetch_entry(1);
+    commit_offsets(1);
+    __syncthreads();
+  }
   load_tile(0);
   store_tile(0);
   __syncthreads();
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int buf = tile & 1;
     const bool more = tile + 1 < n_tiles;
+    fetch_entry(tile + 2);
     if (more) load_tile(tile + 1);
     if (computes) {
       const uint8_t* kb = kv[buf][0];
@@ -231,22 +302,22 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
           st[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr), as_bf16x8(qreg[kk]), st[tb], 0, 0, 0);
         }
       }
-      // Scale, causal / range / skipped-page mask, tile max of row ln.
+      // Scale, causal / window mask, tile max of row ln. Tokens past the
+      // split or behind an invalid table entry were staged with NaN keys:
+      // their scores are NaN and fail the s == s test.
       const int t0 = sp.begin + tile * kVTile + 4 * grp;
       float mt = -INFINITY;
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const uint32_t okw = *reinterpret_cast<const uint32_t*>(&tok_ok[buf][tb * 16 + 4 * grp]);
+      for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = t0 + tb * 16 + r;
-          const bool vis = row_valid && ((okw >> (8 * r)) & 0xffu) != 0 && t <= pos_row &&
-                           (a.window == 0 || t > pos_row - a.window);
-          const float x = vis ? st[tb][r] * a.scale_log2 : -INFINITY;
+          const float sc = st[tb][r];
+          const bool vis = row_valid && sc == sc && t <= pos_row && (a.window == 0 || t > pos_row - a.window);
+          const float x = vis ? sc * a.scale_log2 : -INFINITY;
           st[tb][r] = x;
           mt = fmaxf(mt, x);
         }
-      }
       mt = fmaxf(mt, __shfl_xor(mt, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
       const float m_new = mt > m_run + kLazyMax ? mt : m_run;
@@ -310,8 +381,10 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
       });
     }
     if (more) store_tile(buf ^ 1);
+    commit_offsets(tile + 2);   // slot (tile + 2) % 3 was last read in the previous iteration
     __syncthreads();
   }
+  if (PF && pf_bad && a.err) atomicOr(a.err, 1u);
 
   if (!computes) return;
   // Rows 4 grp + r of O; their (max, sum) are held by lane 4 grp + r of each group.
@@ -380,7 +453,9 @@ hipError_t launch_prefill(const DecodeArgs& a, int head_dim, int group, hipStrea
   if ((head_dim != 128 && head_dim != 256) || group < 1 || a.pf_rows < 1 ||
       group * a.pf_rows > kVWaves * kRowsPerWave)
     return hipErrorInvalidValue;
-  dim3 grid((a.q_len + a.pf_rows - 1) / a.pf_rows, a.hkv, a.num_seqs);
+  const int64_t blocks = int64_t((a.q_len + a.pf_rows - 1) / a.pf_rows) * a.hkv * a.num_seqs;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid(uint32_t(blocks), 1, 1);
   return launch_verify_any<true>(a, head_dim, grid, st, e0, e1);
 }
 
