@@ -65,13 +65,25 @@ __device__ __forceinline__ uint32_t bf16_pair(float x, float y) {
 // rescale of O.
 constexpr float kLazyMax = 8.0f;
 
-// Stand-in 16-byte chunks for tokens a tile must not count (past its range,
-// or behind an invalid table entry): keys are NaN (bf16 NaN pairs; FP8 E4M3FN
-// NaN codes), so such a token's score is NaN and the score filter drops it,
-// and values are zero, so nothing reaches O.
-__device__ __attribute__((aligned(16))) const uint32_t kMaskedKey[2][4] = {
-    {0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u}, {0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu}};
-__device__ __attribute__((aligned(16))) const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
+// Stand-in K/V rows (up to 512 bytes) for tokens a tile must not count (past
+// its range, or behind an invalid table entry): keys are NaN (bf16 NaN pairs;
+// FP8 E4M3FN NaN codes), so such a token's score is NaN and the score filter
+// drops it, and values are zero, so nothing reaches O.
+struct StandInRows {
+  uint32_t nan_key[2][128];   // [bf16, FP8]
+  uint32_t zero[128];
+};
+constexpr StandInRows make_stand_in_rows() {
+  StandInRows r{};
+  for (int i = 0; i < 128; ++i) {
+    r.nan_key[0][i] = 0x7fc07fc0u;
+    r.nan_key[1][i] = 0x7f7f7f7fu;
+    r.zero[i] = 0u;
+  }
+  return r;
+}
+__device__ __attribute__((aligned(16))) const StandInRows kStandIn = make_stand_in_rows();
+constexpr uint32_t kNanBf16Pair = 0x7fc07fc0u;
 
 // Padding of an LDS token row: for D = 256, 32 bytes shift consecutive rows
 // by 8 banks, which suits the transposed V reads (4 lanes x 8 bytes per row)
@@ -101,9 +113,8 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
 
   __shared__ __attribute__((aligned(16))) uint8_t kv[2][2][kVTile * kPitch];
   __shared__ PageOffs tbl[PF ? 1 : kMaxChunk + 2];   // PF reads the table from global memory
-  // PF: K and V offsets of a tile's tokens (-1: none), a ring of 3 tiles: the
-  // tile being computed (its skipped-page mask), the one being loaded and the
-  // one being staged.
+  // PF: K and V byte offsets of a tile's tokens, a ring of 3 tiles (the one
+  // being loaded, the next one, and the one being staged).
   __shared__ __attribute__((aligned(16))) int64_t toff[PF ? 3 : 1][kVTile][2];
 
   int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -166,13 +177,14 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
   const int pos_row = sp.L - q_len + i_row;      // last visible token of the row
 
   // Q of row ln, as the B operand of S^T: k step kk holds d = 32 kk + 8 grp .. +8.
+  // Padding rows hold NaN, so all their scores fail the score filter.
   uint4 qreg[kKSteps];
   {
     const int64_t qoff = ((int64_t(row_base) + i_row) * a.hq + int64_t(g) * G + h_row) * D + 8 * grp;
 #pragma unroll
     for (int kk = 0; kk < kKSteps; ++kk)
       qreg[kk] = (computes && row_valid) ? *reinterpret_cast<const uint4*>(a.q + qoff + 32 * kk)
-                                         : make_uint4(0, 0, 0, 0);
+                                         : make_uint4(kNanBf16Pair, kNanBf16Pair, kNanBf16Pair, kNanBf16Pair);
   }
   __syncthreads();   // table staged
   if constexpr (!PF) flag_invalid_entries(a, tbl, int(magic_div(uint32_t(sp.end - 1), a.bdiv)) - p_first + 1);
@@ -191,25 +203,23 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
       const int tt = c / kChunks, piece = c - tt * kChunks;
       const int t = sp.begin + tile * kVTile + tt;
       const int tc = min(t, sp.end - 1);
-      int64_t ko, vo;
-      bool ok;
-      if constexpr (PF) {
+      const u32x4_t *kp, *vp;
+      if constexpr (PF) {   // staged byte offsets, stand-in rows included
         const int64_t* to = toff[tile % 3][tt];
-        ko = to[0];
-        vo = to[1];
-        ok = ko >= 0;
+        kp = reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint8_t*>(a.k) + to[0]) + piece;
+        vp = reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint8_t*>(a.v) + to[1]) + piece;
         (void)tc;
       } else {
-        ok = token_row(a, tbl, p_first, tc, ko, vo) && t < sp.end;
+        int64_t ko, vo;
+        const bool ok = token_row(a, tbl, p_first, tc, ko, vo) && t < sp.end;
+        // Tokens that must not count read the stand-in rows (NaN keys, zero
+        // values). Element offsets are byte offsets for FP8 caches.
+        const uint8_t* kb = reinterpret_cast<const uint8_t*>(a.k) + (FP8 ? ko : 2 * ko);
+        const uint8_t* vb = reinterpret_cast<const uint8_t*>(a.v) + (FP8 ? vo : 2 * vo);
+        kp = ok ? reinterpret_cast<const u32x4_t*>(kb) + piece
+                : reinterpret_cast<const u32x4_t*>(kStandIn.nan_key[FP8 ? 1 : 0]);
+        vp = ok ? reinterpret_cast<const u32x4_t*>(vb) + piece : reinterpret_cast<const u32x4_t*>(kStandIn.zero);
       }
-      // Tokens that must not count read the stand-in chunks (NaN keys, zero values).
-      // (Element offsets are byte offsets for FP8 caches.)
-      const uint8_t* kb = reinterpret_cast<const uint8_t*>(a.k) + (FP8 ? ko : 2 * ko);
-      const uint8_t* vb = reinterpret_cast<const uint8_t*>(a.v) + (FP8 ? vo : 2 * vo);
-      const u32x4_t* kp = ok ? reinterpret_cast<const u32x4_t*>(kb) + piece
-                             : reinterpret_cast<const u32x4_t*>(kMaskedKey[FP8 ? 1 : 0]);
-      const u32x4_t* vp = ok ? reinterpret_cast<const u32x4_t*>(vb) + piece
-                             : reinterpret_cast<const u32x4_t*>(kZeroChunk);
       stk[k] = *kp;
       stv[k] = *vp;
     });
@@ -257,12 +267,17 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
     if constexpr (PF) {
       if (tid < kVTile) {
         const int t = sp.begin + tile * kVTile + tid;
-        int64_t ko = -1, vo = -1;
+        // Byte offsets from a.k / a.v; tokens that must not count point at
+        // the stand-in rows.
+        int64_t ko = int64_t(reinterpret_cast<uintptr_t>(kStandIn.nan_key[FP8 ? 1 : 0]) -
+                             reinterpret_cast<uintptr_t>(a.k));
+        int64_t vo = int64_t(reinterpret_cast<uintptr_t>(kStandIn.zero) - reinterpret_cast<uintptr_t>(a.v));
         if (t < sp.end) {
           const int off = t - int(magic_div(uint32_t(t), a.bdiv) * a.bdiv.d);
           if (uint32_t(pf_entry) < uint32_t(a.num_pages)) {
-            ko = int64_t(pf_entry) * a.k_sp + int64_t(g) * a.k_sh + int64_t(off * int32_t(a.k_st));
-            vo = int64_t(pf_entry) * a.v_sp + int64_t(g) * a.v_sh + int64_t(off * int32_t(a.v_st));
+            constexpr int kEb = FP8 ? 1 : 2;   // bytes per element
+            ko = (int64_t(pf_entry) * a.k_sp + int64_t(g) * a.k_sh + int64_t(off * int32_t(a.k_st))) * kEb;
+            vo = (int64_t(pf_entry) * a.v_sp + int64_t(g) * a.v_sh + int64_t(off * int32_t(a.v_st))) * kEb;
           } else {
             pf_bad = true;
           }
@@ -305,15 +320,19 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
       // Scale, causal / window mask, tile max of row ln. Tokens past the
       // split or behind an invalid table entry were staged with NaN keys:
       // their scores are NaN and fail the s == s test.
-      const int t0 = sp.begin + tile * kVTile + 4 * grp;
+      // Token (tile start + 4 grp + c) is visible to the row when c <= dist
+      // and c > wdist (dist clamped at -1: nothing visible; a window of 2^30
+      // or more covers every position).
+      const int dist = max(pos_row - (sp.begin + tile * kVTile + 4 * grp), -1);
+      const int wdist = (a.window > 0 && a.window < (1 << 30)) ? dist - a.window : -(1 << 30) - 2;
       float mt = -INFINITY;
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int t = t0 + tb * 16 + r;
+          const int c = tb * 16 + r;
           const float sc = st[tb][r];
-          const bool vis = row_valid && sc == sc && t <= pos_row && (a.window == 0 || t > pos_row - a.window);
+          const bool vis = sc == sc && c <= dist && c > wdist;
           const float x = vis ? sc * a.scale_log2 : -INFINITY;
           st[tb][r] = x;
           mt = fmaxf(mt, x);
