@@ -113,9 +113,9 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
 
   __shared__ __attribute__((aligned(16))) uint8_t kv[2][2][kVTile * kPitch];
   __shared__ PageOffs tbl[PF ? 1 : kMaxChunk + 2];   // PF reads the table from global memory
-  // PF: K and V byte offsets of a tile's tokens, a ring of 3 tiles (the one
-  // being loaded, the next one, and the one being staged).
-  __shared__ __attribute__((aligned(16))) int64_t toff[PF ? 3 : 1][kVTile][2];
+  // K and V byte offsets of a tile's tokens, a ring of 3 tiles (the one being
+  // loaded, the next one, and the one being staged).
+  __shared__ __attribute__((aligned(16))) int64_t toff[3][kVTile][2];
 
   int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   int p0 = 0;                                     // PF: first query position of the block
@@ -201,27 +201,10 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
       constexpr int k = decltype(kc)::value;
       const int c = tid + kVThreads * k;
       const int tt = c / kChunks, piece = c - tt * kChunks;
-      const int t = sp.begin + tile * kVTile + tt;
-      const int tc = min(t, sp.end - 1);
-      const u32x4_t *kp, *vp;
-      if constexpr (PF) {   // staged byte offsets, stand-in rows included
-        const int64_t* to = toff[tile % 3][tt];
-        kp = reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint8_t*>(a.k) + to[0]) + piece;
-        vp = reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint8_t*>(a.v) + to[1]) + piece;
-        (void)tc;
-      } else {
-        int64_t ko, vo;
-        const bool ok = token_row(a, tbl, p_first, tc, ko, vo) && t < sp.end;
-        // Tokens that must not count read the stand-in rows (NaN keys, zero
-        // values). Element offsets are byte offsets for FP8 caches.
-        const uint8_t* kb = reinterpret_cast<const uint8_t*>(a.k) + (FP8 ? ko : 2 * ko);
-        const uint8_t* vb = reinterpret_cast<const uint8_t*>(a.v) + (FP8 ? vo : 2 * vo);
-        kp = ok ? reinterpret_cast<const u32x4_t*>(kb) + piece
-                : reinterpret_cast<const u32x4_t*>(kStandIn.nan_key[FP8 ? 1 : 0]);
-        vp = ok ? reinterpret_cast<const u32x4_t*>(vb) + piece : reinterpret_cast<const u32x4_t*>(kStandIn.zero);
-      }
-      stk[k] = *kp;
-      stv[k] = *vp;
+      // Staged byte offsets (stand-in rows for tokens that must not count).
+      const int64_t* to = toff[tile % 3][tt];
+      stk[k] = *(reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint8_t*>(a.k) + to[0]) + piece);
+      stv[k] = *(reinterpret_cast<const u32x4_t*>(reinterpret_cast<const uint8_t*>(a.v) + to[1]) + piece);
     });
   };
   // FP8: 16 codes -> 16 exact bf16 values (32 bytes).
@@ -251,9 +234,11 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
     });
   };
 
-  // PF token offsets: lane `tid` (wave 0) fetches the table entry of token
-  // tid of a tile early and writes the offsets after the tile's compute, so
-  // its wait on the entry does not also wait on that tile's K/V loads.
+  // Token offsets, one lane per token: lane `tid` (wave 0) stages token tid
+  // of a tile two tiles ahead. PF reads the block table from global memory:
+  // the entry is fetched early and the offsets written after the tile's
+  // compute, so its wait on the entry does not also wait on that tile's K/V
+  // loads. Otherwise the entry comes from the LDS table.
   int pf_entry = 0;
   bool pf_bad = false;                            // an entry outside [0, num_pages) was met
   auto fetch_entry = [&](int tile) __attribute__((always_inline)) {
@@ -264,38 +249,42 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
     }
   };
   auto commit_offsets = [&](int tile) __attribute__((always_inline)) {
-    if constexpr (PF) {
-      if (tid < kVTile) {
-        const int t = sp.begin + tile * kVTile + tid;
-        // Byte offsets from a.k / a.v; tokens that must not count point at
-        // the stand-in rows.
-        int64_t ko = int64_t(reinterpret_cast<uintptr_t>(kStandIn.nan_key[FP8 ? 1 : 0]) -
-                             reinterpret_cast<uintptr_t>(a.k));
-        int64_t vo = int64_t(reinterpret_cast<uintptr_t>(kStandIn.zero) - reinterpret_cast<uintptr_t>(a.v));
-        if (t < sp.end) {
+    if (tid < kVTile) {
+      constexpr int kEb = FP8 ? 1 : 2;   // bytes per element
+      const int t = sp.begin + tile * kVTile + tid;
+      // Byte offsets from a.k / a.v; tokens that must not count point at
+      // the stand-in rows.
+      int64_t ko = int64_t(reinterpret_cast<uintptr_t>(kStandIn.nan_key[FP8 ? 1 : 0]) -
+                           reinterpret_cast<uintptr_t>(a.k));
+      int64_t vo = int64_t(reinterpret_cast<uintptr_t>(kStandIn.zero) - reinterpret_cast<uintptr_t>(a.v));
+      if (t < sp.end) {
+        if constexpr (PF) {
           const int off = t - int(magic_div(uint32_t(t), a.bdiv) * a.bdiv.d);
           if (uint32_t(pf_entry) < uint32_t(a.num_pages)) {
-            constexpr int kEb = FP8 ? 1 : 2;   // bytes per element
             ko = (int64_t(pf_entry) * a.k_sp + int64_t(g) * a.k_sh + int64_t(off * int32_t(a.k_st))) * kEb;
             vo = (int64_t(pf_entry) * a.v_sp + int64_t(g) * a.v_sh + int64_t(off * int32_t(a.v_st))) * kEb;
           } else {
             pf_bad = true;
           }
+        } else {
+          int64_t ke, ve;
+          if (token_row(a, tbl, p_first, t, ke, ve)) {
+            ko = ke * kEb;
+            vo = ve * kEb;
+          }
         }
-        toff[tile % 3][tid][0] = ko;
-        toff[tile % 3][tid][1] = vo;
       }
+      toff[tile % 3][tid][0] = ko;
+      toff[tile % 3][tid][1] = vo;
     }
   };
 
   const int n_tiles = (sp.end - sp.begin + kVTile - 1) / kVTile;
-  if constexpr (PF) {
-    fetch_entry(0);
-    commit_offsets(0);
-    fetch_entry(1);
-    commit_offsets(1);
-    __syncthreads();
-  }
+  fetch_entry(0);
+  commit_offsets(0);
+  fetch_entry(1);
+  commit_offsets(1);
+  __syncthreads();
   load_tile(0);
   store_tile(0);
   __syncthreads();
