@@ -197,17 +197,33 @@ def _blas_threads() -> int:
         return int(os.environ.get("OMP_NUM_THREADS", "1"))
 
 
-def cpu_baseline(case, varlen, window, kv_bytes_per_call, seconds):
-    """The oracle as it stands, on the host cores, over whole calls of the same
-    workload until about `seconds` of CPU work has run."""
-    threads = _blas_threads()
+def _oracle_calls(case, varlen, window, seconds):
+    """Whole oracle calls until about `seconds` have run: (calls, seconds)."""
     n, t0 = 0, time.perf_counter()
     while True:
         oracle_call(case, varlen, window)
         n += 1
         el = time.perf_counter() - t0
         if el >= seconds or n >= 1000:
-            break
+            return n, el
+
+
+def cpu_baseline(case, varlen, window, kv_bytes_per_call, seconds):
+    """The oracle as it stands, on the host cores, over whole calls of the same
+    workload until about `seconds` of CPU work has run; then the same with
+    BLAS limited to one thread for a third of that time."""
+    threads = _blas_threads()
+    n, el = _oracle_calls(case, varlen, window, seconds)
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            n1, el1 = _oracle_calls(case, varlen, window, seconds / 3)
+        single = {"value": round(kv_bytes_per_call * n1 / el1 / 1e9, 3), "unit": "GB/s",
+                  "us_per_call": round(el1 / n1 * 1e6, 1), "cores": 1,
+                  "sample": f"{n1} full oracle calls, BLAS limited to 1 thread, {el1:.1f} s"}
+    except ImportError:
+        pass
     return {
         "value": round(kv_bytes_per_call * n / el / 1e9, 3),
         "unit": "GB/s",
@@ -217,6 +233,7 @@ def cpu_baseline(case, varlen, window, kv_bytes_per_call, seconds):
         "sample": f"{n} full oracle calls on the benchmark input (fp64 NumPy, BLAS threads={threads}), {el:.1f} s",
         "host_cpus": os.cpu_count(),
         "affinity_cpus": len(os.sched_getaffinity(0)),
+        "single_thread": single,
     }
 
 
@@ -433,6 +450,9 @@ def main():
             "variant": variant,
         },
         "us_per_step": round(ms_per_step * 1e3, 2),
+        # 16 full-attention layers make one decode step of the hybrid model;
+        # the pages quote per-step attention time for 16 such calls.
+        "us_per_hybrid_step_16_layers": round(16 * ms_per_step * 1e3, 1),
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 1),
         "us_per_step_regions": {"median": round(med, 2), "min": round(min(region_us), 2),
                                 "max": round(max(region_us), 2),

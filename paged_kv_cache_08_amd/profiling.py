@@ -11,6 +11,13 @@
         plain copy of known size in the same run (the largest
         __amd_rocclr_copyBuffer dispatch, which copies N bytes). The record is
         stored under KEY with the hash of the kernel sources it was taken on.
+
+    python -m paged_kv_cache_08_amd.profiling counters --kernel NAME DB...
+        Shader counters of kernel NAME from one or more --pmc runs (each with
+        GRBM_GUI_ACTIVE), averaged over dispatches, and the busy / utilisation
+        figures rocprofv3 derives from them (same expressions: SQ counters
+        summed over their instances, GRBM_GUI_ACTIVE the maximum over its
+        instances; 256 CUs, 1024 SIMDs, 32 wave slots per CU on MI355X).
 """
 from __future__ import annotations
 
@@ -66,6 +73,79 @@ def pmc_per_dispatch(path: str, counter: str) -> dict:
     for did, v in per.items():
         out[name[did]].append(v)
     return out
+
+
+CU_NUM = 256       # MI355X compute units
+SIMD_NUM = 1024    # 4 SIMDs per CU
+WAVE_SLOTS = 32    # wave slots per CU in rocprofv3's occupancy expression
+
+
+def pmc_dispatch_values(path: str, kernel: str) -> dict:
+    """{counter: [per-dispatch value, ...]} for dispatches of kernels whose
+    name contains `kernel`: SQ_* and other block counters summed over their
+    instances, GRBM_GUI_ACTIVE the maximum over its instances."""
+    con = _db(path)
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for did, nm, cn, cv in con.execute("select dispatch_id, name, counter_name, counter_value from pmc_events"):
+        if kernel in nm:
+            per[cn][did].append(cv or 0.0)
+    out = {}
+    for cn, d in per.items():
+        red = max if cn == "GRBM_GUI_ACTIVE" else sum
+        out[cn] = [red(v) for v in d.values()]
+    return out
+
+
+def counter_summary(paths, kernel: str) -> dict:
+    """Mean per-dispatch counters over the given runs, and the derived figures."""
+    vals = {}
+    grbm = []
+    for p in paths:
+        d = pmc_dispatch_values(p, kernel)
+        for cn, v in d.items():
+            if cn == "GRBM_GUI_ACTIVE":
+                grbm.extend(v)
+            else:
+                vals[cn] = sum(v) / len(v)
+    if not grbm:
+        raise KeyError(f"no GRBM_GUI_ACTIVE for {kernel}")
+    g = sum(grbm) / len(grbm)
+    der = {}
+
+    def have(*cs):
+        return all(c in vals for c in cs)
+
+    if have("SQ_VALU_MFMA_BUSY_CYCLES"):
+        der["MfmaUtil %"] = 100.0 * vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * SIMD_NUM)
+    if have("SQ_ACTIVE_INST_VALU"):
+        der["VALUBusy %"] = 100.0 * vals["SQ_ACTIVE_INST_VALU"] / CU_NUM / g
+    if have("SQ_LDS_IDX_ACTIVE"):
+        der["LdsUtil %"] = 100.0 * vals["SQ_LDS_IDX_ACTIVE"] / (g * CU_NUM)
+    if have("SQ_LDS_BANK_CONFLICT"):
+        der["LDSBankConflict %"] = 100.0 * vals["SQ_LDS_BANK_CONFLICT"] / g / CU_NUM
+    if have("SQ_WAVE_CYCLES"):
+        der["OccupancyPercent %"] = 400.0 * vals["SQ_WAVE_CYCLES"] / g / CU_NUM / WAVE_SLOTS
+    if have("SQ_BUSY_CU_CYCLES"):
+        der["CU busy %"] = 100.0 * vals["SQ_BUSY_CU_CYCLES"] / (g * CU_NUM)
+    if have("SQ_WAVES", "SQ_INSTS_VALU"):
+        der["VALU instructions per wave"] = vals["SQ_INSTS_VALU"] / vals["SQ_WAVES"]
+    if have("SQ_WAVES", "SQ_INSTS_MFMA"):
+        der["MFMA instructions per wave"] = vals["SQ_INSTS_MFMA"] / vals["SQ_WAVES"]
+    if have("SQ_WAVES", "SQ_INSTS_LDS"):
+        der["LDS instructions per wave"] = vals["SQ_INSTS_LDS"] / vals["SQ_WAVES"]
+    return {"kernel": kernel, "dispatches": len(grbm), "GRBM_GUI_ACTIVE": g, "counters": vals, "derived": der}
+
+
+def counter_table(summary: dict) -> str:
+    rows = [f"Kernel `{summary['kernel']}`, {summary['dispatches']} dispatches; GRBM_GUI_ACTIVE "
+            f"{summary['GRBM_GUI_ACTIVE']:.0f} cycles per dispatch.", "",
+            "| counter (sum over instances, mean per dispatch) | value |", "|---|---:|"]
+    for cn, v in sorted(summary["counters"].items()):
+        rows.append(f"| {cn} | {v:.0f} |")
+    rows += ["", "| derived (rocprofv3 expressions) | value |", "|---|---:|"]
+    for cn, v in summary["derived"].items():
+        rows.append(f"| {cn} | {v:.1f} |")
+    return "\n".join(rows)
 
 
 def short(name: str) -> str:
@@ -125,9 +205,16 @@ def main(argv=None):
     t.add_argument("--calib-bytes", type=int, required=True)
     t.add_argument("--key", required=True)
     t.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("db", nargs="+")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(stats_table(a.db))
+        return 0
+    if a.cmd == "counters":
+        paths = [p for pat in a.db for p in (glob.glob(pat) or [pat])]
+        print(counter_table(counter_summary(paths, a.kernel)))
         return 0
     rec = traffic(a.fetch_db, a.write_db, a.kernel, a.calib_bytes)
     data = {}
