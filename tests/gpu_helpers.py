@@ -69,11 +69,22 @@ def errors(gpu, ref):
     return float(err.max(initial=0.0)), float(rel.max(initial=0.0))
 
 
+def unfloored_rel(gpu, ref):
+    """p99 and max of |gpu - ref| / |ref| over elements with ref != 0 (reported only)."""
+    nz = ref != 0
+    if not np.any(nz):
+        return 0.0, 0.0
+    r = np.abs(gpu[nz] - ref[nz]) / np.abs(ref[nz])
+    return float(np.percentile(r, 99)), float(r.max())
+
+
 def assert_matches_oracle(gpu, ref, what=""):
     assert gpu.shape == ref.shape
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite output"
     mx, rel = errors(gpu, ref)
-    log(f"  {what}: max abs err {mx:.3e}, max rel err {rel:.3e}")
+    p99, umax = unfloored_rel(gpu, ref)
+    log(f"  {what}: max abs err {mx:.3e}, max rel err {rel:.3e} "
+        f"(unfloored relative: p99 {p99:.3e}, max {umax:.3e})")
     assert mx <= ATOL, f"{what}: max abs err {mx} > {ATOL}"
     assert rel <= RTOL, f"{what}: max rel err {rel} > {RTOL}"
 
@@ -120,3 +131,12 @@ def ref_without_tokens(case, b, q_rows, rows, drop):
             e = np.exp(s - s.max())
             out[r, h] = e @ V / e.sum()
     return out
+
+
+def bf16_ulp_distance(a_bits, b_bits):
+    """Distance in bf16 steps between two arrays of bf16 bit patterns (uint16),
+    on the monotone ordering of the values (the two zeros coincide)."""
+    def order(x):
+        x = np.asarray(x, dtype=np.int64)
+        return np.where(x & 0x8000, -(x & 0x7FFF), x)
+    return np.abs(order(a_bits) - order(b_bits))

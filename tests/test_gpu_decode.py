@@ -5,7 +5,7 @@ import pytest
 
 import oracle.paged_attention as O
 from paged_kv_cache_08_amd import workloads as W
-from tests.gpu_helpers import assert_matches_oracle, log, run_gpu, to_device
+from tests.gpu_helpers import ATOL, REL_FLOOR, assert_matches_oracle, bf16_ulp_distance, log, run_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -139,6 +139,16 @@ def test_bf16_output_is_rounded_f32_output():
     f32 = run_gpu(case).astype(np.float32)
     b16 = run_gpu(case, out_dtype=torch.bfloat16).astype(np.float32)
     np.testing.assert_array_equal(W.f32_to_bf16_bits(b16), W.f32_to_bf16_bits(f32))
+    # Against the oracle rounded to bf16: within one bf16 step wherever
+    # |oracle| >= 1e-3 (below that the fp32 error can exceed a bf16 step),
+    # and everywhere within the absolute tolerance plus the rounding to bf16
+    # (half a step: 2^-9 of the value, bounded here by 2^-8).
+    ref = oracle_out(case)
+    big = np.abs(ref) >= REL_FLOOR
+    d = bf16_ulp_distance(W.f32_to_bf16_bits(b16), W.f32_to_bf16_bits(ref.astype(np.float32)))
+    log(f"  bf16 out vs rounded oracle: max {int(d[big].max())} steps where |oracle| >= {REL_FLOOR}")
+    assert int(d[big].max()) <= 1
+    assert np.all(np.abs(b16 - ref) <= ATOL + np.abs(ref) * 2.0**-8)
 
 
 @pytest.mark.parametrize("bs", [1, 3, 16, 784])
