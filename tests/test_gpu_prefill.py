@@ -181,3 +181,48 @@ def test_inconsistent_rows_are_flagged_and_skipped():
     assert_matches_oracle(got[:25], ref[:25], "seq 0")
     assert_matches_oracle(got[65:], ref[65:], "seq 2")
     assert np.all(got[25:65] == 7.0)
+
+
+def test_chunks_match_the_whole_prompt_bitwise():
+    import torch
+    import paged_kv_cache_08_amd as P
+    # A 2000-token prompt as one call, and as chunks of 700, 800 and 500 rows
+    # with the cache length at each chunk's end. A row's result depends only
+    # on its own tokens and on the fixed 64-token tile walk from the start
+    # (fully masked tiles add exact zeros), not on which block holds it.
+    log("case: prompt 2000 as one prefill call vs chunks 700 + 800 + 500, page 784")
+    case = W.make_case(1127, [2000], q_len=2000, block_size=784, boost_frac=0.05)
+    q_all, cu_all = W.pack_varlen(case, [2000])
+    whole, _ = run_prefill(case, q_all, cu_all)
+    _, k, v, table, _ = to_device(case)
+    parts, start = [], 0
+    for n in (700, 800, 500):
+        lens = torch.tensor([start + n], dtype=torch.int32, device="cuda")
+        cu = torch.tensor([0, n], dtype=torch.int32, device="cuda")
+        out = P.paged_prefill_attention(bf16_tensor(q_all[start:start + n]), k, v, table, lens, cu,
+                                        case.block_size, case.scale, max_q_len=n, max_seq_len=start + n)
+        torch.cuda.synchronize()
+        parts.append(out.cpu().numpy().astype(np.float64))
+        start += n
+    np.testing.assert_array_equal(np.concatenate(parts), whole)
+    rows = [0, 699, 700, 1499, 1500, 1999]
+    assert_matches_oracle(whole[rows], oracle_rows(case, q_all, cu_all, 0, rows), "prompt rows")
+
+
+def test_decode_at_a_position_matches_its_prefill_row():
+    import torch
+    import paged_kv_cache_08_amd as P
+    # Prefill row i of a 300-row chunk on 1300 tokens and a decode call with
+    # that row's query on the first 1000 + i + 1 tokens (different kernels,
+    # same attention): within the tolerance of each other and of the oracle.
+    log("case: prefill rows vs q_len-1 decode calls on the matching prefixes")
+    case = W.make_case(1128, [1300], q_len=300, block_size=16, boost_frac=0.05)
+    q, cu = W.pack_varlen(case, [300])
+    pre, _ = run_prefill(case, q, cu)
+    _, k, v, table, _ = to_device(case)
+    for i in (0, 1, 150, 299):
+        lens = torch.tensor([1000 + i + 1], dtype=torch.int32, device="cuda")
+        dec = P.paged_decode_attention(bf16_tensor(q[i:i + 1][None]), k, v, table, lens, 16, case.scale,
+                                       max_seq_len=1300)
+        torch.cuda.synchronize()
+        assert_matches_oracle(dec.cpu().numpy().astype(np.float64)[0, 0], pre[i], f"decode vs prefill row {i}")
