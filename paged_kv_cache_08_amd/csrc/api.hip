@@ -260,7 +260,7 @@ int launch_call(const pkv_decode_params* p, const void* q, const void* k_cache, 
   hipError_t e;
   const char* split_name;
   int window;
-  if (p->q_len == 1 && !cu_q) {
+  if (p->q_len == 1 && !cu_q && pkv::decode_supported(p->head_dim, group)) {
     e = pkv::launch_decode_split(a, p->head_dim, group, st, g_ev_start, g_ev_stop);
     split_name = "decode_valu";
     window = pkv::decode_window(chunk);
@@ -291,10 +291,11 @@ int pkv_validate_params(const pkv_decode_params* p) {
   int rc = validate_common(p);
   if (rc) return rc;
   const int group = p->num_q_heads / p->num_kv_heads;
-  if (p->q_len == 1 && !pkv::decode_supported(p->head_dim, group))
-    return fail(PKV_ERR_UNSUPPORTED, "decode (q_len 1) needs at most 8 query heads per KV head");
-  if (p->q_len > 1 && !pkv::verify_supported(p->head_dim, group, p->q_len))
-    return fail(PKV_ERR_UNSUPPORTED, "multi-row calls need (Hq / Hkv) * q_len <= 128");
+  // q_len 1 with up to 8 query heads per KV head runs on the decode kernel;
+  // larger groups and multi-row calls on the MFMA kernel.
+  if (!(p->q_len == 1 && pkv::decode_supported(p->head_dim, group)) &&
+      !pkv::verify_supported(p->head_dim, group, p->q_len))
+    return fail(PKV_ERR_UNSUPPORTED, "needs (Hq / Hkv) * q_len <= 128");
   return PKV_OK;
 }
 

@@ -60,7 +60,8 @@ def params(**kw):
     ({"num_q_heads": 25}, -1),
     ({"head_dim": 64}, -2),
     ({"head_dim": 512}, -2),
-    ({"num_q_heads": 36}, -2),           # group 9 at q_len 1
+    ({"num_q_heads": 36}, 0),            # group 9 at q_len 1: the MFMA kernel
+    ({"num_q_heads": 516}, -2),          # group 129: more than 128 rows per KV head
     ({"num_q_heads": 48, "q_len": 5}, 0),   # 12 heads x 5 rows = 60 verify rows per KV head
     ({"num_q_heads": 48, "q_len": 11}, -2),  # 132 rows > 128
     ({"num_q_heads": 32, "q_len": 16}, 0),   # 8 x 16 = 128 rows

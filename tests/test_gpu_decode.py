@@ -246,3 +246,18 @@ def test_split_ranges_bit_exact(name, make):
         r = P.debug_split_ranges(p, lens)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(r.cpu().numpy(), O.split_ranges_ref(case.seq_lens, S, chunk))
+
+
+@pytest.mark.parametrize("hq,hkv,d,bs,lens", [
+    (24, 2, 256, 784, [32768]),        # 12 query heads per KV head
+    (32, 2, 128, 16, [5000, 17, 0]),   # 16 per KV head
+    (128, 1, 128, 832, [3000]),        # 128 per KV head: the MFMA kernel's limit
+])
+def test_large_groups_run_on_the_mfma_kernel(hq, hkv, d, bs, lens):
+    import paged_kv_cache_08_amd as P
+    log(f"case: q_len 1, {hq}/{hkv}/{d}, page {bs}, lengths {lens}")
+    case = W.make_case(90 + hq + hkv, lens, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs,
+                       interleave=True, boost_frac=0.05)
+    got = run_gpu(case)
+    assert P.last_variant().startswith("verify_mfma")
+    assert_matches_oracle(got, oracle_out(case), f"q1 {hq}/{hkv}/{d} B{bs}")
