@@ -100,7 +100,8 @@ const char* pkv_strerror(int code);
  * string); empty when none. Static thread-local storage. */
 const char* pkv_last_error(void);
 
-/* Host-only check of *p (no HIP call): sizes, group size, head_dim, q_len,
+/* Host-only check of *p (no HIP call): sizes (num_seqs, num_kv_heads and
+ * num_q_heads at most 65535 for the decode and varlen calls), group size, head_dim, q_len,
  * strides (positive, multiples of 8 so every K/V row starts on 16 bytes;
  * block_size <= 2^20 and block_size * token stride below 2^31 elements, else
  * PKV_ERR_UNSUPPORTED), max_seq_len <= 2^30 (else PKV_ERR_UNSUPPORTED) and

@@ -190,8 +190,17 @@ int validate_common(const pkv_decode_params* p, int32_t max_q_len = 16) {
   return PKV_OK;
 }
 
+// The split and merge grids of the decode and varlen calls put sequences, KV
+// heads and query heads in their y and z dimensions (at most 65535 each).
+int validate_grid_yz(const pkv_decode_params* p) {
+  if (p->num_seqs > 65535 || p->num_kv_heads > 65535 || p->num_q_heads > 65535)
+    return fail(PKV_ERR_UNSUPPORTED, "more than 65535 sequences, KV heads or query heads");
+  return PKV_OK;
+}
+
 int validate_varlen(const pkv_decode_params* p) {
   int rc = validate_common(p);
+  if (!rc) rc = validate_grid_yz(p);
   if (rc) return rc;
   if (!pkv::verify_supported(p->head_dim, p->num_q_heads / p->num_kv_heads, p->q_len))
     return fail(PKV_ERR_UNSUPPORTED, "varlen calls need (Hq / Hkv) * max q_len <= 128");
@@ -289,6 +298,7 @@ extern "C" {
 
 int pkv_validate_params(const pkv_decode_params* p) {
   int rc = validate_common(p);
+  if (!rc) rc = validate_grid_yz(p);
   if (rc) return rc;
   const int group = p->num_q_heads / p->num_kv_heads;
   // q_len 1 with up to 8 query heads per KV head runs on the decode kernel;

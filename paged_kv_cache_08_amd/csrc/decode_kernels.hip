@@ -44,8 +44,8 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(DecodeArgs a) {
   __shared__ float sm_w[kMergeSplitsLds];
   __shared__ float red[4];
   __shared__ float part[4][64];
-  const int cb = blockIdx.x, h = blockIdx.y;
-  const int i = blockIdx.z % a.q_len, b = blockIdx.z / a.q_len;
+  const int cb = blockIdx.z, h = blockIdx.y;
+  const int i = blockIdx.x % a.q_len, b = blockIdx.x / a.q_len;
   const QRows qr = seq_q_rows(a, b);
   if (i >= qr.n) return;          // no such row in a varlen batch
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -248,7 +248,7 @@ hipError_t launch_lse_merge(const DecodeArgs& a, int head_dim, hipStream_t st) {
       return hipErrorInvalidValue;
     return hipGetLastError();
   }
-  dim3 grid(head_dim / 64, a.hq, a.q_len * a.num_seqs);
+  dim3 grid(a.q_len * a.num_seqs, a.hq, head_dim / 64);
   if (head_dim == 256)
     hipLaunchKernelGGL(lse_merge_kernel<256>, grid, dim3(256), 0, st, a);
   else if (head_dim == 128)

@@ -86,6 +86,8 @@ def params(**kw):
     ({"out_dtype": 7}, -1),
     ({"num_splits": -3}, -1),
     ({"total_tokens": -1}, -1),
+    ({"num_seqs": 65535}, 0),
+    ({"num_seqs": 65536}, -2),           # launch grid limit (y / z)
 ])
 def test_validation_codes(kw, code):
     assert P.validate(params(**kw)) == code
@@ -111,6 +113,7 @@ def _prefill(p, ws_bytes=256, ptr=0):
     ({"q_len": 4096, "window": 2048}, -1),
     ({"q_len": 4096, "head_dim": 64}, -2),
     ({"q_len": 4096, "kv_dtype": 1, "k_scale": -1.0, "v_scale": 1.0}, -1),
+    ({"q_len": 16, "num_seqs": 100000}, -1),   # 1-D grid: no 65535 limit on sequences
 ])
 def test_prefill_validation_codes(kw, code):
     assert _prefill(params(**kw)) == code
