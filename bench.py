@@ -241,7 +241,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards by sequence, KV head or context; see the design notes)", file=sys.stderr)
+              "(the path shards by sequence, KV head or context range; this harness measures one GPU's share)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -37,9 +37,12 @@ it, so the oracle evaluates the definition directly):
 with K_j, V_j read through the block table and widened exactly to fp64 (bf16
 bits, or FP8 E4M3 codes decoded from the OCP definition times the float32
 per-tensor scale), and sigma = float64(float32(scale)), the value the kernel
-receives. Varlen calls apply this to each sequence's own rows (q_len = n_b).
+receives. Varlen calls apply this to each sequence's own rows (q_len = n_b);
+so do chunked-prefill calls, whose n_b new rows may number in the thousands
+("DCU page832 attention" §6 serves prompts in chunks of 4096 rows and a
+shorter tail chunk, each as causal attention over the paged context).
 
-Readings where the pages are silent (each also listed in the design notes):
+Readings where the pages are silent:
 GQA head h uses KV head h // G; a sequence with L = 0 yields zeros; the
 multi-row causal window is bottom-right aligned (row i sees j <= L - q_len + i);
 a sliding window counts positions and includes the row's own token.
