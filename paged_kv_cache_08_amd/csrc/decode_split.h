@@ -36,10 +36,11 @@
 //     a token then costs one division by the page size (multiply-high), one
 //     LDS read and a 32-bit multiply-add.
 //   * Epilogue: the 4 token rows of a wave are merged by a reduce-scatter over
-//     lane swaps (v_permlane32_swap, v_permlane16_swap), the 8 waves through
-//     LDS, in a fixed order; the split's (max, sum, accumulator) go to the
-//     workspace, or the normalised output directly when the sequence has a
-//     single split.
+//     lane swaps (v_permlane32_swap, v_permlane16_swap); the 8 waves publish
+//     their sums with their reference max in LDS and, after one barrier, are
+//     rescaled to the workgroup max and added in a fixed order; the split's
+//     (max, sum, accumulator) go to the workspace, or the normalised output
+//     directly when the sequence has a single split.
 // Every reduction order depends only on logical token indices and the split
 // plan, never on block_size or physical page ids, so the same logical K/V gives
 // bitwise-identical output for any page size or page placement.
@@ -170,8 +171,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
 
   __shared__ PageOffs tbl[kTblSplit];
   __shared__ __attribute__((aligned(16))) float mrg_acc[kWaves][G][D];
-  __shared__ float mrg_m[kWaves][G];
-  __shared__ float mrg_l[kWaves][G];
+  __shared__ __attribute__((aligned(16))) float mrg_m[G][kWaves];
+  __shared__ __attribute__((aligned(16))) float mrg_l[G][kWaves];
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
@@ -388,7 +389,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   // rows, and reduce-scatter the accumulators over the rows with lane swaps
   // (wave halves, then row pairs). Row r of lane column col ends with the
   // sums of elements e in [r * kEpl / 4, (r + 1) * kEpl / 4) of each head.
-  // All of this runs before the first barrier, while slower waves stream.
+  // All of this runs before the barrier, while slower waves stream.
   constexpr int kE2 = kEpl / 2, kE4 = kEpl / 4;
   float m[G], l[G];
   head_bcast<G>(m_row, m);
@@ -408,22 +409,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
       part[h][e] = p.lo + p.hi;
     }
   }
-  if (lane == 0)
-#pragma unroll
-    for (int h = 0; h < G; ++h) mrg_m[wave][h] = m[h];
-  __syncthreads();
-
-  // Rescale the wave's sums to the workgroup max of each head.
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float M = mrg_m[0][h];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mrg_m[w][h]);
-    const float f = fast_exp2(m[h] - M);
-    l[h] *= f;
-#pragma unroll
-    for (int e = 0; e < kE4; ++e) part[h][e] *= f;
-  }
+  // Every wave publishes its sums with its reference max and its sum of
+  // probabilities; after one barrier the final pass rescales each wave to the
+  // workgroup max while it adds the waves (fixed order).
   {
     const int d0 = elem_d<FP8, kEpl>(col, row * kE4);     // kE4 contiguous elements
 #pragma unroll
@@ -437,20 +425,39 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
     }
     if (lane == 0)
 #pragma unroll
-      for (int h = 0; h < G; ++h) mrg_l[wave][h] = l[h];
+      for (int h = 0; h < G; ++h) {
+        mrg_m[h][wave] = m[h];
+        mrg_l[h][wave] = l[h];
+      }
   }
   __syncthreads();
 
-  // Sum the waves (all already relative to the workgroup max; fixed order)
-  // and write the split's result.
   const int64_t prow0 = int64_t(b) * a.q_len * a.hq + int64_t(g) * G;   // partial row of head 0, query row 0
   for (int i = tid; i < G * D; i += kThreads) {
     const int h = i / D, d = i - h * D;
+    float mw[kWaves], lw[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; w += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(&mrg_m[h][w]);
+      const float4 y = *reinterpret_cast<const float4*>(&mrg_l[h][w]);
+      mw[w] = x.x;
+      mw[w + 1] = x.y;
+      mw[w + 2] = x.z;
+      mw[w + 3] = x.w;
+      lw[w] = y.x;
+      lw[w + 1] = y.y;
+      lw[w + 2] = y.z;
+      lw[w + 3] = y.w;
+    }
+    float M = mw[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mw[w]);
     float num = 0.0f, den = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      num += mrg_acc[w][h][d];
-      den += mrg_l[w][h];
+      const float f = fast_exp2(mw[w] - M);
+      num = fmaf(f, mrg_acc[w][h][d], num);
+      den = fmaf(f, lw[w], den);
     }
     if (sp.nsplit == 1) {
       store_out(a, out_row0 + i, den > 0.0f ? num / den : 0.0f);
@@ -458,9 +465,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
       const int64_t pr = (prow0 + h) * a.num_splits + s;
       a.part_acc[pr * D + d] = num;
       if (d == 0) {
-        float M = mrg_m[0][h];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mrg_m[w][h]);
         a.part_ml[pr * 2] = M;
         a.part_ml[pr * 2 + 1] = den;
       }
