@@ -94,6 +94,31 @@ def test_forced_split_counts_agree(splits):
     assert_matches_oracle(got, oracle_out(case), f"S={splits}")
 
 
+# Beyond 32K: the planner's 512-token splits (137 of them), and a forced plan
+# of 1094 one-tile splits, more than the merge keeps per-split weights for
+# in LDS (1024), so the merge's global-memory path for the rest runs too.
+@pytest.mark.parametrize("splits", [0, 1094])
+def test_long_context_70000(splits):
+    import paged_kv_cache_08_amd as P
+    log(f"case: context 70000, page 784, splits {splits or 'planned'}")
+    case = hybrid(70000)
+    got = run_gpu(case, num_splits=splits)
+    S, chunk = O.split_plan_ref(1, 4, 70000, 784, P.device_cu_count(), forced_splits=splits)
+    assert f"splits={S} chunk={chunk} " in P.last_variant()
+    assert (S, chunk) == ((137, 512) if splits == 0 else (1094, 64))
+    assert_matches_oracle(got, oracle_out(case), f"L70000 S={S}")
+
+
+def test_batch_of_96_short_and_empty_sequences():
+    lens = np.random.default_rng(1013).integers(0, 2001, size=96)
+    lens[[5, 77]] = 0
+    log(f"case: 96 sequences, lengths 0..2000 (sum {int(lens.sum())}), page 16, interleaved pages")
+    case = W.make_case(1013, lens.tolist(), block_size=16, interleave=True, boost_frac=0.05)
+    got = run_gpu(case, total_tokens=int(lens.sum()))
+    assert_matches_oracle(got, oracle_out(case), "96 sequences")
+    assert np.all(got[[5, 77]] == 0.0)
+
+
 def test_repeat_runs_are_bitwise_identical():
     log("case: repeat, context 4096, page 784")
     case = hybrid(4096)
