@@ -70,7 +70,7 @@ constexpr float kMinit = -1.0e30f;             // floor of a row's max (finite: 
 // Lane n of each 16-lane row, broadcast to the whole row (DPP row_newbcast).
 template <int N>
 __device__ __forceinline__ float row_bcast(float x) {
-  return dpp_move<0x150 + N>(x);
+  return dpp_move_full<0x150 + N>(x);
 }
 
 // out[h] = value held by lane 2h of the row (the lanes that own head h after

@@ -26,6 +26,12 @@ __device__ __forceinline__ float dpp_move(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
                                                                CTRL, 0xF, 0xF, false));
 }
+// The same move for controls where every lane has a source lane (broadcasts
+// within a row): no old value, so no register is zeroed first.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move_full(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
