@@ -11,38 +11,31 @@ namespace {
 
 constexpr int kMergeSplitsLds = 1024;          // splits whose weights the merge keeps in LDS
 
-// Block-wide reductions over the 256 threads of a merge workgroup.
-__device__ __forceinline__ float block_max256(float x, float* red) {
+// Wave-wide reductions (every lane gets the result; fixed butterfly order).
+__device__ __forceinline__ float wave_max64(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  return x;
 }
-
-__device__ __forceinline__ float block_sum256(float x, float* red) {
+__device__ __forceinline__ float wave_sum64(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  return (red[0] + red[1]) + (red[2] + red[3]);
+  return x;
 }
 
 // out[b,i,h,:] = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s over the
 // sequence's splits with l_s > 0, M = max of their m_s; a row with no such
 // split gets zeros. Workgroup = (64-column block, query head, query row x
-// sequence), 4 waves; wave w sums splits w, w + 4, .... The accumulator and
-// (m, l) loads are all issued first; the per-split weights 2^(m_s - M) / den
-// are computed once into LDS. All sums run in a fixed order.
+// sequence), 4 waves; wave w sums splits w, w + 4, .... The accumulator loads
+// are issued first. Every wave finds M and the denominator over all splits
+// by itself (wave-wide reductions, the (m, l) pairs are a few hundred bytes)
+// and keeps its weights 2^(m_s - M) in its own LDS row, so the only barrier
+// is the one before the 4 wave sums are added. All sums run in a fixed order.
 template <int D>
 __global__ __launch_bounds__(256) void lse_merge_kernel(DecodeArgs a) {
   constexpr int kPerWave = 16;    // accumulator loads in flight per thread per pass
   constexpr int kPass = 4 * kPerWave;
-  __shared__ float sm_m[kMergeSplitsLds];
-  __shared__ float sm_w[kMergeSplitsLds];
-  __shared__ float red[4];
+  __shared__ float sm_w[4][kMergeSplitsLds];
   __shared__ float part[4][64];
   const int cb = blockIdx.z, h = blockIdx.y;
   const int i = blockIdx.x % a.q_len, b = blockIdx.x / a.q_len;
@@ -65,36 +58,28 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(DecodeArgs a) {
   }
   // (m, l) of every split; a split with l = 0 (no visible token) gets m = -inf.
   float mloc = -INFINITY;
-  for (int t = tid; t < ns; t += 256) {
+  for (int t = lane; t < ns; t += 64) {
     const float2 v = reinterpret_cast<const float2*>(ml)[t];
-    const float mv = v.y > 0.0f ? v.x : -INFINITY;
-    if (t < kMergeSplitsLds) {
-      sm_m[t] = mv;
-      sm_w[t] = v.y;
-    }
-    mloc = fmaxf(mloc, mv);
+    mloc = fmaxf(mloc, v.y > 0.0f ? v.x : -INFINITY);
   }
-  const float M = block_max256(mloc, red);
+  const float M = wave_max64(mloc);   // the same in every wave
   if (M == -INFINITY) {
     if (wave == 0) store_out(a, prow * D + d, 0.0f);
     return;
   }
   float dloc = 0.0f;
-  for (int t = tid; t < ns; t += 256) {
-    float mv, lv;
-    if (t < kMergeSplitsLds) {
-      mv = sm_m[t];
-      lv = sm_w[t];
-    } else {
-      const float2 v = reinterpret_cast<const float2*>(ml)[t];
-      mv = v.y > 0.0f ? v.x : -INFINITY;
-      lv = v.y;
-    }
-    const float f = fast_exp2(mv - M);    // 0 for empty splits
-    dloc += f * lv;
-    if (t < kMergeSplitsLds) sm_w[t] = f;
+  for (int t = lane; t < ns; t += 64) {
+    const float2 v = reinterpret_cast<const float2*>(ml)[t];
+    const float f = v.y > 0.0f ? fast_exp2(v.x - M) : 0.0f;   // 0 for empty splits
+    dloc += f * v.y;
+    if (t < kMergeSplitsLds) sm_w[wave][t] = f;
   }
-  const float inv_den = 1.0f / block_sum256(dloc, red);   // barrier inside: sm_w is complete
+  const float inv_den = 1.0f / wave_sum64(dloc);
+  // The wave reads back the weights it wrote (LDS operations of one wave run
+  // in order; this keeps the compiler from moving the reads above the writes).
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   float num = 0.0f;
   for (int s0 = 0; s0 < ns; s0 += kPass) {
@@ -111,7 +96,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(DecodeArgs a) {
       if (sidx < ns) {
         float f;
         if (sidx < kMergeSplitsLds) {
-          f = sm_w[sidx];
+          f = sm_w[wave][sidx];
         } else {
           const float2 v = reinterpret_cast<const float2*>(ml)[sidx];
           f = v.y > 0.0f ? fast_exp2(v.x - M) : 0.0f;
@@ -184,11 +169,14 @@ __global__ __launch_bounds__(256) void lse_merge_few_kernel(DecodeArgs a) {
   for (int c = 0; c < kCols; ++c) store_out(a, prow * D + c * 64 + lane, num[c] * inv);
 }
 
-// Debug: offsets of every live token row, through the same split range,
-// table staging and token_row() the split kernel uses.
+// Debug: offsets of every live token row of the split ranges, found both
+// ways the kernels find them: token_row() on the staged table (the MFMA
+// kernel) and token_row_direct() on the table row in global memory (the
+// single-query split kernel). A token on which they disagree gets -3, an
+// invalid page entry -2.
 __global__ __launch_bounds__(kThreads) void debug_offsets_kernel(DecodeArgs a, int g, int max_seq_len,
                                                                  int64_t* k_off, int64_t* v_off) {
-  __shared__ PageOffs tbl[kTblSplit];
+  __shared__ PageOffs tbl[kMaxChunk + 2];
   const int s = blockIdx.x, b = blockIdx.y;
   const SplitSpan sp = split_span(a, b, s, a.q_len);
   if (sp.begin >= sp.L) return;
@@ -198,10 +186,12 @@ __global__ __launch_bounds__(kThreads) void debug_offsets_kernel(DecodeArgs a, i
   __syncthreads();
   const int t_end = min(sp.end, max_seq_len);
   for (int t = sp.begin + threadIdx.x; t < t_end; t += kThreads) {
-    int64_t ko, vo;
-    const bool ok = token_row(a, tbl, p_first, t, ko, vo);
-    k_off[int64_t(b) * max_seq_len + t] = ok ? ko : -2;
-    v_off[int64_t(b) * max_seq_len + t] = ok ? vo : -2;
+    int64_t ko = 0, vo = 0, kd = 0, vd = 0;
+    const bool ok = token_row(a, tbl, p_first, t, ko, vo);     // staged table (MFMA kernel)
+    const bool okd = token_row_direct(a, b, g, t, kd, vd);     // table row in global memory (split kernel)
+    const bool same = ok == okd && (!ok || (ko == kd && vo == vd));
+    k_off[int64_t(b) * max_seq_len + t] = !same ? -3 : ok ? ko : -2;
+    v_off[int64_t(b) * max_seq_len + t] = !same ? -3 : ok ? vo : -2;
   }
 }
 

@@ -31,10 +31,13 @@
 //   * V pass: with the exact maximum of the lane's own window scores, each
 //     probability is computed once per (token, head), broadcast to the row with
 //     DPP row_newbcast, and accumulated with fp32 FMAs.
-//   * Page offsets (page * page_stride + head * head_stride, for K and V) are
-//     staged in LDS once per split, fetched while seq_lens is still in flight;
-//     a token then costs one division by the page size (multiply-high), one
-//     LDS read and a 32-bit multiply-add.
+//   * Token offsets: one thread per window token divides the token index by
+//     the page size (multiply-high), reads the block-table entry and stores
+//     the token's K and V row offsets in LDS, once per split (without a
+//     sliding window, while seq_lens is still in flight); a masked token gets
+//     the offset of the q row. A lane then costs one LDS read and one address
+//     add per K or V row, instead of every lane of a row repeating the
+//     division and the table lookup.
 //   * Epilogue: the 4 token rows of a wave are merged by a reduce-scatter over
 //     lane swaps (v_permlane32_swap, v_permlane16_swap); the 8 waves publish
 //     their sums with their reference max in LDS and, after one barrier, are
@@ -64,7 +67,6 @@ constexpr int kStep = kWaves * kRowsPerWave;   // tokens per workgroup sub-step
 // Register ring depth (steps in flight + 1); shallower where G * D leaves
 // fewer registers (depths 4..10 measured alike at G = 6, D = 256).
 constexpr int ring_depth(int D, int G) { return (D == 256 && G >= 7) ? 3 : 6; }
-constexpr int kTblSplit = kMaxChunk + 2;       // page entries one split can span (B = 1)
 constexpr float kMinit = -1.0e30f;             // floor of a row's max (finite: no inf - inf)
 
 // Lane n of each 16-lane row, broadcast to the whole row (DPP row_newbcast).
@@ -165,11 +167,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   constexpr int kCpl = FP8 ? 1 : kCq;      // 16-byte K/V loads per lane and row (FP8 at D = 128: 8 bytes)
   constexpr int kSteps = 2 * kSubSteps;    // K pass, then V pass
   constexpr int kRing = ring_depth(D, G);
+  constexpr int kWin = kSubSteps * kStep;  // tokens of the window
+  constexpr int kEsz = FP8 ? 1 : 2;        // bytes per cache element
   static_assert(kCpl >= 1 && kEpl % 8 == 0, "head_dim must be a multiple of 128");
   static_assert(G <= 8, "at most 8 query heads per KV head");
-  static_assert(kSubSteps >= 1 && kSubSteps * kStep <= kMaxChunk, "window of at most kMaxChunk tokens");
+  static_assert(kSubSteps >= 1 && kWin <= kMaxChunk && kWin <= kThreads, "window of at most kMaxChunk tokens");
 
-  __shared__ PageOffs tbl[kTblSplit];
+  __shared__ int64_t tok_k[kWin];   // element offset of each window token's K row (a masked token: the q row)
+  __shared__ int64_t tok_v[kWin];
   __shared__ __attribute__((aligned(16))) float mrg_acc[kWaves][G][D];
   __shared__ __attribute__((aligned(16))) float mrg_m[G][kWaves];
   __shared__ __attribute__((aligned(16))) float mrg_l[G][kWaves];
@@ -180,10 +185,49 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   const int lane = tid & 63, wave = tid >> 6;
   const int row = lane >> 4, col = lane & 15;
 
-  // Without a sliding window the table slots and q do not depend on the
-  // sequence length: fetch them while seq_lens is still in flight.
-  SplitPages pages = split_pages(a, s);
-  if (a.window == 0) stage_table(a, b, g, pages.p_first, pages.n, tbl);
+  // A masked token (past the split end, or behind an invalid page entry)
+  // reads the group's first q row instead: finite and in bounds. Its offset
+  // from each cache base, in cache elements (every base is 16-byte aligned).
+  const int64_t qrow_addr = int64_t(reinterpret_cast<uintptr_t>(a.q + out_row0));
+  const int64_t kmask = (qrow_addr - int64_t(reinterpret_cast<uintptr_t>(a.k))) / kEsz;
+  const int64_t vmask = (qrow_addr - int64_t(reinterpret_cast<uintptr_t>(a.v))) / kEsz;
+  // The lane's first element of any row, as a byte address relative to a row start.
+  const uint8_t* const kbase = reinterpret_cast<const uint8_t*>(a.k) + elem_d<FP8, kEpl>(col, 0) * kEsz;
+  const uint8_t* const vbase = reinterpret_cast<const uint8_t*>(a.v) + elem_d<FP8, kEpl>(col, 0) * kEsz;
+
+  // One thread per window token finds its K and V rows. The loads the
+  // start-up waits on are issued together: the sequence length and the
+  // block-table entry of the thread's token. Without a sliding window
+  // the split starts at s * chunk for every sequence length, so the entry
+  // needs no length; the token index is clamped into the mapped range, so
+  // the load needs no branch (an entry beyond the split is read but unused).
+  const int L_in = a.seq_lens[b];
+  int e_tok = -1;
+  if (a.window == 0) {
+    const int t = min(s * a.chunk + min(tid, a.chunk - 1), planned_cap(a) - 1);
+    e_tok = table_entry(a, b, t);
+  }
+
+  const SplitSpan sp = split_span_len(a, L_in, s, 1);
+  if (sp.begin >= sp.L) {
+    if (s == 0)   // empty sequence: zeros
+      for (int i = tid; i < G * D; i += kThreads) store_out(a, out_row0 + i, 0.0f);
+    return;
+  }
+  const bool live = sp.begin + tid < sp.end;   // implies tid < chunk
+  if (a.window > 0 && live) e_tok = table_entry(a, b, sp.begin + tid);
+  int64_t ko = kmask, vo = vmask;
+  const bool entry_ok = token_row_entry(a, e_tok, g, sp.begin + tid, ko, vo);
+  if (tid < kWin) {
+    const bool ok = live && entry_ok;
+    tok_k[tid] = ok ? ko : kmask;
+    tok_v[tid] = ok ? vo : vmask;
+  }
+  if (a.err && __any(live && !entry_ok) && lane == 0) atomicOr(a.err, 1u);
+  __syncthreads();
+  // q is loaded only now, with the first K rows (it is needed no earlier),
+  // so the start-up above waits for nothing but the sequence length and the
+  // block-table entries.
   // q of the group's G heads, in the lane's element order (elem_d).
   uint4 qv[G][kCq];
 #pragma unroll
@@ -192,22 +236,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
     for (int k = 0; k < kCq; ++k)
       qv[h][k] = *reinterpret_cast<const uint4*>(a.q + out_row0 + h * D + elem_d<FP8, kEpl>(col, 8 * k));
 
-  const SplitSpan sp = split_span(a, b, s, 1);
-  if (sp.begin >= sp.L) {
-    if (s == 0)   // empty sequence: zeros
-      for (int i = tid; i < G * D; i += kThreads) store_out(a, out_row0 + i, 0.0f);
-    return;
-  }
-  if (a.window > 0) {   // the split starts at the window's first token
-    pages = span_pages(a, sp);
-    stage_table(a, b, g, pages.p_first, pages.n, tbl);
-  }
-  const int p_first = pages.p_first;
-  __syncthreads();
-  flag_invalid_entries(a, tbl, int(magic_div(uint32_t(sp.end - 1), a.bdiv)) - p_first + 1);
-
   // The split is one window of at most kSubSteps sub-steps of kStep tokens;
-  // row `row` of wave `wave` owns tokens begin + j * kStep + my.
+  // row `row` of wave `wave` owns window tokens j * kStep + my.
   const int my = wave * kRowsPerWave + row;
   const int n_sub = (sp.end - sp.begin + kStep - 1) / kStep;   // uniform, <= kSubSteps
 
@@ -216,63 +246,34 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < kEpl; ++e) acc[h][e] = 0.0f;
-  float sc[kSubSteps];        // score of head (col / 2) for each sub-step's token (log2 units)
-  uint32_t tix[kSubSteps];    // (table slot << 20) | in-page offset of that token; ~0u if masked
+  // Score of head (col / 2) for each sub-step's token (log2 units); the K
+  // fetch sets it to +inf for a live token and -inf for a masked one.
+  float sc[kSubSteps];
   float m_row = kMinit, l_row = 0.0f;
 
-  const uint16_t* const safe_row = a.q + out_row0 + col * 8;   // finite bf16, in bounds
   uint4 ring[kRing][kCpl];
   // One lane's piece of a K or V row: bf16 kCpl 16-byte loads; FP8 kEpl bytes.
-  auto load_row = [&](const void* bf16_row, const uint8_t* fp8_row, uint4 (&buf)[kCpl]) {
+  auto load_row = [&](const uint8_t* p, uint4 (&buf)[kCpl]) {
     if constexpr (FP8) {
       if constexpr (kEpl == 16) {
-        buf[0] = *reinterpret_cast<const uint4*>(fp8_row);
+        buf[0] = *reinterpret_cast<const uint4*>(p);
       } else {
-        const uint2 h = *reinterpret_cast<const uint2*>(fp8_row);
+        const uint2 h = *reinterpret_cast<const uint2*>(p);
         buf[0] = make_uint4(h.x, h.y, 0u, 0u);
       }
     } else {
 #pragma unroll
-      for (int k = 0; k < kCpl; ++k)
-        buf[k] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(bf16_row) + k * 128);
+      for (int k = 0; k < kCpl; ++k) buf[k] = *reinterpret_cast<const uint4*>(p + k * 256);
     }
   };
-
-  // K step j: locate the token, remember where it is (tix: bit 31 = masked,
-  // bits 20..30 = table slot, bits 0..19 = in-page offset), load its K chunk.
-  // Branch-free: a masked row (past the split end, or an invalid page entry)
-  // reads the q row instead.
+  // K step j: the token's K row (branch-free: a masked token reads the q row).
   auto fetch_k = [&](int j, uint4 (&buf)[kCpl]) {
-    const int t = sp.begin + j * kStep + my;
-    const int tc = min(t, sp.end - 1);
-    const uint32_t pg = magic_div(uint32_t(tc), a.bdiv);
-    const int off = tc - int(pg * a.bdiv.d);
-    const int slot = int(pg) - p_first;
-    const int64_t pk = tbl[slot].k;
-    const bool ok = (t < sp.end) && pk >= 0;
-    tix[j] = (ok ? 0u : 0x80000000u) | (uint32_t(slot) << 20) | uint32_t(off);
-    const int64_t eo = pk + int64_t(off * int32_t(a.k_st)) + elem_d<FP8, kEpl>(col, 0);
-    if constexpr (FP8) {
-      const uint8_t* real = reinterpret_cast<const uint8_t*>(a.k) + eo;
-      load_row(nullptr, ok ? real : reinterpret_cast<const uint8_t*>(safe_row), buf);
-    } else {
-      load_row(ok ? a.k + eo : safe_row, nullptr, buf);
-    }
+    const int64_t off = tok_k[j * kStep + my];
+    sc[j] = off != kmask ? INFINITY : -INFINITY;
+    load_row(kbase + off * kEsz, buf);
   };
-  // V step j: the same token's V chunk (the slot of a masked row is still a
-  // staged entry, so the LDS read is in range).
-  auto fetch_v = [&](int j, uint4 (&buf)[kCpl]) {
-    const uint32_t ti = tix[j];
-    const int slot = int((ti >> 20) & 0x7ffu), off = int(ti & 0xfffffu);
-    const bool ok = !(ti & 0x80000000u);
-    const int64_t eo = tbl[slot].v + int64_t(off * int32_t(a.v_st)) + elem_d<FP8, kEpl>(col, 0);
-    if constexpr (FP8) {
-      const uint8_t* real = reinterpret_cast<const uint8_t*>(a.v) + eo;
-      load_row(nullptr, ok ? real : reinterpret_cast<const uint8_t*>(safe_row), buf);
-    } else {
-      load_row(ok ? a.v + eo : safe_row, nullptr, buf);
-    }
-  };
+  // V step j: the same token's V row.
+  auto fetch_v = [&](int j, uint4 (&buf)[kCpl]) { load_row(vbase + tok_v[j * kStep + my] * kEsz, buf); };
   // q.k of the G heads; lanes 2h, 2h+1 keep head h's score.
   auto consume_k = [&](int j, const uint4 (&kk)[kCpl]) {
     float dq[G];
@@ -310,8 +311,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
         dq[h] = d0;
       }
     }
-    const float r = reduce_scatter16<G>(dq, col) * a.scale_log2;
-    sc[j] = (tix[j] & 0x80000000u) ? -INFINITY : r;
+    // sc[j] is +inf (live) or -inf (masked): the minimum keeps the score of a
+    // live token and gives -inf for a masked one whatever its q-row score is
+    // (NaN included: FP8 codes read from the q row may decode to NaN).
+    sc[j] = fminf(sc[j], reduce_scatter16<G>(dq, col) * a.scale_log2);
   };
   // p of head (col / 2), broadcast to the row, V accumulation.
   auto consume_v = [&](int j, const uint4 (&vv)[kCpl]) {
@@ -320,9 +323,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
     float p[G];
     head_bcast<G>(pl, p);
     if constexpr (FP8) {
-      // A masked row read the q row's bytes, which may decode to NaN, and
-      // 0 * NaN is NaN: its codes are replaced by zeros.
-      const bool ok = !(tix[j] & 0x80000000u);
+      // A masked token read the q row's bytes, which may decode to NaN, and
+      // 0 * NaN is NaN: its codes are replaced by zeros. (A live token's
+      // score is finite.)
+      const bool ok = sc[j] != -INFINITY;
       constexpr int kWords = kEpl / 4;
       const uint32_t w4[4] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w};
 #pragma unroll
@@ -354,12 +358,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   };
   // One stream of 2 * kSubSteps steps (K pass, then V pass) through a ring of
   // kRing register buffers: kRing - 1 steps of loads stay in flight. Fully
-  // unrolled, so every buffer lives in fixed registers; steps past n_sub are
-  // skipped with uniform branches.
-#pragma unroll
-  for (int j = 0; j < kSubSteps; ++j) sc[j] = -INFINITY;
-  // Loads are issued for every step (a dead step only reads the q row); the
-  // arithmetic of steps past n_sub is skipped with uniform branches.
+  // unrolled, so every buffer lives in fixed registers. Loads are issued for
+  // every step (a dead step only reads the q row); the arithmetic of steps
+  // past n_sub is skipped with uniform branches.
   static_for<0, (kRing - 1 < kSteps ? kRing - 1 : kSteps)>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
     if constexpr (j < kSubSteps) fetch_k(j, ring[j % kRing]);
@@ -410,7 +411,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
     }
   }
   // Every wave publishes its sums with its reference max and its sum of
-  // probabilities; after one barrier the final pass rescales each wave to the
+  // probabilities; one barrier; the final pass rescales each wave to the
   // workgroup max while it adds the waves (fixed order).
   {
     const int d0 = elem_d<FP8, kEpl>(col, row * kE4);     // kE4 contiguous elements

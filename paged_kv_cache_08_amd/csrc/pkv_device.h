@@ -84,11 +84,11 @@ __device__ __forceinline__ int planned_cap(const DecodeArgs& a) {
 // windows). Split s covers [lo + s * chunk, min(lo + (s + 1) * chunk, L)). L
 // is clamped to what the block table can map and [lo, L) to what the planned
 // splits cover, so a length above the host's max_seq_len can never index past
-// the table, the grid or the workspace.
-__device__ __forceinline__ SplitSpan split_span(const DecodeArgs& a, int b, int s, int rows) {
+// the table, the grid or the workspace. split_span_len() takes the sequence
+// length already read from seq_lens.
+__device__ __forceinline__ SplitSpan split_span_len(const DecodeArgs& a, int64_t L, int s, int rows) {
   const int64_t table_cap = int64_t(a.max_pages) * int64_t(a.bdiv.d);
   const int64_t planned = int64_t(a.num_splits) * a.chunk;
-  int64_t L = a.seq_lens[b];
   L = L < 0 ? 0 : (L > table_cap ? table_cap : L);
   int64_t lo = 0;
   if (a.window > 0) {
@@ -103,6 +103,10 @@ __device__ __forceinline__ SplitSpan split_span(const DecodeArgs& a, int b, int 
   r.end = min(r.begin + a.chunk, r.L);
   r.nsplit = (r.L - r.lo + a.chunk - 1) / a.chunk;
   return r;
+}
+
+__device__ __forceinline__ SplitSpan split_span(const DecodeArgs& a, int b, int s, int rows) {
+  return split_span_len(a, a.seq_lens[b], s, rows);
 }
 
 // Query rows of sequence b: rows [base, base + n) of the packed q and out.
@@ -224,6 +228,31 @@ __device__ __forceinline__ bool token_row(const DecodeArgs& a, const PageOffs* t
   ko = po.k + int64_t(off * int32_t(a.k_st));
   vo = po.v + int64_t(off * int32_t(a.v_st));
   return po.k >= 0;
+}
+
+// The same element offsets from page entry e (already read from the block
+// table) and the token index; false if e is outside [0, num_pages).
+__device__ __forceinline__ bool token_row_entry(const DecodeArgs& a, int e, int g, int t, int64_t& ko,
+                                                int64_t& vo) {
+  if (uint32_t(e) >= uint32_t(a.num_pages)) return false;
+  const uint32_t pg = magic_div(uint32_t(t), a.bdiv);
+  const int off = t - int(pg * a.bdiv.d);
+  ko = (int64_t(e) * a.k_sp + int64_t(g) * a.k_sh) + int64_t(off * int32_t(a.k_st));
+  vo = (int64_t(e) * a.v_sp + int64_t(g) * a.v_sh) + int64_t(off * int32_t(a.v_st));
+  return true;
+}
+
+// Block-table entry of token t of sequence b (t below max_pages * B).
+__device__ __forceinline__ int table_entry(const DecodeArgs& a, int b, int t) {
+  return a.table[int64_t(b) * a.max_pages + magic_div(uint32_t(t), a.bdiv)];
+}
+
+// Element offsets of token t's rows with the entry read straight from
+// sequence b's block-table row (no staged table). Same arithmetic as
+// token_row(), so both give the same bits.
+__device__ __forceinline__ bool token_row_direct(const DecodeArgs& a, int b, int g, int t, int64_t& ko,
+                                                 int64_t& vo) {
+  return token_row_entry(a, table_entry(a, b, t), g, t, ko, vo);
 }
 
 // Calls f(std::integral_constant<int, J>) for J = I .. N-1, so every index the
