@@ -237,9 +237,13 @@ int pkv_last_variant(char* buf, int32_t len);
 int pkv_set_timing_events(void* ev_start, void* ev_stop);
 
 /* Debug: the element offset of every live token row of KV head kv_head, as the
- * split kernel computes it (same device code: split range, table staging,
- * division by block_size, stride arithmetic). k_off, v_off: device int64
- * [num_seqs, max_seq_len]; slots j >= L_b get -1. */
+ * kernels compute it (same device code: split range, division by block_size,
+ * stride arithmetic), found both ways they find it: from the page table staged
+ * in LDS (the multi-row kernel) and from the block-table row in global memory
+ * (the single-query split kernel). k_off, v_off: device int64
+ * [num_seqs, max_seq_len]; a live token whose page entry is outside
+ * [0, num_pages) gets -2, one on which the two ways disagree gets -3; slots
+ * j >= L_b get -1. */
 int pkv_debug_token_offsets(const pkv_decode_params* p, const int32_t* block_table,
                             const int32_t* seq_lens, int32_t kv_head,
                             int64_t* k_off, int64_t* v_off, void* stream);

@@ -323,7 +323,8 @@ def paged_prefill_attention(q, k_cache, v_cache, block_table, seq_lens, cu_seqle
 
 
 def debug_token_offsets(p: DecodeParams, block_table, seq_lens, kv_head: int):
-    """Per-token K and V row offsets as the split kernel computes them ([num_seqs, max_seq_len] int64)."""
+    """Per-token K and V row offsets as the kernels compute them ([num_seqs, max_seq_len] int64;
+    -2 for an invalid page entry, -3 where the staged-table and direct-table paths disagree)."""
     torch = _torch()
     shape = (p.num_seqs, max(p.max_seq_len, 1))
     k_off = torch.empty(shape, dtype=torch.int64, device=block_table.device)
