@@ -89,35 +89,6 @@ __device__ __forceinline__ void head_bcast(float x, float (&out)[G]) {
   if constexpr (G > 7) out[7] = row_bcast<14>(x);
 }
 
-// gfx950 lane swaps. swap32(a, b) returns {[a_lo, b_lo], [a_hi, b_hi]} (wave
-// halves of 32 lanes); swap16(a, b) returns {[a0, b0, a2, b2], [a1, b1, a3, b3]}
-// (16-lane rows). With a == b they pair lane l with l ^ 32, or l ^ 16.
-struct Pair {
-  float lo, hi;
-};
-__device__ __forceinline__ Pair swap32(float a, float b) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
-}
-__device__ __forceinline__ Pair swap16(float a, float b) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
-}
-// Max and sum over the 4 rows of a wave (same lane column); every lane gets
-// the result, in a fixed order.
-__device__ __forceinline__ float rows_max(float x) {
-  const Pair p = swap32(x, x);
-  const float y = fmaxf(p.lo, p.hi);
-  const Pair q = swap16(y, y);
-  return fmaxf(q.lo, q.hi);
-}
-__device__ __forceinline__ float rows_sum(float x) {
-  const Pair p = swap32(x, x);
-  const float y = p.lo + p.hi;
-  const Pair q = swap16(y, y);
-  return q.lo + q.hi;
-}
-
 // Reduce-scatter of up to 8 per-lane partial sums over the 16 lanes of a row.
 // Partners are lane ^ 15 (row_mirror), ^ 7 (row_half_mirror), ^ 2 and ^ 1
 // (quad_perm); at each step a lane keeps the half of the heads selected by one

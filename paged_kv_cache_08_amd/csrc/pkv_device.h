@@ -35,6 +35,35 @@ __device__ __forceinline__ float dpp_move_full(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// gfx950 lane swaps. swap32(a, b) returns {[a_lo, b_lo], [a_hi, b_hi]} (wave
+// halves of 32 lanes); swap16(a, b) returns {[a0, b0, a2, b2], [a1, b1, a3, b3]}
+// (16-lane rows). With a == b they pair lane l with l ^ 32, or l ^ 16.
+struct Pair {
+  float lo, hi;
+};
+__device__ __forceinline__ Pair swap32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ Pair swap16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+// Max and sum over the 4 rows of a wave (same lane column); every lane gets
+// the result, in a fixed order.
+__device__ __forceinline__ float rows_max(float x) {
+  const Pair p = swap32(x, x);
+  const float y = fmaxf(p.lo, p.hi);
+  const Pair q = swap16(y, y);
+  return fmaxf(q.lo, q.hi);
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const Pair p = swap32(x, x);
+  const float y = p.lo + p.hi;
+  const Pair q = swap16(y, y);
+  return q.lo + q.hi;
+}
+
 // Two OCP FP8 E4M3 codes of a 32-bit word (bytes 0, 1, or 2, 3 when hi) as an
 // exact bf16 pair, or as two floats (low byte first); one instruction each.
 template <bool HI>

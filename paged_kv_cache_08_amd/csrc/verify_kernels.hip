@@ -22,7 +22,8 @@
 //     layout (lane l: tokens 4(l/16)..+3 of row l%16) is exactly the A-operand
 //     layout of P for O = P V, so P never leaves registers.
 //   * Online softmax per row with the exact tile max (log2 units); rows are
-//     reduced across the four 16-lane groups with two shuffles.
+//     reduced across the four 16-lane groups with two lane swaps
+//     (v_permlane32_swap, v_permlane16_swap), no LDS round trip.
 //   * P is split into bf16 hi + lo (hi = bf16(p), lo = bf16(p - hi)), two MFMAs
 //     per block, so the bf16 operand costs about 2^-16 relative error instead of
 //     2^-9. V enters as the B operand through ds_read_b64_tr_b16: lane j of a
@@ -326,8 +327,7 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
           st[tb][r] = x;
           mt = fmaxf(mt, x);
         }
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt = rows_max(mt);   // the 4 lane groups hold the same row's tokens: lane swaps, no LDS
       const float m_new = mt > m_run + kLazyMax ? mt : m_run;
       const float alpha = fast_exp2(m_run - m_new);
       float ls = 0.0f;
@@ -339,8 +339,7 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
           st[tb][r] = p;
           ls += p;
         }
-      ls += __shfl_xor(ls, 16);
-      ls += __shfl_xor(ls, 32);
+      ls = rows_sum(ls);
       const bool moved = m_new != m_run;
       l_run = l_run * alpha + ls;
       m_run = m_new;
