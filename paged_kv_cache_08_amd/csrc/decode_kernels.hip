@@ -26,17 +26,21 @@ __device__ __forceinline__ float wave_sum64(float x) {
 // out[b,i,h,:] = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s over the
 // sequence's splits with l_s > 0, M = max of their m_s; a row with no such
 // split gets zeros. Workgroup = (64-column block, query head, query row x
-// sequence), 4 waves; wave w sums splits w, w + 4, .... The accumulator loads
-// are issued first. Every wave finds M and the denominator over all splits
-// by itself (wave-wide reductions, the (m, l) pairs are a few hundred bytes)
-// and keeps its weights 2^(m_s - M) in its own LDS row, so the only barrier
-// is the one before the 4 wave sums are added. All sums run in a fixed order.
-template <int D>
-__global__ __launch_bounds__(256) void lse_merge_kernel(DecodeArgs a) {
-  constexpr int kPerWave = 16;    // accumulator loads in flight per thread per pass
-  constexpr int kPass = 4 * kPerWave;
-  __shared__ float sm_w[4][kMergeSplitsLds];
-  __shared__ float part[4][64];
+// sequence), MW waves; wave w sums splits w, w + MW, .... The accumulator
+// loads are issued first. Every wave finds M and the denominator over all
+// splits by itself (wave-wide reductions, the (m, l) pairs are a few hundred
+// bytes) and keeps its weights 2^(m_s - M) in its own LDS row, so the only
+// barrier is the one before the MW wave sums are added. All sums run in a
+// fixed order. MW = 8 (8 splits per wave) for small grids (a batch-1 decode
+// step has 24 (row, head) pairs), MW = 4 (16 splits per wave) otherwise:
+// measured, small grids want more waves with fewer loads each, large grids
+// the opposite.
+template <int D, int MW>
+__global__ __launch_bounds__(64 * MW) void lse_merge_kernel(DecodeArgs a) {
+  constexpr int kPerWave = 64 / MW;   // accumulator loads in flight per thread per pass
+  constexpr int kPass = MW * kPerWave;
+  __shared__ float sm_w[MW][kMergeSplitsLds];
+  __shared__ float part[MW][64];
   const int cb = blockIdx.z, h = blockIdx.y;
   const int i = blockIdx.x % a.q_len, b = blockIdx.x / a.q_len;
   const QRows qr = seq_q_rows(a, b);
@@ -53,7 +57,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(DecodeArgs a) {
   float vals[kPerWave];
 #pragma unroll
   for (int j = 0; j < kPerWave; ++j) {
-    const int sidx = wave + 4 * j;
+    const int sidx = wave + MW * j;
     vals[j] = sidx < ns ? ac[int64_t(sidx) * D + d] : 0.0f;
   }
   // (m, l) of every split; a split with l = 0 (no visible token) gets m = -inf.
@@ -86,13 +90,13 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(DecodeArgs a) {
     if (s0 > 0) {
 #pragma unroll
       for (int j = 0; j < kPerWave; ++j) {
-        const int sidx = s0 + wave + 4 * j;
+        const int sidx = s0 + wave + MW * j;
         vals[j] = sidx < ns ? ac[int64_t(sidx) * D + d] : 0.0f;
       }
     }
 #pragma unroll
     for (int j = 0; j < kPerWave; ++j) {
-      const int sidx = s0 + wave + 4 * j;
+      const int sidx = s0 + wave + MW * j;
       if (sidx < ns) {
         float f;
         if (sidx < kMergeSplitsLds) {
@@ -107,8 +111,11 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(DecodeArgs a) {
   }
   part[wave][lane] = num;
   __syncthreads();
-  if (wave == 0)
-    store_out(a, prow * D + d, ((part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane])) * inv_den);
+  if (wave == 0) {
+    float t = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
+    if constexpr (MW == 8) t += (part[4][lane] + part[5][lane]) + (part[6][lane] + part[7][lane]);
+    store_out(a, prow * D + d, t * inv_den);
+  }
 }
 
 // The merge for plans of at most kFewSplits splits (short contexts, batched
@@ -239,12 +246,20 @@ hipError_t launch_lse_merge(const DecodeArgs& a, int head_dim, hipStream_t st) {
     return hipGetLastError();
   }
   dim3 grid(a.q_len * a.num_seqs, a.hq, head_dim / 64);
-  if (head_dim == 256)
-    hipLaunchKernelGGL(lse_merge_kernel<256>, grid, dim3(256), 0, st, a);
-  else if (head_dim == 128)
-    hipLaunchKernelGGL(lse_merge_kernel<128>, grid, dim3(256), 0, st, a);
-  else
+  const bool small = int64_t(a.q_len) * a.num_seqs * a.hq < 128;
+  if (head_dim == 256) {
+    if (small)
+      hipLaunchKernelGGL((lse_merge_kernel<256, 8>), grid, dim3(512), 0, st, a);
+    else
+      hipLaunchKernelGGL((lse_merge_kernel<256, 4>), grid, dim3(256), 0, st, a);
+  } else if (head_dim == 128) {
+    if (small)
+      hipLaunchKernelGGL((lse_merge_kernel<128, 8>), grid, dim3(512), 0, st, a);
+    else
+      hipLaunchKernelGGL((lse_merge_kernel<128, 4>), grid, dim3(256), 0, st, a);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
