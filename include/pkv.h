@@ -119,10 +119,13 @@ int pkv_validate_params(const pkv_decode_params* p);
  *   *num_splits = ceil(n_tiles / c); *chunk_tokens = c * T.
  * Sequence b with n_b query rows sees tokens [lo_b, L_b), lo_b = 0, or
  * max(0, L_b - n_b + 1 - window) with a window; it uses
- * ceil((L_b - lo_b) / chunk) splits and split s covers
- * [lo_b + s * chunk, min(lo_b + (s + 1) * chunk, L_b)). A split never exceeds
- * max_tiles * T tokens (one unrolled window of the split kernel), so a
- * requested num_splits may be raised. cu_count must be >= 1. */
+ * n_split_b = ceil((L_b - lo_b) / chunk) splits. On the multi-row kernel
+ * split s covers [lo_b + s * chunk, min(lo_b + (s + 1) * chunk, L_b)). The
+ * single-query split kernel deals the same number of splits out strided:
+ * [lo_b, L_b) in blocks of 32 tokens, block k to split k mod n_split_b (at
+ * most chunk / 32 blocks per split); see pkv_debug_token_splits. A split
+ * never exceeds max_tiles * T tokens (one unrolled window of the split
+ * kernel), so a requested num_splits may be raised. cu_count must be >= 1. */
 int pkv_plan_splits(const pkv_decode_params* p, int32_t cu_count,
                     int32_t* num_splits, int32_t* chunk_tokens);
 
@@ -248,11 +251,23 @@ int pkv_debug_token_offsets(const pkv_decode_params* p, const int32_t* block_tab
                             const int32_t* seq_lens, int32_t kv_head,
                             int64_t* k_off, int64_t* v_off, void* stream);
 
-/* Debug: every split's token range [begin, end) as the split kernel derives it.
- * ranges: device int32 [num_seqs, num_splits, 2] for the planned num_splits
- * (pkv_plan_splits with the device CU count); unused splits get [L, L). */
+/* Debug: every split's token range [begin, end) as the multi-row kernel
+ * derives it (contiguous splits, pkv_plan_splits). ranges: device int32
+ * [num_seqs, num_splits, 2] for the planned num_splits (pkv_plan_splits with
+ * the device CU count); unused splits get [L, L). */
 int pkv_debug_split_ranges(const pkv_decode_params* p, const int32_t* seq_lens,
                            int32_t* ranges, void* stream);
+
+/* Debug: which split, and which slot of its window, the single-query split
+ * kernel reads each token with (same device code as the kernel: sequence
+ * span, split count, strided block mapping, sub-steps per split). p must
+ * describe a q_len == 1 call (else PKV_ERR_INVALID). slots: device int32
+ * [num_seqs, max_seq_len, 2], (split, slot) per token, where slot
+ * j * 32 + r is row r of sub-step j; tokens no split reads (outside
+ * [lo_b, L_b)) get (-1, -1). The split plan of the call
+ * (pkv_plan_splits with the device CU count) gives num_splits and chunk. */
+int pkv_debug_token_splits(const pkv_decode_params* p, const int32_t* seq_lens,
+                           int32_t* slots, void* stream);
 
 /* Host self-check of the division by an invariant integer used for
  * token / block_size (Granlund & Montgomery, PLDI 1994, unsigned case): returns

@@ -61,6 +61,7 @@ __all__ = [
     "bf16_bits_to_f64", "fp8_e4m3_to_f64", "kv_widen", "page_of", "token_offsets_ref", "gather_token_rows",
     "kv_head_of", "last_visible", "first_visible", "paged_attention_ref", "paged_attention_varlen_ref",
     "partial_stats_ref", "merge_partials_ref", "split_attention_ref", "split_plan_ref", "split_ranges_ref",
+    "decode_token_splits_ref",
     "kv_bytes_ref",
 ]
 
@@ -319,6 +320,11 @@ def split_attention_ref(q, k_cache, v_cache, block_table, seq_lens, block_size: 
 #   max(0, L_b - n_b + 1 - window) with a window; it uses
 #   S_b = ceil((L_b - lo_b) / chunk) splits and split s covers
 #   [lo_b + s * chunk, min(lo_b + (s + 1) * chunk, L_b)).
+#   The single-query kernel deals the same S_b splits out strided instead:
+#   [lo_b, L_b) in blocks of 32 tokens, block k to split k mod S_b, where it
+#   is the (k div S_b)-th block of that split (window slots of 32 tokens).
+#   The merge is exact for any partition of the tokens, so only the grouping
+#   (hence the rounding order) differs; the mapping itself is index work.
 # ---------------------------------------------------------------------------
 
 def _cdiv(a: int, b: int) -> int:
@@ -355,6 +361,26 @@ def split_ranges_ref(seq_lens, num_splits: int, chunk: int, window: int = 0, row
             lo = min(first + s * chunk, L)
             hi = min(first + (s + 1) * chunk, L)
             r[b, s] = (lo, hi)
+    return r
+
+
+def decode_token_splits_ref(seq_lens, num_splits: int, chunk: int, window: int = 0,
+                            max_seq_len: int | None = None, block: int = 32) -> np.ndarray:
+    """[num_seqs, max_seq_len, 2] int32: (split, window slot) of every token the
+    single-query kernel reads; (-1, -1) outside the sequence's visible range.
+    Written token by token from the rule above: offset u = t - lo_b, block
+    k = u // block, split k % S_b, slot (k // S_b) * block + u % block."""
+    seq_lens = [int(x) for x in np.asarray(seq_lens).tolist()]
+    width = max(seq_lens + [1]) if max_seq_len is None else max(int(max_seq_len), 1)
+    r = np.full((len(seq_lens), width, 2), -1, dtype=np.int32)
+    for b, L in enumerate(seq_lens):
+        lo = max(0, L - window) if window > 0 else 0
+        S_b = _cdiv(L - lo, chunk)
+        assert S_b <= num_splits, "the plan covers every visible token"
+        for t in range(lo, L):
+            u = t - lo
+            k = u // block
+            r[b, t] = (k % S_b, (k // S_b) * block + u % block)
     return r
 
 

@@ -80,6 +80,7 @@ _SIGNATURES = {
     "pkv_set_timing_events": (ctypes.c_int, [_vp, _vp]),
     "pkv_debug_token_offsets": (ctypes.c_int, [_P, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp]),
     "pkv_debug_split_ranges": (ctypes.c_int, [_P, _vp, _vp, _vp]),
+    "pkv_debug_token_splits": (ctypes.c_int, [_P, _vp, _vp, _vp]),
     "pkv_magic_div_check": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int64]),
     "pkv_read_error_word": (ctypes.c_int, [_vp, _i32p]),
 }
@@ -336,13 +337,24 @@ def debug_token_offsets(p: DecodeParams, block_table, seq_lens, kv_head: int):
 
 
 def debug_split_ranges(p: DecodeParams, seq_lens):
-    """[num_seqs, S, 2] split ranges as the split kernel derives them."""
+    """[num_seqs, S, 2] contiguous split ranges as the multi-row kernel derives them."""
     torch = _torch()
     S, _ = plan_splits(p, device_cu_count())
     r = torch.empty((p.num_seqs, S, 2), dtype=torch.int32, device=seq_lens.device)
     stream = torch.cuda.current_stream(seq_lens.device).cuda_stream
     check(lib().pkv_debug_split_ranges(ctypes.byref(p), seq_lens.data_ptr(), r.data_ptr(), stream),
           "pkv_debug_split_ranges")
+    return r
+
+
+def debug_token_splits(p: DecodeParams, seq_lens):
+    """[num_seqs, max_seq_len, 2] int32 (split, window slot) with which the single-query
+    split kernel reads each token; (-1, -1) for tokens no split reads. q_len must be 1."""
+    torch = _torch()
+    r = torch.empty((p.num_seqs, max(p.max_seq_len, 1), 2), dtype=torch.int32, device=seq_lens.device)
+    stream = torch.cuda.current_stream(seq_lens.device).cuda_stream
+    check(lib().pkv_debug_token_splits(ctypes.byref(p), seq_lens.data_ptr(), r.data_ptr(), stream),
+          "pkv_debug_token_splits")
     return r
 
 

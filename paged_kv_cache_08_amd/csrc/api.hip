@@ -461,6 +461,27 @@ int pkv_debug_split_ranges(const pkv_decode_params* p, const int32_t* seq_lens, 
   return PKV_OK;
 }
 
+int pkv_debug_token_splits(const pkv_decode_params* p, const int32_t* seq_lens, int32_t* slots, void* stream) {
+  int rc = pkv_validate_params(p);
+  if (rc) return rc;
+  if (!seq_lens || !slots) return fail(PKV_ERR_INVALID, "a device pointer is NULL");
+  if (p->q_len != 1) return fail(PKV_ERR_INVALID, "the strided splits are those of q_len == 1 calls");
+  int32_t cu = 0;
+  rc = device_cu_count(&cu);
+  if (rc) return rc;
+  int32_t S = 0, chunk = 0;
+  plan(p, cu, &S, &chunk);
+  pkv::DecodeArgs a = make_args(p, S, chunk);
+  a.seq_lens = seq_lens;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  const size_t n = size_t(p->num_seqs) * size_t(p->max_seq_len) * 2 * sizeof(int32_t);
+  if (n > 0 && (e = hipMemsetAsync(slots, 0xff, n, st)) != hipSuccess) return hip_fail(e, "hipMemsetAsync");
+  e = pkv::launch_debug_token_splits(a, p->max_seq_len, slots, st);
+  if (e != hipSuccess) return hip_fail(e, "debug kernel launch");
+  return PKV_OK;
+}
+
 int64_t pkv_magic_div_check(int32_t divisor, int64_t n_max) {
   if (divisor < 1 || n_max < 0 || n_max > 0xffffffffLL) return -2;
   const pkv::MagicDiv md = pkv::make_magic(uint32_t(divisor));

@@ -213,6 +213,25 @@ __global__ void debug_ranges_kernel(DecodeArgs a, int32_t* ranges) {
   }
 }
 
+// Debug: the split and window slot the single-query split kernel reads each
+// token with, written forward from strided_token() and strided_blocks() the
+// way the kernel derives them: slots[(b * max_seq_len + t) * 2] = split,
+// [... + 1] = slot. Tokens that no slot reads keep what the host wrote.
+__global__ __launch_bounds__(kMaxChunk) void debug_token_splits_kernel(DecodeArgs a, int max_seq_len, int win,
+                                                                       int32_t* slots) {
+  const int s = blockIdx.x, b = blockIdx.y;
+  const SplitSpan sp = split_span(a, b, s, 1);
+  if (sp.begin >= sp.L) return;
+  const int n_sub = strided_blocks(sp, s);
+  for (int i = threadIdx.x; i < win; i += blockDim.x) {
+    const int t = strided_token(sp.lo, sp.nsplit, s, i);
+    if (i / kBlockTokens < n_sub && t < sp.L && t < max_seq_len) {
+      slots[(int64_t(b) * max_seq_len + t) * 2] = s;
+      slots[(int64_t(b) * max_seq_len + t) * 2 + 1] = i;
+    }
+  }
+}
+
 }  // namespace
 
 bool decode_supported(int head_dim, int group) {
@@ -267,6 +286,13 @@ hipError_t launch_debug_offsets(const DecodeArgs& a, int kv_head, int max_seq_le
                                 int64_t* v_off, hipStream_t st) {
   dim3 grid(a.num_splits, a.num_seqs);
   hipLaunchKernelGGL(debug_offsets_kernel, grid, dim3(kThreads), 0, st, a, kv_head, max_seq_len, k_off, v_off);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_token_splits(const DecodeArgs& a, int max_seq_len, int32_t* slots, hipStream_t st) {
+  dim3 grid(a.num_splits, a.num_seqs);
+  hipLaunchKernelGGL(debug_token_splits_kernel, grid, dim3(kMaxChunk), 0, st, a, max_seq_len,
+                     decode_window(a.chunk), slots);
   return hipGetLastError();
 }
 

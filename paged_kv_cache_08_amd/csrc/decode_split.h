@@ -14,8 +14,14 @@
 // paragraph of "vLLM 下双卡 Radeon 上的混合 SSM 解码速率".
 //
 // Work mapping (one workgroup = one split of one (sequence, KV head)):
-//   * 8 waves (2 per SIMD) x 4 token rows per wave: 32 consecutive logical
-//     tokens per sub-step, one token row per 16-lane DPP row. Each lane owns
+//   * Splits are strided: the sequence's context is dealt out in blocks of
+//     32 tokens, block k to split k mod n (n = the sequence's split count),
+//     so the n workgroups of a (sequence, KV head) stream neighbouring blocks
+//     at the same time. (Bare reads of the same bytes finish about 3% sooner
+//     when the whole chip streams one band than with n bands far apart.)
+//   * 8 waves (2 per SIMD) x 4 token rows per wave: one block of 32
+//     consecutive logical tokens per sub-step, one token row per 16-lane DPP
+//     row. Each lane owns
 //     D/16 head-dim elements of its row and loads them with 16-byte global
 //     loads (a 512-byte K row of D = 256 is read by 16 lanes in two fully used
 //     256-byte segments). The G query heads of the group all use the row held
@@ -31,11 +37,12 @@
 //   * V pass: with the exact maximum of the lane's own window scores, each
 //     probability is computed once per (token, head), broadcast to the row with
 //     DPP row_newbcast, and accumulated with fp32 FMAs.
-//   * Token offsets: one thread per window token divides the token index by
+//   * Token offsets: one thread per window slot divides its token index by
 //     the page size (multiply-high), reads the block-table entry and stores
 //     the token's K and V row offsets in LDS, once per split (without a
-//     sliding window, while seq_lens is still in flight); a masked token gets
-//     the offset of the q row. A lane then costs one LDS read and one address
+//     sliding window, while seq_lens is still in flight, for the stride of a
+//     sequence that uses every split); a masked slot gets the offset of the
+//     q row. A lane then costs one LDS read and one address
 //     add per K or V row, instead of every lane of a row repeating the
 //     division and the table lookup.
 //   * Epilogue: the 4 token rows of a wave are merged by a reduce-scatter over
@@ -64,6 +71,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kLanesPerRow = 16;
 constexpr int kRowsPerWave = 64 / kLanesPerRow;
 constexpr int kStep = kWaves * kRowsPerWave;   // tokens per workgroup sub-step
+static_assert(kStep == kBlockTokens, "a sub-step reads one strided block of the split");
 // Register ring depth (steps in flight + 1); shallower where G * D leaves
 // fewer registers (depths 4..10 measured alike at G = 6, D = 256).
 constexpr int ring_depth(int D, int G) { return (D == 256 && G >= 7) ? 3 : 6; }
@@ -166,16 +174,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   const uint8_t* const kbase = reinterpret_cast<const uint8_t*>(a.k) + elem_d<FP8, kEpl>(col, 0) * kEsz;
   const uint8_t* const vbase = reinterpret_cast<const uint8_t*>(a.v) + elem_d<FP8, kEpl>(col, 0) * kEsz;
 
-  // One thread per window token finds its K and V rows. The loads the
+  // One thread per window slot finds its token's K and V rows. The loads the
   // start-up waits on are issued together: the sequence length and the
-  // block-table entry of the thread's token. Without a sliding window
-  // the split starts at s * chunk for every sequence length, so the entry
-  // needs no length; the token index is clamped into the mapped range, so
-  // the load needs no branch (an entry beyond the split is read but unused).
+  // block-table entry of the slot's token. Without a sliding window the
+  // entry is fetched before the length is known, for the stride of a
+  // sequence that uses every planned split (the token index is clamped into
+  // the mapped range, so the load needs no branch); a sequence with fewer
+  // splits, or a window, fetches it again once the length is known.
   const int L_in = a.seq_lens[b];
   int e_tok = -1;
   if (a.window == 0) {
-    const int t = min(s * a.chunk + min(tid, a.chunk - 1), planned_cap(a) - 1);
+    const int t = min(strided_token(0, a.num_splits, s, min(tid, kWin - 1)), planned_cap(a) - 1);
     e_tok = table_entry(a, b, t);
   }
 
@@ -185,10 +194,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
       for (int i = tid; i < G * D; i += kThreads) store_out(a, out_row0 + i, 0.0f);
     return;
   }
-  const bool live = sp.begin + tid < sp.end;   // implies tid < chunk
-  if (a.window > 0 && live) e_tok = table_entry(a, b, sp.begin + tid);
+  const int t_tok = strided_token(sp.lo, sp.nsplit, s, min(tid, kWin - 1));
+  const bool live = tid < kWin && t_tok < sp.L;
+  if ((a.window > 0 || sp.nsplit != a.num_splits) && live) e_tok = table_entry(a, b, t_tok);
   int64_t ko = kmask, vo = vmask;
-  const bool entry_ok = token_row_entry(a, e_tok, g, sp.begin + tid, ko, vo);
+  const bool entry_ok = token_row_entry(a, e_tok, g, t_tok, ko, vo);
   if (tid < kWin) {
     const bool ok = live && entry_ok;
     tok_k[tid] = ok ? ko : kmask;
@@ -207,10 +217,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
     for (int k = 0; k < kCq; ++k)
       qv[h][k] = *reinterpret_cast<const uint4*>(a.q + out_row0 + h * D + elem_d<FP8, kEpl>(col, 8 * k));
 
-  // The split is one window of at most kSubSteps sub-steps of kStep tokens;
-  // row `row` of wave `wave` owns window tokens j * kStep + my.
+  // The split is one window of at most kSubSteps sub-steps of kStep tokens
+  // (one strided block each); row `row` of wave `wave` owns window slots
+  // j * kStep + my.
   const int my = wave * kRowsPerWave + row;
-  const int n_sub = (sp.end - sp.begin + kStep - 1) / kStep;   // uniform, <= kSubSteps
+  const int n_sub = strided_blocks(sp, s);   // uniform, <= kSubSteps
 
   float acc[G][kEpl];
 #pragma unroll

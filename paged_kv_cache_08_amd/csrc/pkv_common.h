@@ -110,6 +110,7 @@ hipError_t launch_lse_merge(const DecodeArgs& a, int head_dim, hipStream_t st);
 hipError_t launch_debug_offsets(const DecodeArgs& a, int kv_head, int max_seq_len,
                                 int64_t* k_off, int64_t* v_off, hipStream_t st);
 hipError_t launch_debug_ranges(const DecodeArgs& a, int32_t* ranges, hipStream_t st);
+hipError_t launch_debug_token_splits(const DecodeArgs& a, int max_seq_len, int32_t* slots, hipStream_t st);
 bool decode_supported(int head_dim, int group);
 bool verify_supported(int head_dim, int group, int q_len);
 

@@ -138,6 +138,27 @@ __device__ __forceinline__ SplitSpan split_span(const DecodeArgs& a, int b, int 
   return split_span_len(a, a.seq_lens[b], s, rows);
 }
 
+// The single-query split kernel deals its splits out strided: [lo, L) is cut
+// into blocks of kBlockTokens tokens and split s of the sequence's n = nsplit
+// splits takes blocks s, s + n, s + 2n, ... (the same number of splits as the
+// contiguous plan, and at most chunk / kBlockTokens blocks each, since the
+// plan gives n * chunk >= L - lo). Slot i of the split's window holds token
+// lo + kBlockTokens * (s + (i / kBlockTokens) * n) + i % kBlockTokens; the
+// slot is live while that token is below L. At any moment the splits of one
+// sequence then stream one band of the context together instead of n bands
+// far apart.
+constexpr int kBlockTokens = 32;
+
+__device__ __forceinline__ int strided_token(int lo, int nsplit, int s, int i) {
+  return lo + kBlockTokens * (s + (i / kBlockTokens) * nsplit) + i % kBlockTokens;
+}
+
+// Sub-steps of kBlockTokens tokens that split s (< sp.nsplit) reads.
+__device__ __forceinline__ int strided_blocks(const SplitSpan& sp, int s) {
+  const int nb = (sp.L - sp.lo + kBlockTokens - 1) / kBlockTokens;
+  return (nb - s + sp.nsplit - 1) / sp.nsplit;
+}
+
 // Query rows of sequence b: rows [base, base + n) of the packed q and out.
 // Uniform calls: base = b * q_len, n = q_len. Varlen calls take them from
 // cu_q and check 0 <= cu_q[b] <= cu_q[b + 1] <= cu_q[num_seqs],

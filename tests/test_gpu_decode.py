@@ -273,6 +273,24 @@ def test_split_ranges_bit_exact(name, make):
         np.testing.assert_array_equal(r.cpu().numpy(), O.split_ranges_ref(case.seq_lens, S, chunk))
 
 
+@pytest.mark.parametrize("name,make", INDEX_CASES, ids=[c[0] for c in INDEX_CASES])
+def test_strided_token_splits_bit_exact(name, make):
+    import torch
+    import paged_kv_cache_08_amd as P
+    log(f"case: strided token splits, {name}")
+    case = make()
+    q, k, v, table, lens = to_device(case)
+    cu = P.device_cu_count()
+    for forced in (0, 3, 1000):
+        p = P.make_params(q, k, v, table, case.block_size, case.scale, max_seq_len=case.max_seq_len,
+                          num_splits=forced)
+        S, chunk = P.plan_splits(p, cu)
+        r = P.debug_token_splits(p, lens)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(r.cpu().numpy(), O.decode_token_splits_ref(
+            case.seq_lens, S, chunk, max_seq_len=case.max_seq_len))
+
+
 @pytest.mark.parametrize("hq,hkv,d,bs,lens", [
     (24, 2, 256, 784, [32768]),        # 12 query heads per KV head
     (32, 2, 128, 16, [5000, 17, 0]),   # 16 per KV head

@@ -75,6 +75,22 @@ def test_window_page_sizes_bitwise():
     np.testing.assert_array_equal(outs[2], outs[0])
 
 
+@pytest.mark.parametrize("window,forced", [(2048, 0), (300, 3), (1, 0), (40000, 0)])
+def test_window_strided_token_splits_bit_exact(window, forced):
+    import torch
+    import paged_kv_cache_08_amd as P
+    log(f"case: strided token splits with window {window}, forced {forced}")
+    case = W.make_case(989, [32768, 5000, 2047, 3, 0], block_size=784, interleave=True, poison=False)
+    q, k, v, table, lens = to_device(case)
+    p = P.make_params(q, k, v, table, case.block_size, case.scale, max_seq_len=case.max_seq_len,
+                      num_splits=forced, window=window)
+    S, chunk = P.plan_splits(p, P.device_cu_count())
+    r = P.debug_token_splits(p, lens)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(r.cpu().numpy(), O.decode_token_splits_ref(
+        case.seq_lens, S, chunk, window=window, max_seq_len=case.max_seq_len))
+
+
 @pytest.mark.parametrize("ql,window,forced", [(1, 2048, 0), (1, 300, 3), (16, 2048, 0), (4, 1, 0)])
 def test_window_split_ranges_bit_exact(ql, window, forced):
     import torch

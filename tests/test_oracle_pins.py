@@ -374,6 +374,72 @@ def test_split_plan_invariants(ns, hkv, L, bs, cu, total, forced):
         assert all(r[b, s, 1] == r[b, s + 1, 0] for s in range(S - 1))
 
 
+def test_decode_token_splits_worked_example():
+    # 200 tokens, chunk 64: ceil(200 / 64) = 4 splits for this sequence even
+    # though the launch plans 8; seven 32-token blocks go to splits
+    # 0, 1, 2, 3, 0, 1, 2, the second block of a split at slots 32 .. 63.
+    r = O.decode_token_splits_ref([200, 0], 8, 64)
+    assert r.shape == (2, 200, 2)
+    assert [int(r[0, 32 * k, 0]) for k in range(7)] == [0, 1, 2, 3, 0, 1, 2]
+    assert r[0, 0].tolist() == [0, 0] and r[0, 31].tolist() == [0, 31]
+    assert r[0, 128].tolist() == [0, 32] and r[0, 159].tolist() == [0, 63]
+    assert r[0, 96].tolist() == [3, 0] and r[0, 199].tolist() == [2, 32 + 7]
+    assert np.all(r[1] == -1)
+    # A sliding window of 150 over 300 tokens: visible [150, 300), 3 splits of
+    # 64, five blocks to splits 0, 1, 2, 0, 1.
+    w = O.decode_token_splits_ref([300], 8, 64, window=150)
+    assert np.all(w[0, :150] == -1)
+    assert w[0, 150].tolist() == [0, 0] and w[0, 182].tolist() == [1, 0] and w[0, 214].tolist() == [2, 0]
+    assert w[0, 246].tolist() == [0, 32] and w[0, 278].tolist() == [1, 32] and w[0, 299].tolist() == [1, 53]
+
+
+@pytest.mark.parametrize("ns,hkv,L,bs,cu,total,forced", PLAN_CASES)
+@pytest.mark.parametrize("window", [0, 2048])
+def test_decode_token_splits_invariants(ns, hkv, L, bs, cu, total, forced, window):
+    S, chunk = O.split_plan_ref(ns, hkv, L, bs, cu, total_tokens=total, forced_splits=forced, window=window)
+    lens = [L] + [max(0, L - 1717 * k) for k in range(1, min(ns, 4))]
+    r = O.decode_token_splits_ref(lens, S, chunk, window=window, max_seq_len=L)
+    ranges = O.split_ranges_ref(lens, S, chunk, window=window)
+    for b, Lb in enumerate(lens):
+        lo = max(0, Lb - window) if window else 0
+        assert np.all(r[b, :lo] == -1) and np.all(r[b, Lb:] == -1)
+        sp, slot = r[b, lo:Lb, 0].astype(np.int64), r[b, lo:Lb, 1].astype(np.int64)
+        S_b = int(np.sum(ranges[b, :, 1] > ranges[b, :, 0]))     # same split count as the contiguous plan
+        assert (Lb == lo and S_b == 0) or (sp.min() == 0 and sp.max() == S_b - 1)
+        assert np.all(slot >= 0) and np.all(slot < chunk)       # a split fits its window
+        u = np.arange(Lb - lo)
+        assert np.array_equal(slot % 32, u % 32)                 # rows of a block stay together
+        assert len(set(zip(sp.tolist(), slot.tolist()))) == Lb - lo   # one token per (split, slot)
+        blk = u // 32
+        assert np.array_equal(sp, blk % max(S_b, 1))              # block k to split k mod S_b
+        if S_b:
+            counts = np.bincount(sp, minlength=S_b)
+            assert counts.max() - counts.min() <= 32              # balanced to within one block
+
+
+@pytest.mark.parametrize("window", [0, 100])
+def test_strided_decode_splits_merge_to_the_direct_result(window):
+    case = W.make_case(37, [1500, 63, 1, 0], q_len=1, block_size=784, interleave=True, boost_frac=0.05)
+    ref = O.paged_attention_ref(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                                case.block_size, case.scale, window)
+    S, chunk = 12, 128
+    r = O.decode_token_splits_ref(case.seq_lens, S, chunk, window=window)
+    ranges = []
+    for b in range(case.num_seqs):
+        # each split's tokens as its 32-token runs, split after split, slot order
+        runs = []
+        for s in range(S):
+            toks = sorted((int(r[b, t, 1]), t) for t in np.nonzero(r[b, :, 0] == s)[0])
+            for i in range(0, len(toks), 32):
+                blk = [t for _, t in toks[i:i + 32]]
+                assert blk == list(range(blk[0], blk[0] + len(blk)))
+                runs.append((blk[0], blk[-1] + 1))
+        ranges.append(runs or [(0, 0)])
+    got = O.split_attention_ref(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                                case.block_size, case.scale, ranges, window)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
+
+
 def test_split_plan_headline_shape():
     # 32K tokens x 4 KV heads spread over 256 CUs: 64 splits of 512 tokens per KV head.
     assert O.split_plan_ref(1, 4, 32768, 784, 256) == (64, 512)
