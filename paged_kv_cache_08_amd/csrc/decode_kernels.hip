@@ -26,19 +26,23 @@ __device__ __forceinline__ float wave_sum64(float x) {
 // out[b,i,h,:] = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s over the
 // sequence's splits with l_s > 0, M = max of their m_s; a row with no such
 // split gets zeros. Workgroup = (64-column block, query head, query row x
-// sequence), MW waves; wave w sums splits w, w + MW, .... The accumulator
-// loads are issued first. Every wave finds M and the denominator over all
-// splits by itself (wave-wide reductions, the (m, l) pairs are a few hundred
-// bytes) and keeps its weights 2^(m_s - M) in its own LDS row, so the only
-// barrier is the one before the MW wave sums are added. All sums run in a
+// sequence), MW waves; wave w sums splits w, w + MW, .... The first
+// accumulator loads are issued as early as possible (see kAhead). Every wave
+// finds M and the denominator over all splits by itself (wave-wide
+// reductions, the (m, l) pairs are a few hundred bytes) and keeps its
+// weights 2^(m_s - M) in its own LDS row, so the only barrier is the one
+// before the MW wave sums are added. All sums run in a
 // fixed order. MW = 8 (8 splits per wave) for small grids (a batch-1 decode
 // step has 24 (row, head) pairs), MW = 4 (16 splits per wave) otherwise:
 // measured, small grids want more waves with fewer loads each, large grids
-// the opposite.
+// the opposite. Small grids also load their first pass before the sequence
+// length is known (32K decode step -0.4 us); in large grids of mostly short
+// sequences those loads of unused splits cost more than they save.
 template <int D, int MW>
 __global__ __launch_bounds__(64 * MW) void lse_merge_kernel(DecodeArgs a) {
   constexpr int kPerWave = 64 / MW;   // accumulator loads in flight per thread per pass
   constexpr int kPass = MW * kPerWave;
+  constexpr bool kAhead = MW == 8;    // small grids: latency-bound, load ahead of the length
   __shared__ float sm_w[MW][kMergeSplitsLds];
   __shared__ float part[MW][64];
   const int cb = blockIdx.z, h = blockIdx.y;
@@ -47,33 +51,44 @@ __global__ __launch_bounds__(64 * MW) void lse_merge_kernel(DecodeArgs a) {
   if (i >= qr.n) return;          // no such row in a varlen batch
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int d = cb * 64 + lane;
-  const SplitSpan sp = split_span(a, b, 0, qr.n);
-  if (sp.nsplit <= 1) return;    // written by the split kernel
-  const int ns = sp.nsplit;
   const int64_t prow = (int64_t(qr.base) + i) * a.hq + h;
   const float* ml = a.part_ml + prow * a.num_splits * 2;
   const float* ac = a.part_acc + prow * a.num_splits * D;
-
+  // The first pass of accumulators and the first 64 (m, l) pairs. With
+  // kAhead they are loaded for every planned split before the sequence
+  // length arrives (the row is known without a load unless the call is
+  // varlen): one memory round trip instead of two, values of splits the
+  // sequence does not use dropped, and no branch between these loads and
+  // their first use, so they stay ahead of the wait for the length.
+  // Otherwise only the splits the sequence uses are loaded, once the length
+  // is known.
   float vals[kPerWave];
+  float2 ml0;
+  auto load_first = [&](int n) {
 #pragma unroll
-  for (int j = 0; j < kPerWave; ++j) {
-    const int sidx = wave + MW * j;
-    vals[j] = sidx < ns ? ac[int64_t(sidx) * D + d] : 0.0f;
+    for (int j = 0; j < kPerWave; ++j) {
+      const int sidx = wave + MW * j;
+      vals[j] = sidx < n ? ac[int64_t(sidx) * D + d] : 0.0f;
+    }
+    ml0 = lane < n ? reinterpret_cast<const float2*>(ml)[lane] : make_float2(0.0f, 0.0f);
+  };
+  if constexpr (kAhead) load_first(a.num_splits);
+  const SplitSpan sp = split_span(a, b, 0, qr.n);
+  const int ns = sp.nsplit;      // <= 1: the split kernel wrote the output
+  if constexpr (!kAhead) {
+    if (ns <= 1) return;
+    load_first(ns);
   }
   // (m, l) of every split; a split with l = 0 (no visible token) gets m = -inf.
-  float mloc = -INFINITY;
-  for (int t = lane; t < ns; t += 64) {
+  float mloc = lane < ns && ml0.y > 0.0f ? ml0.x : -INFINITY;
+  for (int t = lane + 64; t < ns; t += 64) {
     const float2 v = reinterpret_cast<const float2*>(ml)[t];
     mloc = fmaxf(mloc, v.y > 0.0f ? v.x : -INFINITY);
   }
-  const float M = wave_max64(mloc);   // the same in every wave
-  if (M == -INFINITY) {
-    if (wave == 0) store_out(a, prow * D + d, 0.0f);
-    return;
-  }
+  const float M = wave_max64(mloc);   // the same in every wave; -inf: no split has a visible token
   float dloc = 0.0f;
   for (int t = lane; t < ns; t += 64) {
-    const float2 v = reinterpret_cast<const float2*>(ml)[t];
+    const float2 v = t < 64 ? ml0 : reinterpret_cast<const float2*>(ml)[t];
     const float f = v.y > 0.0f ? fast_exp2(v.x - M) : 0.0f;   // 0 for empty splits
     dloc += f * v.y;
     if (t < kMergeSplitsLds) sm_w[wave][t] = f;
@@ -85,14 +100,19 @@ __global__ __launch_bounds__(64 * MW) void lse_merge_kernel(DecodeArgs a) {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
+  // First pass from the registers loaded up front; an unused split adds 0.
   float num = 0.0f;
-  for (int s0 = 0; s0 < ns; s0 += kPass) {
-    if (s0 > 0) {
 #pragma unroll
-      for (int j = 0; j < kPerWave; ++j) {
-        const int sidx = s0 + wave + MW * j;
-        vals[j] = sidx < ns ? ac[int64_t(sidx) * D + d] : 0.0f;
-      }
+  for (int j = 0; j < kPerWave; ++j) {
+    const int sidx = wave + MW * j;   // < 64 <= kMergeSplitsLds
+    const float f = sidx < ns ? sm_w[wave][sidx] : 0.0f;
+    num += f * (sidx < ns ? vals[j] : 0.0f);
+  }
+  for (int s0 = kPass; s0 < ns; s0 += kPass) {
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j) {
+      const int sidx = s0 + wave + MW * j;
+      vals[j] = sidx < ns ? ac[int64_t(sidx) * D + d] : 0.0f;
     }
 #pragma unroll
     for (int j = 0; j < kPerWave; ++j) {
@@ -111,10 +131,10 @@ __global__ __launch_bounds__(64 * MW) void lse_merge_kernel(DecodeArgs a) {
   }
   part[wave][lane] = num;
   __syncthreads();
-  if (wave == 0) {
+  if (wave == 0 && ns > 1) {
     float t = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
     if constexpr (MW == 8) t += (part[4][lane] + part[5][lane]) + (part[6][lane] + part[7][lane]);
-    store_out(a, prow * D + d, t * inv_den);
+    store_out(a, prow * D + d, M == -INFINITY ? 0.0f : t * inv_den);
   }
 }
 
