@@ -25,7 +25,8 @@
 //     D/16 head-dim elements of its row and loads them with 16-byte global
 //     loads (a 512-byte K row of D = 256 is read by 16 lanes in two fully used
 //     256-byte segments). The G query heads of the group all use the row held
-//     in registers, so K and V are fetched once per group.
+//     in registers, so K and V are fetched once per group. The K/V loads are
+//     non-temporal: each byte is read once per call.
 //   * The split is one window, fully unrolled: a K pass over its NS sub-steps,
 //     then a V pass over the same tokens. Loads run through a ring of register
 //     buffers that spans both passes, so the first V loads are in flight while
@@ -76,6 +77,15 @@ static_assert(kStep == kBlockTokens, "a sub-step reads one strided block of the 
 // fewer registers (depths 4..10 measured alike at G = 6, D = 256).
 constexpr int ring_depth(int D, int G) { return (D == 256 && G >= 7) ? 3 : 6; }
 constexpr float kMinit = -1.0e30f;             // floor of a row's max (finite: no inf - inf)
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// 16 bytes read with a non-temporal load (global_load_dwordx4 ... nt).
+__device__ __forceinline__ uint4 load_stream16(const uint8_t* p) {
+  const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
 
 // Lane n of each 16-lane row, broadcast to the whole row (DPP row_newbcast).
 template <int N>
@@ -234,18 +244,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   float m_row = kMinit, l_row = 0.0f;
 
   uint4 ring[kRing][kCpl];
-  // One lane's piece of a K or V row: bf16 kCpl 16-byte loads; FP8 kEpl bytes.
+  // One lane's piece of a K or V row: bf16 kCpl 16-byte loads; FP8 kEpl
+  // bytes. Every K/V byte is read once per call, so the loads are
+  // non-temporal (streaming cache policy).
   auto load_row = [&](const uint8_t* p, uint4 (&buf)[kCpl]) {
     if constexpr (FP8) {
       if constexpr (kEpl == 16) {
-        buf[0] = *reinterpret_cast<const uint4*>(p);
+        buf[0] = load_stream16(p);
       } else {
-        const uint2 h = *reinterpret_cast<const uint2*>(p);
-        buf[0] = make_uint4(h.x, h.y, 0u, 0u);
+        const u32x2_t h = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+        buf[0] = make_uint4(h[0], h[1], 0u, 0u);
       }
     } else {
 #pragma unroll
-      for (int k = 0; k < kCpl; ++k) buf[k] = *reinterpret_cast<const uint4*>(p + k * 256);
+      for (int k = 0; k < kCpl; ++k) buf[k] = load_stream16(p + k * 256);
     }
   };
   // K step j: the token's K row (branch-free: a masked token reads the q row).
