@@ -34,7 +34,9 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed steps first; fewer than about 500 leave the first timed region "
+                         "about 5%% slow while the GPU settles (about 30 ms of work at the default size)")
     ap.add_argument("--workload", default="hybrid", choices=["hybrid", "dense", "mixed", "verify", "varlen", "prefill"])
     ap.add_argument("--context", type=int, default=None,
                     help="tokens in the cache (default 32768; 8192 for prefill)")
