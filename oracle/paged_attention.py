@@ -60,6 +60,7 @@ import numpy as np
 __all__ = [
     "bf16_bits_to_f64", "fp8_e4m3_to_f64", "kv_widen", "page_of", "token_offsets_ref", "gather_token_rows",
     "kv_head_of", "last_visible", "first_visible", "paged_attention_ref", "paged_attention_varlen_ref",
+    "paged_attention_lse_ref", "paged_attention_varlen_lse_ref",
     "partial_stats_ref", "merge_partials_ref", "split_attention_ref", "split_plan_ref", "split_ranges_ref",
     "decode_token_splits_ref",
     "kv_bytes_ref",
@@ -232,6 +233,55 @@ def paged_attention_varlen_ref(q_packed, cu_seqlens_q, k_cache, v_cache, block_t
                                          np.asarray(seq_lens)[b:b + 1], block_size, scale, window, kv_dtype,
                                          k_scale, v_scale)[0]
     return out
+
+
+def paged_attention_lse_ref(q, k_cache, block_table, seq_lens, block_size: int, scale: float,
+                            window: int = 0, kv_dtype: str = "bf16", k_scale: float = 1.0) -> np.ndarray:
+    """Log-sum-exp of every row's scaled scores, the softmax normaliser of the
+    definition above: lse[b,i,h] = ln sum_j exp(sigma * q[b,i,h,:] . K_j) over
+    the row's visible tokens j (natural log), -inf for a row that sees none.
+    It is what a caller needs to merge this attention with attention over
+    other keys, the same (max, sum) statistic the split merge combines.
+    Returns float64 [num_seqs, q_len, Hq]."""
+    q = np.asarray(q)
+    ns, q_len, hq, _ = q.shape
+    hkv = np.asarray(k_cache).shape[2]
+    G = hq // hkv
+    sigma = float(np.float32(scale))
+    lse = np.full((ns, q_len, hq), -np.inf, dtype=np.float64)
+    for b in range(ns):
+        L = int(seq_lens[b])
+        if L == 0:
+            continue
+        widen = kv_widen(kv_dtype, k_scale)
+        K = [gather_token_rows(k_cache, block_table[b], L, block_size, g, widen) for g in range(hkv)]
+        for i in range(q_len):
+            pos = last_visible(L, q_len, i)
+            lo = first_visible(pos, window)
+            if pos < lo:
+                continue
+            for h in range(hq):
+                s = _scaled_scores(K[kv_head_of(h, G)][lo: pos + 1], bf16_bits_to_f64(q[b, i, h]), sigma)
+                m = float(s.max())
+                lse[b, i, h] = m + math.log(float(np.exp(s - m).sum()))
+    return lse
+
+
+def paged_attention_varlen_lse_ref(q_packed, cu_seqlens_q, k_cache, block_table, seq_lens, block_size: int,
+                                   scale: float, window: int = 0, kv_dtype: str = "bf16",
+                                   k_scale: float = 1.0) -> np.ndarray:
+    """paged_attention_lse_ref for packed varlen rows: float64 [total_q, Hq]."""
+    q_packed = np.asarray(q_packed)
+    cu = [int(x) for x in np.asarray(cu_seqlens_q).tolist()]
+    lse = np.full(q_packed.shape[:2], -np.inf, dtype=np.float64)
+    for b in range(len(cu) - 1):
+        lo, hi = cu[b], cu[b + 1]
+        if hi == lo:
+            continue
+        lse[lo:hi] = paged_attention_lse_ref(q_packed[None, lo:hi], k_cache, block_table[b:b + 1],
+                                             np.asarray(seq_lens)[b:b + 1], block_size, scale, window,
+                                             kv_dtype, k_scale)[0]
+    return lse
 
 
 # ---------------------------------------------------------------------------

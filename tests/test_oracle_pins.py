@@ -8,6 +8,8 @@
 * invariants: physical-page relabelling, page size, combined vs split cache,
   split-count agreement of the split/merge mode;
 * the page geometry and KV byte counts the pages print (tests/golden);
+* the rows' log-sum-exp: brute force, closed forms (identical keys, zero
+  scale, one token, a window) and the one-more-token identity of causal rows;
 * planted mistakes: a wrong oracle must fail the brute-force pin.
 """
 import json
@@ -748,3 +750,115 @@ def test_planted_fp8_mistakes_fail_the_pins(monkeypatch, name, attr, bad):
     monkeypatch.setattr(O, attr, bad)
     got = _fp8_oracle(case)
     assert not np.allclose(got, ref, rtol=1e-6, atol=1e-8), name
+
+
+# ---------------------------------------------------------------------------
+# Log-sum-exp of the scaled scores (the softmax normaliser each row returns on
+# request, so that callers can merge with attention over other keys).
+# ---------------------------------------------------------------------------
+
+def brute_force_lse(case: W.DecodeCase, window: int = 0) -> np.ndarray:
+    """ln sum_j exp(s_j) over each row's visible tokens, in pure Python on the
+    logical rows (fsum of exp after subtracting the max)."""
+    ns, ql, hq, d = case.q.shape
+    G = hq // case.logical_k[0].shape[1] if case.logical_k else 1
+    sigma = float(np.float32(case.scale))
+    out = np.full((ns, ql, hq), -math.inf)
+    for b in range(ns):
+        L = int(case.seq_lens[b])
+        if L == 0:
+            continue
+        K = case.logical_k[b].tolist()
+        for i in range(ql):
+            p = L - ql + i
+            toks = range(max(0, p - window + 1) if window else 0, p + 1)
+            for h in range(hq):
+                qv = [_widen(x) for x in case.q[b, i, h].tolist()]
+                s = [sigma * math.fsum(qv[e] * _widen(K[j][h // G][e]) for e in range(d)) for j in toks]
+                m = max(s)
+                out[b, i, h] = m + math.log(math.fsum(math.exp(x - m) for x in s))
+    return out
+
+
+@pytest.mark.parametrize("bs,hkv,G,d,lens,ql,window", [
+    (7, 2, 3, 8, [40, 0, 9], 1, 0),
+    (5, 1, 6, 4, [23], 4, 0),
+    (16, 2, 1, 8, [37, 12], 3, 5),
+    (3, 2, 2, 16, [11], 1, 30),
+])
+def test_lse_matches_brute_force(bs, hkv, G, d, lens, ql, window):
+    case = W.make_case(61, lens, q_len=ql, num_q_heads=hkv * G, num_kv_heads=hkv, head_dim=d, block_size=bs,
+                       interleave=True, poison=False)
+    got = O.paged_attention_lse_ref(case.q, case.k_cache, case.block_table, case.seq_lens, case.block_size,
+                                    case.scale, window)
+    want = brute_force_lse(case, window)
+    assert np.array_equal(np.isinf(got), np.isinf(want))
+    fin = np.isfinite(want)
+    np.testing.assert_allclose(got[fin], want[fin], rtol=1e-13, atol=1e-13)
+
+
+def test_lse_closed_forms():
+    # identical keys: lse = s + ln(n); zero scale: ln(n); one token: its score.
+    d, L = 8, 29
+    case = W.make_case(62, [L, 1], q_len=1, num_q_heads=4, num_kv_heads=2, head_dim=d, block_size=5,
+                       poison=False)
+    case.k_cache[...] = case.k_cache[case.block_table[0, 0], 0]
+    sigma = float(np.float32(case.scale))
+    got = O.paged_attention_lse_ref(case.q, case.k_cache, case.block_table, case.seq_lens, 5, case.scale)
+    k_rows = O.bf16_bits_to_f64(case.k_cache[case.block_table[0, 0], 0])     # [Hkv, D]
+    for b, n in ((0, L), (1, 1)):
+        for h in range(4):
+            s = sigma * float(O.bf16_bits_to_f64(case.q[b, 0, h]) @ k_rows[h // 2])
+            assert got[b, 0, h] == pytest.approx(s + math.log(n), rel=1e-14, abs=1e-14)
+    zero = O.paged_attention_lse_ref(case.q, case.k_cache, case.block_table, case.seq_lens, 5, 0.0)
+    np.testing.assert_allclose(zero[0, 0], math.log(L), rtol=1e-15)
+    np.testing.assert_array_equal(zero[1, 0], 0.0)
+    # windows: a row sees min(W, p + 1) tokens
+    w = O.paged_attention_lse_ref(case.q, case.k_cache, case.block_table, case.seq_lens, 5, 0.0, window=10)
+    np.testing.assert_allclose(w[0, 0], math.log(10), rtol=1e-15)
+    # no visible token (empty sequence): -inf
+    e = O.paged_attention_lse_ref(case.q[:1], case.k_cache, case.block_table[:1], np.array([0]), 5, case.scale)
+    assert np.all(np.isneginf(e))
+
+
+def test_lse_rows_extend_by_one_token():
+    # With the same query in every row, row i + 1 sees exactly one more token
+    # than row i: lse_{i+1} = logaddexp(lse_i, s_{p_i + 1}). An off-by-one in
+    # the causal range breaks the identity.
+    L, R = 30, 6
+    case = W.make_case(63, [L], q_len=R, num_q_heads=2, num_kv_heads=1, head_dim=8, block_size=7, poison=False)
+    case.q[0, 1:] = case.q[0, 0]
+    sigma = float(np.float32(case.scale))
+    got = O.paged_attention_lse_ref(case.q, case.k_cache, case.block_table, case.seq_lens, 7, case.scale)
+    K = O.bf16_bits_to_f64(case.logical_k[0])
+    for h in range(2):
+        qv = O.bf16_bits_to_f64(case.q[0, 0, h])
+        for i in range(R - 1):
+            s_new = sigma * float(K[L - R + i + 1, 0] @ qv)
+            assert got[0, i + 1, h] == pytest.approx(np.logaddexp(got[0, i, h], s_new), rel=1e-13)
+
+
+def test_planted_lse_in_log2_units_fails_the_pin(monkeypatch):
+    # An oracle that returned the normaliser in log2 units (as kernels keep it
+    # internally) must fail the brute-force pin.
+    case = W.make_case(64, [20], num_q_heads=2, num_kv_heads=1, head_dim=8, block_size=7, poison=False)
+    real = math.log
+    monkeypatch.setattr(O.math, "log", lambda x: real(x) / real(2.0))
+    got = O.paged_attention_lse_ref(case.q, case.k_cache, case.block_table, case.seq_lens, 7, case.scale)
+    monkeypatch.undo()
+    assert not np.allclose(got, brute_force_lse(case), rtol=1e-6)
+
+
+def test_varlen_lse_equals_per_sequence_calls():
+    case = W.make_case(65, [40, 9, 17], q_len=4, num_q_heads=4, num_kv_heads=2, head_dim=8, block_size=5,
+                       poison=False)
+    cu = np.array([0, 4, 5, 8])
+    packed = np.concatenate([case.q[0, :4], case.q[1, 3:4], case.q[2, 1:4]])
+    got = O.paged_attention_varlen_lse_ref(packed, cu, case.k_cache, case.block_table, case.seq_lens, 5,
+                                           case.scale)
+    full = O.paged_attention_lse_ref(case.q, case.k_cache, case.block_table, case.seq_lens, 5, case.scale)
+    np.testing.assert_array_equal(got[0:4], full[0])
+    np.testing.assert_array_equal(got[5:8], full[2, 1:4])
+    single = O.paged_attention_lse_ref(case.q[1:2, 3:4], case.k_cache, case.block_table[1:2], case.seq_lens[1:2],
+                                       5, case.scale)
+    np.testing.assert_array_equal(got[4], single[0, 0])
