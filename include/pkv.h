@@ -154,6 +154,13 @@ int pkv_device_cu_count(int32_t* cu_count);
  *               the q_len new ones included. L = 0 gives zeros; a query row
  *               with no visible token gives zeros.
  *   out         device [num_seqs, q_len, Hq, D], float32 or bf16 (out_dtype).
+ *   lse         device float32 [num_seqs, q_len, Hq], 4-byte aligned, or NULL
+ *               (not written): the natural-log log-sum-exp of each row's
+ *               scaled scores, ln sum_j exp(scale * q . K_j) over the tokens
+ *               the row sees (FP8: K_j including k_scale), -inf for a row
+ *               that sees none. Written wherever out is written. With it a
+ *               caller can merge this result with attention over other keys
+ *               (the same statistic the split merge combines).
  *   workspace   device, >= pkv_workspace_bytes(p, 0) bytes, 256-byte aligned;
  *               its first 4 bytes are a sticky error word (bit 0: a block-table
  *               entry outside [0, num_pages) was met and its tokens skipped;
@@ -167,7 +174,7 @@ int pkv_device_cu_count(int32_t* cu_count);
 int pkv_paged_decode_attention(const pkv_decode_params* p,
                                const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* block_table, const int32_t* seq_lens,
-                               void* out, void* workspace, int64_t workspace_bytes,
+                               void* out, float* lse, void* workspace, int64_t workspace_bytes,
                                void* stream);
 
 /*
@@ -179,6 +186,7 @@ int pkv_paged_decode_attention(const pkv_decode_params* p,
  *   cu_seqlens_q device int32 [num_seqs + 1], non-decreasing, cu_seqlens_q[0] = 0
  *                and total_q <= num_seqs * q_len (the workspace's rows).
  *   out          device [total_q, Hq, D], float32 or bf16.
+ *   lse          device float32 [total_q, Hq] or NULL, as for the uniform call.
  * p->q_len is the largest n_b (a host-known bound, like max_seqlen_q of the
  * vendor interface in "DCU page832 attention" §6); (Hq / Hkv) * q_len <= 128.
  * Row i of sequence b sees the tokens j <= seq_lens[b] - n_b + i (the n_b new
@@ -193,7 +201,7 @@ int pkv_paged_varlen_attention(const pkv_decode_params* p,
                                const void* q, const void* k_cache, const void* v_cache,
                                const int32_t* block_table, const int32_t* seq_lens,
                                const int32_t* cu_seqlens_q,
-                               void* out, void* workspace, int64_t workspace_bytes,
+                               void* out, float* lse, void* workspace, int64_t workspace_bytes,
                                void* stream);
 
 /* Workspace bytes of a prefill call: the error word's header only. */
@@ -223,7 +231,7 @@ int pkv_paged_prefill_attention(const pkv_decode_params* p,
                                 const void* q, const void* k_cache, const void* v_cache,
                                 const int32_t* block_table, const int32_t* seq_lens,
                                 const int32_t* cu_seqlens_q,
-                                void* out, void* workspace, int64_t workspace_bytes,
+                                void* out, float* lse, void* workspace, int64_t workspace_bytes,
                                 void* stream);
 
 /* Which kernels the last successful attention call on this thread launched,

@@ -71,11 +71,12 @@ _SIGNATURES = {
     "pkv_plan_constants": (ctypes.c_int, [_i32p, _i32p, _i32p, _i32p]),
     "pkv_workspace_bytes": (ctypes.c_int64, [_P, ctypes.c_int32]),
     "pkv_device_cu_count": (ctypes.c_int, [_i32p]),
-    "pkv_paged_decode_attention": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64, _vp]),
-    "pkv_paged_varlen_attention": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64,
+    "pkv_paged_decode_attention": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64,
                                                   _vp]),
-    "pkv_paged_prefill_attention": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64,
-                                                   _vp]),
+    "pkv_paged_varlen_attention": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                  ctypes.c_int64, _vp]),
+    "pkv_paged_prefill_attention": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                   ctypes.c_int64, _vp]),
     "pkv_last_variant": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_int32]),
     "pkv_set_timing_events": (ctypes.c_int, [_vp, _vp]),
     "pkv_debug_token_offsets": (ctypes.c_int, [_P, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp]),
@@ -209,9 +210,10 @@ def make_params(q, k_cache, v_cache, block_table, block_size: int, scale: float,
 def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, block_size: int, scale: float, *,
                            max_seq_len: int | None = None, total_tokens: int = 0, num_splits: int = 0,
                            out=None, out_dtype=None, workspace=None, stream=None, window: int = 0,
-                           k_scale: float = 1.0, v_scale: float = 1.0):
+                           k_scale: float = 1.0, v_scale: float = 1.0, lse=None):
     """out[b,i,h,:] = softmax(scale * q[b,i,h,:] . K_j) V_j over the visible tokens of sequence b
-    (with window > 0, only the last `window` of them for each row).
+    (with window > 0, only the last `window` of them for each row). lse: optional float32
+    [num_seqs, q_len, Hq] on the GPU that receives ln sum_j exp(scale * q . K_j) per row.
 
     q: bf16 [num_seqs, q_len, Hq, D] (contiguous, on the GPU); k_cache / v_cache:
     bf16 [num_pages, B, Hkv, D] (views of a combined [num_pages, 2, B, Hkv, D]
@@ -240,10 +242,20 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, block_siz
         stream = torch.cuda.current_stream(q.device).cuda_stream
     rc = lib().pkv_paged_decode_attention(
         ctypes.byref(p), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
-        seq_lens.data_ptr(), out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-        stream)
+        seq_lens.data_ptr(), out.data_ptr(), _lse_ptr(lse, q.shape[:-1]), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), stream)
     check(rc, "pkv_paged_decode_attention")
     return out
+
+
+def _lse_ptr(lse, rows_shape):
+    """Device pointer of the optional float32 log-sum-exp output (None: not written)."""
+    if lse is None:
+        return None
+    torch = _torch()
+    assert lse.is_cuda and lse.dtype == torch.float32 and lse.is_contiguous()
+    assert tuple(lse.shape) == tuple(rows_shape), "lse has one float per (query row, head)"
+    return lse.data_ptr()
 
 
 def _KV_DTYPES():
@@ -254,12 +266,13 @@ def _KV_DTYPES():
 def paged_varlen_attention(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, block_size: int,
                            scale: float, *, max_q_len: int, max_seq_len: int, total_tokens: int = 0,
                            num_splits: int = 0, out=None, out_dtype=None, workspace=None, stream=None,
-                           window: int = 0, k_scale: float = 1.0, v_scale: float = 1.0):
+                           window: int = 0, k_scale: float = 1.0, v_scale: float = 1.0, lse=None):
     """Varlen multi-row call: sequence b's query rows are q[cu_seqlens_q[b]:cu_seqlens_q[b+1]].
 
     q: bf16 [total_q, Hq, D] packed rows (contiguous, on the GPU); cu_seqlens_q:
     int32 [num_seqs + 1] on the GPU; max_q_len: the largest row count (host
-    bound); max_seq_len: host bound of seq_lens. Returns out [total_q, Hq, D].
+    bound); max_seq_len: host bound of seq_lens. Returns out [total_q, Hq, D];
+    lse (optional float32 [total_q, Hq]) receives each row's log-sum-exp.
     """
     torch = _torch()
     assert q.is_cuda and q.dtype == torch.bfloat16 and q.is_contiguous() and q.dim() == 3
@@ -283,8 +296,8 @@ def paged_varlen_attention(q, k_cache, v_cache, block_table, seq_lens, cu_seqlen
         stream = torch.cuda.current_stream(q.device).cuda_stream
     rc = lib().pkv_paged_varlen_attention(
         ctypes.byref(p), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
-        seq_lens.data_ptr(), cu_seqlens_q.data_ptr(), out.data_ptr(), workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), stream)
+        seq_lens.data_ptr(), cu_seqlens_q.data_ptr(), out.data_ptr(), _lse_ptr(lse, q.shape[:-1]),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
     check(rc, "pkv_paged_varlen_attention")
     return out
 
@@ -292,11 +305,12 @@ def paged_varlen_attention(q, k_cache, v_cache, block_table, seq_lens, cu_seqlen
 def paged_prefill_attention(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, block_size: int,
                             scale: float, *, max_q_len: int, max_seq_len: int, out=None, out_dtype=None,
                             workspace=None, stream=None, window: int = 0, k_scale: float = 1.0,
-                            v_scale: float = 1.0):
+                            v_scale: float = 1.0, lse=None):
     """Chunked prefill: like paged_varlen_attention (packed rows q [total_q, Hq, D],
     cu_seqlens_q, causal rows ending at seq_lens[b]) for any number of new rows
     per sequence; one pass per block of query positions, no split workspace
-    (the workspace holds only the 256-byte error-word header)."""
+    (the workspace holds only the 256-byte error-word header). lse (optional
+    float32 [total_q, Hq]) receives each row's log-sum-exp."""
     torch = _torch()
     assert q.is_cuda and q.dtype == torch.bfloat16 and q.is_contiguous() and q.dim() == 3
     assert cu_seqlens_q.dtype == torch.int32 and cu_seqlens_q.is_contiguous()
@@ -317,8 +331,8 @@ def paged_prefill_attention(q, k_cache, v_cache, block_table, seq_lens, cu_seqle
         stream = torch.cuda.current_stream(q.device).cuda_stream
     rc = lib().pkv_paged_prefill_attention(
         ctypes.byref(p), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
-        seq_lens.data_ptr(), cu_seqlens_q.data_ptr(), out.data_ptr(), workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), stream)
+        seq_lens.data_ptr(), cu_seqlens_q.data_ptr(), out.data_ptr(), _lse_ptr(lse, q.shape[:-1]),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
     check(rc, "pkv_paged_prefill_attention")
     return out
 
@@ -372,12 +386,13 @@ class PreparedDecode:
     strides as the one given at construction. With ``cu_seqlens_q`` (int32 on
     the GPU) and ``max_q_len`` the call is the varlen one on packed rows
     q [total_q, Hq, D]; ``prefill=True`` makes it the chunked-prefill call on
-    the same packed rows."""
+    the same packed rows. ``lse`` (float32, one value per query row and head)
+    receives each row's log-sum-exp on every run."""
 
     def __init__(self, q, k_cache, v_cache, block_table, seq_lens, block_size: int, scale: float, *,
                  max_seq_len: int, total_tokens: int = 0, num_splits: int = 0, out=None, workspace=None,
                  stream=None, cu_seqlens_q=None, max_q_len: int | None = None, window: int = 0,
-                 k_scale: float = 1.0, v_scale: float = 1.0, prefill: bool = False):
+                 k_scale: float = 1.0, v_scale: float = 1.0, prefill: bool = False, lse=None):
         torch = _torch()
         assert q.is_cuda and q.dtype == torch.bfloat16 and q.is_contiguous()
         assert block_table.is_contiguous() and seq_lens.is_contiguous()
@@ -409,7 +424,9 @@ class PreparedDecode:
         self._keep = self._keep + (cu_seqlens_q,)
         self._pp = ctypes.byref(self.params)
         self._fixed = (q.data_ptr(), block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
-                       workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
+                       _lse_ptr(lse, q.shape[:-1]), workspace.data_ptr(),
+                       workspace.numel() * workspace.element_size(), stream)
+        self.lse = lse
         self._cu = cu_seqlens_q.data_ptr() if self.varlen else None
         self._name = ("pkv_paged_prefill_attention" if prefill else
                       "pkv_paged_varlen_attention" if self.varlen else "pkv_paged_decode_attention")
@@ -418,11 +435,11 @@ class PreparedDecode:
 
     def run_ptrs(self, k_ptr: int, v_ptr: int) -> None:
         """Like run() with raw device pointers of a pool laid out like the original."""
-        qp, tp, lp, op, wp, wn, st = self._fixed
+        qp, tp, lp, op, sp, wp, wn, st = self._fixed
         if self._cu is None:
-            rc = self._fn(self._pp, qp, k_ptr, v_ptr, tp, lp, op, wp, wn, st)
+            rc = self._fn(self._pp, qp, k_ptr, v_ptr, tp, lp, op, sp, wp, wn, st)
         else:
-            rc = self._fn(self._pp, qp, k_ptr, v_ptr, tp, lp, self._cu, op, wp, wn, st)
+            rc = self._fn(self._pp, qp, k_ptr, v_ptr, tp, lp, self._cu, op, sp, wp, wn, st)
         if rc != PKV_OK:
             check(rc, self._name)
 

@@ -234,9 +234,10 @@ int validate_any(const pkv_decode_params* p);
 // kernel.
 int launch_call(const pkv_decode_params* p, const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* block_table, const int32_t* seq_lens, const int32_t* cu_q, void* out,
-                void* workspace, int64_t workspace_bytes, void* stream) {
+                float* lse, void* workspace, int64_t workspace_bytes, void* stream) {
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out || !workspace)
     return fail(PKV_ERR_INVALID, "a device pointer is NULL");
+  if ((reinterpret_cast<uintptr_t>(lse) & 3) != 0) return fail(PKV_ERR_INVALID, "lse must be 4-byte aligned");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return fail(PKV_ERR_INVALID, "q, k_cache, v_cache and out must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
@@ -258,6 +259,7 @@ int launch_call(const pkv_decode_params* p, const void* q, const void* k_cache, 
   a.seq_lens = seq_lens;
   a.cu_q = cu_q;
   a.out = out;
+  a.lse = lse;
   char* ws = static_cast<char*>(workspace);
   const int64_t rows = int64_t(p->num_seqs) * p->q_len * p->num_q_heads;
   a.err = reinterpret_cast<uint32_t*>(ws);
@@ -343,32 +345,33 @@ int pkv_device_cu_count(int32_t* cu_count) {
 
 int pkv_paged_decode_attention(const pkv_decode_params* p, const void* q, const void* k_cache,
                                const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
-                               void* out, void* workspace, int64_t workspace_bytes, void* stream) {
+                               void* out, float* lse, void* workspace, int64_t workspace_bytes, void* stream) {
   int rc = pkv_validate_params(p);
   if (rc) return rc;
-  return launch_call(p, q, k_cache, v_cache, block_table, seq_lens, nullptr, out, workspace, workspace_bytes,
+  return launch_call(p, q, k_cache, v_cache, block_table, seq_lens, nullptr, out, lse, workspace, workspace_bytes,
                      stream);
 }
 
 int pkv_paged_varlen_attention(const pkv_decode_params* p, const void* q, const void* k_cache,
                                const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
-                               const int32_t* cu_seqlens_q, void* out, void* workspace, int64_t workspace_bytes,
-                               void* stream) {
+                               const int32_t* cu_seqlens_q, void* out, float* lse, void* workspace,
+                               int64_t workspace_bytes, void* stream) {
   int rc = validate_varlen(p);
   if (rc) return rc;
   if (!cu_seqlens_q) return fail(PKV_ERR_INVALID, "cu_seqlens_q is NULL");
-  return launch_call(p, q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, out, workspace,
+  return launch_call(p, q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q, out, lse, workspace,
                      workspace_bytes, stream);
 }
 
 int pkv_paged_prefill_attention(const pkv_decode_params* p, const void* q, const void* k_cache,
                                 const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
-                                const int32_t* cu_seqlens_q, void* out, void* workspace, int64_t workspace_bytes,
-                                void* stream) {
+                                const int32_t* cu_seqlens_q, void* out, float* lse, void* workspace,
+                                int64_t workspace_bytes, void* stream) {
   int rc = validate_prefill(p);
   if (rc) return rc;
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !cu_seqlens_q || !out || !workspace)
     return fail(PKV_ERR_INVALID, "a device pointer is NULL");
+  if ((reinterpret_cast<uintptr_t>(lse) & 3) != 0) return fail(PKV_ERR_INVALID, "lse must be 4-byte aligned");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return fail(PKV_ERR_INVALID, "q, k_cache, v_cache and out must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
@@ -385,6 +388,7 @@ int pkv_paged_prefill_attention(const pkv_decode_params* p, const void* q, const
   a.seq_lens = seq_lens;
   a.cu_q = cu_seqlens_q;
   a.out = out;
+  a.lse = lse;
   a.err = static_cast<uint32_t*>(workspace);
   const int group = p->num_q_heads / p->num_kv_heads;
   hipError_t e = pkv::launch_prefill(a, p->head_dim, group, static_cast<hipStream_t>(stream), g_ev_start, g_ev_stop);

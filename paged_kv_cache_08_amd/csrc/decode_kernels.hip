@@ -93,7 +93,8 @@ __global__ __launch_bounds__(64 * MW) void lse_merge_kernel(DecodeArgs a) {
     dloc += f * v.y;
     if (t < kMergeSplitsLds) sm_w[wave][t] = f;
   }
-  const float inv_den = 1.0f / wave_sum64(dloc);
+  const float den = wave_sum64(dloc);
+  const float inv_den = 1.0f / den;
   // The wave reads back the weights it wrote (LDS operations of one wave run
   // in order; this keeps the compiler from moving the reads above the writes).
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -135,6 +136,7 @@ __global__ __launch_bounds__(64 * MW) void lse_merge_kernel(DecodeArgs a) {
     float t = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
     if constexpr (MW == 8) t += (part[4][lane] + part[5][lane]) + (part[6][lane] + part[7][lane]);
     store_out(a, prow * D + d, M == -INFINITY ? 0.0f : t * inv_den);
+    if (cb == 0 && lane == 0) store_lse(a, prow, M, M == -INFINITY ? 0.0f : den);
   }
 }
 
@@ -179,6 +181,7 @@ __global__ __launch_bounds__(256) void lse_merge_few_kernel(DecodeArgs a) {
   if (M == -INFINITY) {
 #pragma unroll
     for (int c = 0; c < kCols; ++c) store_out(a, prow * D + c * 64 + lane, 0.0f);
+    if (lane == 0) store_lse(a, prow, 0.0f, 0.0f);
     return;
   }
   float den = 0.0f, num[kCols];
@@ -194,6 +197,7 @@ __global__ __launch_bounds__(256) void lse_merge_few_kernel(DecodeArgs a) {
   const float inv = 1.0f / den;
 #pragma unroll
   for (int c = 0; c < kCols; ++c) store_out(a, prow * D + c * 64 + lane, num[c] * inv);
+  if (lane == 0) store_lse(a, prow, M, den);
 }
 
 // Debug: offsets of every live token row of the split ranges, found both

@@ -200,8 +200,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
 
   const SplitSpan sp = split_span_len(a, L_in, s, 1);
   if (sp.begin >= sp.L) {
-    if (s == 0)   // empty sequence: zeros
+    if (s == 0) {   // empty sequence: zeros (log-sum-exp -inf)
       for (int i = tid; i < G * D; i += kThreads) store_out(a, out_row0 + i, 0.0f);
+      if (tid < G) store_lse(a, out_row0 / D + tid, 0.0f, 0.0f);
+    }
     return;
   }
   const int t_tok = strided_token(sp.lo, sp.nsplit, s, min(tid, kWin - 1));
@@ -456,6 +458,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
     }
     if (sp.nsplit == 1) {
       store_out(a, out_row0 + i, den > 0.0f ? num / den : 0.0f);
+      if (d == 0) store_lse(a, out_row0 / D + h, M, den);
     } else {
       const int64_t pr = (prow0 + h) * a.num_splits + s;
       a.part_acc[pr * D + d] = num;

@@ -74,6 +74,7 @@ struct DecodeArgs {
   int32_t kv_fp8;           // K/V caches hold FP8 E4M3 codes (else bf16)
   float out_scale;          // applied to every stored output (the FP8 V scale, else 1)
   int32_t pf_rows;          // prefill calls: query positions per workgroup block (else 0)
+  float* lse;               // optional [rows, hq] natural-log log-sum-exp of each row's scores (nullptr: none)
 };
 
 // Launchers (decode_kernels.hip, decode_w*.hip, verify_kernels.hip). Return

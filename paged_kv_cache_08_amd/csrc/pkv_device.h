@@ -91,6 +91,14 @@ __device__ __forceinline__ void store_out(const DecodeArgs& a, int64_t idx, floa
     static_cast<float*>(a.out)[idx] = x;
 }
 
+// Optional log-sum-exp output of output row `row` (= query row * hq + head):
+// ln sum_j e^(score_j) from the row's (m, l) in log2 units, l = sum_j
+// 2^(score_j * log2(e) - m): (m + log2 l) * ln 2; -inf for a row that saw no
+// token (l = 0). Not scaled by the V scale.
+__device__ __forceinline__ void store_lse(const DecodeArgs& a, int64_t row, float m, float l) {
+  if (a.lse) a.lse[row] = l > 0.0f ? (m + log2f(l)) * 0.6931471805599453f : -INFINITY;
+}
+
 struct SplitSpan {
   int L;        // live tokens of the sequence (clamped to what the table and the plan can map)
   int lo;       // first token the sequence's query rows can see

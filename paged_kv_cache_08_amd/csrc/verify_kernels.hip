@@ -155,11 +155,12 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
   }
 
   if (sp.begin >= sp.L) {
-    if (s == 0)   // empty sequence: zeros for every row of this KV head
+    if (s == 0)   // empty sequence: zeros (log-sum-exp -inf) for every row of this KV head
       for (int i = tid; i < R * D; i += kVThreads) {
         const int f = i / D, d = i - f * D;
         const int64_t prow = (int64_t(row_base) + f % q_len) * a.hq + int64_t(g) * G + f / q_len;
         store_out(a, prow * D + d, 0.0f);
+        if (d == 0) store_lse(a, prow, 0.0f, 0.0f);
       }
     return;
   }
@@ -409,6 +410,7 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
       const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
 #pragma unroll
       for (int db = 0; db < kDBlocks; ++db) store_out(a, prow * D + 16 * db + ln, o[db][r] * inv);
+      if (ln == 0) store_lse(a, prow, mr, lr);
     } else {
       const int64_t pr = prow * a.num_splits + s;
 #pragma unroll

@@ -99,7 +99,7 @@ def _prefill(p, ws_bytes=256, ptr=0):
     f = P.lib().pkv_paged_prefill_attention
     import ctypes
     a = ptr or None
-    return f(ctypes.byref(p), a, a, a, a, a, a, a, a, ws_bytes, None)
+    return f(ctypes.byref(p), a, a, a, a, a, a, a, None, a, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -1,0 +1,129 @@
+"""GPU parity of the optional log-sum-exp output (ln sum_j exp(scale q.k_j) per
+query row and head) against the fp64 oracle, through the C ABI, on every path
+that writes rows: the split kernel alone (one split), with the many-split and
+the few-split merge, the MFMA kernel (verify, large groups, varlen) and the
+prefill call; empty sequences give -inf. Passing lse must not change out."""
+import numpy as np
+import pytest
+
+import oracle.paged_attention as O
+from paged_kv_cache_08_amd import workloads as W
+from tests.gpu_helpers import ATOL, assert_matches_oracle, bf16_tensor, kv_kwargs, log, oracle_kv, to_device
+
+pytestmark = pytest.mark.gpu
+
+# The outputs' bound; the fp32 scores and log2 keep the log-sum-exp far inside it.
+LSE_ATOL = ATOL
+
+
+def check_lse(got, ref, what):
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == ref.shape
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref)), f"{what}: rows with no token differ"
+    fin = np.isfinite(ref)
+    assert np.all(np.isfinite(got[fin])), f"{what}: non-finite log-sum-exp"
+    err = float(np.abs(got[fin] - ref[fin]).max(initial=0.0))
+    log(f"  {what}: log-sum-exp max abs err {err:.3e} over {int(fin.sum())} rows")
+    assert err <= LSE_ATOL, f"{what}: log-sum-exp max abs err {err} > {LSE_ATOL}"
+
+
+def oracle_lse(case, window=0):
+    return O.paged_attention_lse_ref(case.q, case.k_cache, case.block_table, case.seq_lens, case.block_size,
+                                     case.scale, window, kv_dtype=case.kv_dtype, k_scale=case.k_scale)
+
+
+def decode_twice(case, **kw):
+    """The uniform call with and without lse; returns (out, out without lse, lse, variant)."""
+    import torch
+    import paged_kv_cache_08_amd as P
+    q, k, v, table, lens = to_device(case)
+    lse = torch.full(q.shape[:-1], float("nan"), dtype=torch.float32, device="cuda")
+    args = (q, k, v, table, lens, case.block_size, case.scale)
+    kw = dict(max_seq_len=case.max_seq_len, **kv_kwargs(case), **kw)
+    out = P.paged_decode_attention(*args, lse=lse, **kw)
+    variant = P.last_variant()
+    plain = P.paged_decode_attention(*args, **kw)
+    torch.cuda.synchronize()
+    return (out.float().cpu().numpy().astype(np.float64), plain.float().cpu().numpy().astype(np.float64),
+            lse.cpu().numpy(), variant)
+
+
+DECODE_CASES = [
+    # name, case, call arguments, expected kernels (substrings of the variant)
+    ("splits + one-split + empty", lambda: W.make_case(1201, [3000, 1, 0, 700], block_size=784, interleave=True,
+                                                       boost_frac=0.05), {}, ("decode_valu", "lse_merge")),
+    ("few splits", lambda: W.make_case(1202, [3000, 5, 700], block_size=784, interleave=True, boost_frac=0.05),
+     {"num_splits": 3}, ("decode_valu", "splits=6")),
+    ("one split", lambda: W.make_case(1203, [300, 64, 0], block_size=16, interleave=True), {"num_splits": 1},
+     ("decode_valu", "splits=1")),
+    ("large grid", lambda: W.make_case(1204, [2000, 2000, 2000, 50, 900, 0], block_size=784, interleave=True,
+                                       boost_frac=0.05), {}, ("decode_valu", "lse_merge")),
+    ("window 2048", lambda: W.make_case(1205, [5000, 100], block_size=784, interleave=True, boost_frac=0.05),
+     {"window": 2048}, ("decode_valu",)),
+    ("FP8 K/V", lambda: W.make_case(1206, [3000, 17, 0], block_size=784, interleave=True, boost_frac=0.05,
+                                    kv_dtype="fp8_e4m3"), {}, ("decode_valu",)),
+    ("group 12 on MFMA", lambda: W.make_case(1207, [2500, 0, 33], num_q_heads=24, num_kv_heads=2, block_size=784,
+                                             interleave=True, boost_frac=0.05), {}, ("verify_mfma",)),
+    ("verify q16", lambda: W.make_case(1208, [3000, 20, 0], q_len=16, block_size=784, interleave=True,
+                                       boost_frac=0.05), {}, ("verify_mfma", "lse_merge")),
+    ("verify q4, one split", lambda: W.make_case(1209, [200, 4], q_len=4, block_size=7, interleave=True),
+     {"num_splits": 1}, ("verify_mfma", "splits=1")),
+]
+
+
+@pytest.mark.parametrize("name,make,kw,kernels", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_lse(name, make, kw, kernels):
+    log(f"case: log-sum-exp, {name}, {kw}")
+    case = make()
+    out, plain, lse, variant = decode_twice(case, **kw)
+    log(f"  variant: {variant}")
+    for k in kernels:
+        assert k in variant
+    np.testing.assert_array_equal(out, plain)     # the extra output changes nothing else
+    window = kw.get("window", 0)
+    assert_matches_oracle(out, O.paged_attention_ref(case.q, case.k_cache, case.v_cache, case.block_table,
+                                                     case.seq_lens, case.block_size, case.scale, window,
+                                                     **oracle_kv(case)), name)
+    check_lse(lse, oracle_lse(case, window), name)
+
+
+def test_varlen_lse():
+    import torch
+    import paged_kv_cache_08_amd as P
+    log("case: log-sum-exp, varlen rows [5, 0, 1, 3], lengths [2000, 40, 700, 3]")
+    case = W.make_case(1210, [2000, 40, 700, 3], q_len=5, block_size=784, interleave=True, boost_frac=0.05)
+    q_packed, cu = W.pack_varlen(case, [5, 0, 1, 3])
+    _, k, v, table, lens = to_device(case)
+    q = bf16_tensor(q_packed)
+    cu_t = torch.from_numpy(np.ascontiguousarray(cu, dtype=np.int32)).cuda()
+    lse = torch.full(q.shape[:-1], float("nan"), dtype=torch.float32, device="cuda")
+    out = P.paged_varlen_attention(q, k, v, table, lens, cu_t, case.block_size, case.scale, max_q_len=5,
+                                   max_seq_len=case.max_seq_len, lse=lse)
+    torch.cuda.synchronize()
+    ref = O.paged_attention_varlen_ref(q_packed, cu, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                                       case.block_size, case.scale)
+    assert_matches_oracle(out.float().cpu().numpy().astype(np.float64), ref, "varlen")
+    check_lse(lse.cpu().numpy(), O.paged_attention_varlen_lse_ref(q_packed, cu, case.k_cache, case.block_table,
+                                                                  case.seq_lens, case.block_size, case.scale),
+              "varlen")
+
+
+@pytest.mark.parametrize("rows,lens,window", [([200], [1000], 0), ([37, 0, 130, 1], [37, 500, 900, 1], 0),
+                                              ([150], [2500], 300)])
+def test_prefill_lse(rows, lens, window):
+    import torch
+    import paged_kv_cache_08_amd as P
+    log(f"case: log-sum-exp, prefill rows {rows}, lengths {lens}, window {window}")
+    case = W.make_case(1211 + len(rows), lens, q_len=max(rows), block_size=784, interleave=True, boost_frac=0.05)
+    q_packed, cu = W.pack_varlen(case, rows)
+    _, k, v, table, lens_t = to_device(case)
+    q = bf16_tensor(q_packed)
+    cu_t = torch.from_numpy(np.ascontiguousarray(cu, dtype=np.int32)).cuda()
+    lse = torch.full(q.shape[:-1], float("nan"), dtype=torch.float32, device="cuda")
+    P.paged_prefill_attention(q, k, v, table, lens_t, cu_t, case.block_size, case.scale, max_q_len=max(rows),
+                              max_seq_len=case.max_seq_len, window=window, lse=lse)
+    torch.cuda.synchronize()
+    assert P.last_variant().startswith("prefill_mfma")
+    check_lse(lse.cpu().numpy(), O.paged_attention_varlen_lse_ref(q_packed, cu, case.k_cache, case.block_table,
+                                                                  case.seq_lens, case.block_size, case.scale,
+                                                                  window), f"prefill {rows}")
