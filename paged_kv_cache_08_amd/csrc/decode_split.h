@@ -458,7 +458,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
     }
     if (sp.nsplit == 1) {
       store_out(a, out_row0 + i, den > 0.0f ? num / den : 0.0f);
-      if (d == 0) store_lse(a, out_row0 / D + h, M, den);
     } else {
       const int64_t pr = (prow0 + h) * a.num_splits + s;
       a.part_acc[pr * D + d] = num;
@@ -467,6 +466,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
         a.part_ml[pr * 2 + 1] = den;
       }
     }
+  }
+  // A single-split sequence's optional log-sum-exp, one thread per head, from
+  // the same (max, sum) pairs and in the same order as the loop above (kept
+  // out of that loop, which every split runs).
+  if (sp.nsplit == 1 && a.lse != nullptr && tid < G) {
+    float M = mrg_m[tid][0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mrg_m[tid][w]);
+    float den = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) den = fmaf(fast_exp2(mrg_m[tid][w] - M), mrg_l[tid][w], den);
+    store_lse(a, out_row0 / D + tid, M, den);
   }
 }
 
