@@ -35,14 +35,15 @@ __device__ __forceinline__ float wave_sum64(float x) {
 // fixed order. MW = 8 (8 splits per wave) for small grids (a batch-1 decode
 // step has 24 (row, head) pairs), MW = 4 (16 splits per wave) otherwise:
 // measured, small grids want more waves with fewer loads each, large grids
-// the opposite. Small grids also load their first pass before the sequence
-// length is known (32K decode step -0.4 us); in large grids of mostly short
-// sequences those loads of unused splits cost more than they save.
-template <int D, int MW>
+// the opposite. AHEAD: the first pass is loaded before the sequence length
+// is known, for small grids (32K decode step -0.4 us) and for a single
+// sequence, whose plan was made for its own length; in large grids of mostly
+// short sequences those loads of unused splits cost more than they save.
+template <int D, int MW, bool AHEAD>
 __global__ __launch_bounds__(64 * MW) void lse_merge_kernel(DecodeArgs a) {
   constexpr int kPerWave = 64 / MW;   // accumulator loads in flight per thread per pass
   constexpr int kPass = MW * kPerWave;
-  constexpr bool kAhead = MW == 8;    // small grids: latency-bound, load ahead of the length
+  constexpr bool kAhead = AHEAD;
   __shared__ float sm_w[MW][kMergeSplitsLds];
   __shared__ float part[MW][64];
   const int cb = blockIdx.z, h = blockIdx.y;
@@ -290,16 +291,21 @@ hipError_t launch_lse_merge(const DecodeArgs& a, int head_dim, hipStream_t st) {
   }
   dim3 grid(a.q_len * a.num_seqs, a.hq, head_dim / 64);
   const bool small = int64_t(a.q_len) * a.num_seqs * a.hq < 128;
+  const bool one_seq = a.num_seqs == 1 && a.cu_q == nullptr;
   if (head_dim == 256) {
     if (small)
-      hipLaunchKernelGGL((lse_merge_kernel<256, 8>), grid, dim3(512), 0, st, a);
+      hipLaunchKernelGGL((lse_merge_kernel<256, 8, true>), grid, dim3(512), 0, st, a);
+    else if (one_seq)
+      hipLaunchKernelGGL((lse_merge_kernel<256, 4, true>), grid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((lse_merge_kernel<256, 4>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((lse_merge_kernel<256, 4, false>), grid, dim3(256), 0, st, a);
   } else if (head_dim == 128) {
     if (small)
-      hipLaunchKernelGGL((lse_merge_kernel<128, 8>), grid, dim3(512), 0, st, a);
+      hipLaunchKernelGGL((lse_merge_kernel<128, 8, true>), grid, dim3(512), 0, st, a);
+    else if (one_seq)
+      hipLaunchKernelGGL((lse_merge_kernel<128, 4, true>), grid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((lse_merge_kernel<128, 4>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((lse_merge_kernel<128, 4, false>), grid, dim3(256), 0, st, a);
   } else {
     return hipErrorInvalidValue;
   }
