@@ -21,10 +21,9 @@
 //     when the whole chip streams one band than with n bands far apart.)
 //   * 8 waves (2 per SIMD) x 4 token rows per wave: one block of 32
 //     consecutive logical tokens per sub-step, one token row per 16-lane DPP
-//     row. Each lane owns
-//     D/16 head-dim elements of its row and loads them with 16-byte global
-//     loads (a 512-byte K row of D = 256 is read by 16 lanes in two fully used
-//     256-byte segments). The G query heads of the group all use the row held
+//     row. Each lane owns D/16 head-dim elements of its row and loads them
+//     with 16-byte global loads (a 512-byte K row of D = 256 is read by 16
+//     lanes in two fully used 256-byte segments). The G query heads of the group all use the row held
 //     in registers, so K and V are fetched once per group. The K/V loads are
 //     non-temporal: each byte is read once per call.
 //   * The split is one window, fully unrolled: a K pass over its NS sub-steps,
@@ -43,9 +42,9 @@
 //     the token's K and V row offsets in LDS, once per split (without a
 //     sliding window, while seq_lens is still in flight, for the stride of a
 //     sequence that uses every split); a masked slot gets the offset of the
-//     q row. A lane then costs one LDS read and one address
-//     add per K or V row, instead of every lane of a row repeating the
-//     division and the table lookup.
+//     q row. A lane then costs one LDS read and one address add per K or V
+//     row, instead of every lane of a row repeating the division and the
+//     table lookup.
 //   * Epilogue: the 4 token rows of a wave are merged by a reduce-scatter over
 //     lane swaps (v_permlane32_swap, v_permlane16_swap); the 8 waves publish
 //     their sums with their reference max in LDS and, after one barrier, are
