@@ -202,3 +202,19 @@ def test_invariant_divisor_division_all_divisors_to_1024():
 
 def test_bad_divisor_is_rejected():
     assert P.magic_div_check(0, 10) == -2
+
+
+def test_misaligned_lse_and_strided_debug_on_multi_row_calls_are_refused():
+    # Fake 256-byte-aligned device pointers pass the pointer checks; these
+    # argument errors are reported before anything touches the device.
+    import ctypes
+    a = 1 << 20
+    lib = P.lib()
+    assert lib.pkv_paged_decode_attention(ctypes.byref(params()), a, a, a, a, a, a, a + 2, a, 1 << 30, None) == -1
+    assert lib.pkv_paged_varlen_attention(ctypes.byref(params(q_len=4)), a, a, a, a, a, a, a, a + 1, a, 1 << 30,
+                                          None) == -1
+    assert lib.pkv_paged_prefill_attention(ctypes.byref(params(q_len=4096)), a, a, a, a, a, a, a, a + 2, a, 256,
+                                           None) == -1
+    # the strided token-to-split map is the single-query kernel's: q_len must be 1
+    assert lib.pkv_debug_token_splits(ctypes.byref(params(q_len=2)), a, a, None) == -1
+    assert lib.pkv_debug_token_splits(ctypes.byref(params()), None, a, None) == -1
