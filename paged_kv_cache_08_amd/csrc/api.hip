@@ -265,6 +265,7 @@ int launch_call(const pkv_decode_params* p, const void* q, const void* k_cache, 
   a.err = reinterpret_cast<uint32_t*>(ws);
   a.part_ml = reinterpret_cast<float*>(ws + pkv::kWsHeaderBytes);
   a.part_acc = reinterpret_cast<float*>(ws + pkv::kWsHeaderBytes + align256(rows * S * 2 * 4));
+  a.many_wg = int64_t(S) * p->num_kv_heads * p->num_seqs > cu ? 1 : 0;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int group = p->num_q_heads / p->num_kv_heads;

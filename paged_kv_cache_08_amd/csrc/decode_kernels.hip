@@ -274,7 +274,9 @@ hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int group, hip
     case 64: return (fp8 ? launch_decode_split_w64_fp8 : launch_decode_split_w64)(a, head_dim, group, st, e0, e1);
     case 128: return (fp8 ? launch_decode_split_w128_fp8 : launch_decode_split_w128)(a, head_dim, group, st, e0, e1);
     case 256: return (fp8 ? launch_decode_split_w256_fp8 : launch_decode_split_w256)(a, head_dim, group, st, e0, e1);
-    default: return (fp8 ? launch_decode_split_w512_fp8 : launch_decode_split_w512)(a, head_dim, group, st, e0, e1);
+    default:
+      if (fp8) return launch_decode_split_w512_fp8(a, head_dim, group, st, e0, e1);
+      return (a.many_wg ? launch_decode_split_w512_shallow : launch_decode_split_w512)(a, head_dim, group, st, e0, e1);
   }
 }
 

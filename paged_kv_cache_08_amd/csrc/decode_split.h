@@ -77,6 +77,12 @@ static_assert(kStep == kBlockTokens, "a sub-step reads one strided block of the 
 // bf16 depth 4 / 6 / 8 gave 29.85 / 29.61 / 29.93 us on a 32K step; the FP8
 // rows are half as long and depth 4 is about 1% faster than 6 there.
 constexpr int ring_depth(int D, int G, bool fp8) { return (D == 256 && G >= 7) ? 3 : fp8 ? 4 : 6; }
+// The shallow variant (at most 4) serves grids of several waves of
+// workgroups: on a 16-sequence mixed batch depth 4 measured 82.3 against
+// 83.3 us at depth 6, on the single-wave 32K step 29.85 against 29.61 us.
+constexpr int ring_depth(int D, int G, bool fp8, bool shallow) {
+  return shallow && ring_depth(D, G, fp8) > 4 ? 4 : ring_depth(D, G, fp8);
+}
 constexpr float kMinit = -1.0e30f;             // floor of a row's max (finite: no inf - inf)
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -150,13 +156,13 @@ __device__ __forceinline__ int elem_d(int col, int e) {
   return FP8 ? col * kEpl + e : (e / 8) * 128 + col * 8 + (e % 8);
 }
 
-template <int D, int G, int kSubSteps, bool FP8>
+template <int D, int G, int kSubSteps, bool FP8, bool SHALLOW>
 __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a) {
   constexpr int kEpl = D / kLanesPerRow;   // head-dim elements per lane: 16 or 8
   constexpr int kCq = kEpl / 8;            // 16-byte pieces of q per lane: 2 or 1
   constexpr int kCpl = FP8 ? 1 : kCq;      // 16-byte K/V loads per lane and row (FP8 at D = 128: 8 bytes)
   constexpr int kSteps = 2 * kSubSteps;    // K pass, then V pass
-  constexpr int kRing = ring_depth(D, G, FP8);
+  constexpr int kRing = ring_depth(D, G, FP8, SHALLOW);
   constexpr int kWin = kSubSteps * kStep;  // tokens of the window
   constexpr int kEsz = FP8 ? 1 : 2;        // bytes per cache element
   static_assert(kCpl >= 1 && kEpl % 8 == 0, "head_dim must be a multiple of 128");
@@ -482,39 +488,41 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   }
 }
 
-template <int D, int G, int NS, bool FP8>
+template <int D, int G, int NS, bool FP8, bool SHALLOW>
 hipError_t launch_decode_k(const DecodeArgs& a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   dim3 grid(a.num_splits, a.hkv, a.num_seqs);
   if (e0 && e1)
-    hipExtLaunchKernelGGL((decode_split_kernel<D, G, NS, FP8>), grid, dim3(kThreads), 0, st, e0, e1, 0, a);
+    hipExtLaunchKernelGGL((decode_split_kernel<D, G, NS, FP8, SHALLOW>), grid, dim3(kThreads), 0, st, e0, e1, 0,
+                          a);
   else
-    hipLaunchKernelGGL((decode_split_kernel<D, G, NS, FP8>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, G, NS, FP8, SHALLOW>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
-template <int D, int NS, bool FP8>
+template <int D, int NS, bool FP8, bool SHALLOW>
 hipError_t launch_decode_d(const DecodeArgs& a, int group, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   switch (group) {
-    case 1: return launch_decode_k<D, 1, NS, FP8>(a, st, e0, e1);
-    case 2: return launch_decode_k<D, 2, NS, FP8>(a, st, e0, e1);
-    case 3: return launch_decode_k<D, 3, NS, FP8>(a, st, e0, e1);
-    case 4: return launch_decode_k<D, 4, NS, FP8>(a, st, e0, e1);
-    case 5: return launch_decode_k<D, 5, NS, FP8>(a, st, e0, e1);
-    case 6: return launch_decode_k<D, 6, NS, FP8>(a, st, e0, e1);
-    case 7: return launch_decode_k<D, 7, NS, FP8>(a, st, e0, e1);
-    case 8: return launch_decode_k<D, 8, NS, FP8>(a, st, e0, e1);
+    case 1: return launch_decode_k<D, 1, NS, FP8, SHALLOW>(a, st, e0, e1);
+    case 2: return launch_decode_k<D, 2, NS, FP8, SHALLOW>(a, st, e0, e1);
+    case 3: return launch_decode_k<D, 3, NS, FP8, SHALLOW>(a, st, e0, e1);
+    case 4: return launch_decode_k<D, 4, NS, FP8, SHALLOW>(a, st, e0, e1);
+    case 5: return launch_decode_k<D, 5, NS, FP8, SHALLOW>(a, st, e0, e1);
+    case 6: return launch_decode_k<D, 6, NS, FP8, SHALLOW>(a, st, e0, e1);
+    case 7: return launch_decode_k<D, 7, NS, FP8, SHALLOW>(a, st, e0, e1);
+    case 8: return launch_decode_k<D, 8, NS, FP8, SHALLOW>(a, st, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }
 
 // Launch the split kernel with a window of NS sub-steps (a.chunk <= NS * 32)
-// for bf16 (FP8 = false) or FP8 caches.
-template <int NS, bool FP8>
+// for bf16 (FP8 = false) or FP8 caches; SHALLOW selects the shallow register
+// ring (ring_depth()).
+template <int NS, bool FP8, bool SHALLOW = false>
 hipError_t launch_decode_window(const DecodeArgs& a, int head_dim, int group, hipStream_t st, hipEvent_t e0,
                                 hipEvent_t e1) {
   if (a.chunk > NS * kStep || bool(a.kv_fp8) != FP8) return hipErrorInvalidValue;
-  if (head_dim == 256) return launch_decode_d<256, NS, FP8>(a, group, st, e0, e1);
-  if (head_dim == 128) return launch_decode_d<128, NS, FP8>(a, group, st, e0, e1);
+  if (head_dim == 256) return launch_decode_d<256, NS, FP8, SHALLOW>(a, group, st, e0, e1);
+  if (head_dim == 128) return launch_decode_d<128, NS, FP8, SHALLOW>(a, group, st, e0, e1);
   return hipErrorInvalidValue;
 }
 

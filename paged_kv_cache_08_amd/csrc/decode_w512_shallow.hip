@@ -1,0 +1,13 @@
+// Split kernels with a 512-token window (16 sub-steps of 32 tokens), bf16
+// caches, shallow register ring: the variant for grids of several waves of
+// workgroups (ring_depth()).
+#include "decode_split.h"
+
+namespace pkv {
+
+hipError_t launch_decode_split_w512_shallow(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
+                                            hipEvent_t e0, hipEvent_t e1) {
+  return launch_decode_window<16, false, true>(a, head_dim, group, st, e0, e1);
+}
+
+}  // namespace pkv

@@ -75,6 +75,7 @@ struct DecodeArgs {
   float out_scale;          // applied to every stored output (the FP8 V scale, else 1)
   int32_t pf_rows;          // prefill calls: query positions per workgroup block (else 0)
   float* lse;               // optional [rows, hq] natural-log log-sum-exp of each row's scores (nullptr: none)
+  int32_t many_wg;          // the split grid holds more workgroups than the device has CUs
 };
 
 // Launchers (decode_kernels.hip, decode_w*.hip, verify_kernels.hip). Return
@@ -85,6 +86,8 @@ struct DecodeArgs {
 int decode_window(int chunk);
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
                                hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_decode_split_w512_shallow(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
+                                            hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_decode_split_w64(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
                                    hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_decode_split_w64_fp8(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
