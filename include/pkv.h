@@ -148,8 +148,10 @@ int pkv_device_cu_count(int32_t* cu_count);
  *               page * k_stride_page + token * k_stride_tok + kv_head * k_stride_head;
  *               both [P, B, Hkv, D] and views of [P, 2, B, Hkv, D] fit.
  *   v_cache     device bf16, same with the v_* strides.
- *   block_table device int32 [num_seqs, max_pages_per_seq]; entries past a
- *               sequence's last page are never read.
+ *   block_table device int32 [num_seqs, max_pages_per_seq], all of it
+ *               allocated: entries past a sequence's last page may be read
+ *               (the kernels fetch a split's entries before its length is
+ *               known) but are never dereferenced, so they may hold anything.
  *   seq_lens    device int32 [num_seqs]; tokens in the cache for each sequence,
  *               the q_len new ones included. L = 0 gives zeros; a query row
  *               with no visible token gives zeros.
@@ -162,12 +164,17 @@ int pkv_device_cu_count(int32_t* cu_count);
  *               caller can merge this result with attention over other keys
  *               (the same statistic the split merge combines).
  *   workspace   device, >= pkv_workspace_bytes(p, 0) bytes, 256-byte aligned;
- *               its first 4 bytes are a sticky error word (bit 0: a block-table
- *               entry outside [0, num_pages) was met and its tokens skipped;
- *               bit 1: a sequence's cu_seqlens_q rows were inconsistent and
- *               the sequence was skipped, varlen calls only); zero it once
- *               after allocating. Calls that share a workspace must not
- *               overlap in time.
+ *               zero all of it once after allocating. Its first 4 bytes are a
+ *               sticky error word:
+ *                 bit 0: a block-table entry outside [0, num_pages) was met
+ *                        and its tokens skipped;
+ *                 bit 1: a sequence's cu_seqlens_q rows were inconsistent and
+ *                        the sequence was skipped (varlen calls only);
+ *                 bit 2: seq_lens[b] exceeded what the call can map (the
+ *                        table's max_pages_per_seq * block_size tokens, or the
+ *                        splits planned for max_seq_len) and the sequence was
+ *                        cut to that range, so its newest tokens were dropped.
+ *               Calls that share a workspace must not overlap in time.
  *   stream      hipStream_t (NULL = default stream).
  * q, k_cache, v_cache and out must be 16-byte aligned. No input is written.
  */
@@ -237,8 +244,11 @@ int pkv_paged_prefill_attention(const pkv_decode_params* p,
 /* Which kernels the last successful attention call on this thread launched,
  * with the split plan, e.g. "decode_valu d256 g6 q1 w512 + lse_merge
  * splits=64 chunk=512 B=784" (for prefill, w is the query positions per
- * workgroup). Copies at most len-1 characters plus a terminator; returns the
- * full length. */
+ * workgroup). It is this library's run-time marker of the path that ran:
+ * "DCU page832 attention" §8 accepts a measurement only when the run's log
+ * shows the decode marker of the kernel under test, and §11.3 asks to print
+ * that marker and to check that no fallback ran instead. Copies at most
+ * len-1 characters plus a terminator; returns the full length. */
 int pkv_last_variant(char* buf, int32_t len);
 
 /* Profiling hook: when both are non-NULL, later calls on this thread launch

@@ -75,10 +75,22 @@ int plan(const pkv_decode_params* p, int32_t cu_count, int32_t* S, int32_t* chun
   return PKV_OK;
 }
 
-int64_t workspace_for(const pkv_decode_params* p, int32_t S) {
+// Workspace layout: the 256-byte header (error word), the (max, sum) pairs
+// and the accumulators of every split of every output row.
+struct WsLayout {
+  int64_t ml, acc, total;
+};
+
+WsLayout workspace_layout(const pkv_decode_params* p, int32_t S) {
   const int64_t rows = int64_t(p->num_seqs) * p->q_len * p->num_q_heads;
-  return pkv::kWsHeaderBytes + align256(rows * S * 2 * 4) + align256(rows * S * int64_t(p->head_dim) * 4);
+  WsLayout w;
+  w.ml = pkv::kWsHeaderBytes;
+  w.acc = w.ml + align256(rows * S * 2 * 4);
+  w.total = w.acc + align256(rows * S * int64_t(p->head_dim) * 4);
+  return w;
 }
+
+int64_t workspace_for(const pkv_decode_params* p, int32_t S) { return workspace_layout(p, S).total; }
 
 int device_cu_count(int32_t* out) {
   int dev = 0;
@@ -261,10 +273,10 @@ int launch_call(const pkv_decode_params* p, const void* q, const void* k_cache, 
   a.out = out;
   a.lse = lse;
   char* ws = static_cast<char*>(workspace);
-  const int64_t rows = int64_t(p->num_seqs) * p->q_len * p->num_q_heads;
+  const WsLayout wl = workspace_layout(p, S);
   a.err = reinterpret_cast<uint32_t*>(ws);
-  a.part_ml = reinterpret_cast<float*>(ws + pkv::kWsHeaderBytes);
-  a.part_acc = reinterpret_cast<float*>(ws + pkv::kWsHeaderBytes + align256(rows * S * 2 * 4));
+  a.part_ml = reinterpret_cast<float*>(ws + wl.ml);
+  a.part_acc = reinterpret_cast<float*>(ws + wl.acc);
   a.many_wg = int64_t(S) * p->num_kv_heads * p->num_seqs > cu ? 1 : 0;
 
   hipStream_t st = static_cast<hipStream_t>(stream);

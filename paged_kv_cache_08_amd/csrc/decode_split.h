@@ -206,6 +206,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   }
 
   const SplitSpan sp = split_span_len(a, L_in, s, 1);
+  flag_clamped(a, sp, s == 0 && g == 0 && tid == 0);
   if (sp.begin >= sp.L) {
     if (s == 0) {   // empty sequence: zeros (log-sum-exp -inf)
       for (int i = tid; i < G * D; i += kThreads) store_out(a, out_row0 + i, 0.0f);

@@ -105,7 +105,16 @@ struct SplitSpan {
   int begin;    // first token of the split
   int end;      // one past the last token
   int nsplit;   // splits this sequence uses
+  bool clamped; // the sequence length was cut to what the table or the plan can map
 };
+
+// Bit 2 of the workspace error word: a sequence longer than the launch can
+// map (seq_lens[b] above what max_pages_per_seq * block_size, or the splits
+// planned for max_seq_len, cover) was cut to that range. Reported once per
+// sequence, by the thread passed as `lead`.
+__device__ __forceinline__ void flag_clamped(const DecodeArgs& a, const SplitSpan& sp, bool lead) {
+  if (a.err && sp.clamped && lead) atomicOr(a.err, 4u);
+}
 
 // Longest token range the launch can map without a sliding window: what the
 // block table can address and what the planned splits cover. (The host keeps
@@ -126,14 +135,19 @@ __device__ __forceinline__ int planned_cap(const DecodeArgs& a) {
 __device__ __forceinline__ SplitSpan split_span_len(const DecodeArgs& a, int64_t L, int s, int rows) {
   const int64_t table_cap = int64_t(a.max_pages) * int64_t(a.bdiv.d);
   const int64_t planned = int64_t(a.num_splits) * a.chunk;
+  bool clamped = L > table_cap;
   L = L < 0 ? 0 : (L > table_cap ? table_cap : L);
   int64_t lo = 0;
   if (a.window > 0) {
     lo = L - rows + 1 - a.window;
     lo = lo < 0 ? 0 : lo;
   }
-  if (L - lo > planned) L = lo + planned;
+  if (L - lo > planned) {
+    L = lo + planned;
+    clamped = true;
+  }
   SplitSpan r;
+  r.clamped = clamped;
   r.L = int(L);
   r.lo = int(lo);
   r.begin = r.lo + s * a.chunk;
@@ -259,6 +273,7 @@ __device__ __forceinline__ void flag_invalid_entries(const DecodeArgs& a, const 
 __device__ __forceinline__ SplitSpan prefill_span(const DecodeArgs& a, int b, int n, int p0, int rows) {
   const int64_t table_cap = int64_t(a.max_pages) * int64_t(a.bdiv.d);
   int64_t L = a.seq_lens[b];
+  const bool clamped = L > table_cap;
   L = L < 0 ? 0 : (L > table_cap ? table_cap : L);
   int64_t end = L - n + p0 + rows;
   end = end < 0 ? 0 : end;
@@ -273,6 +288,7 @@ __device__ __forceinline__ SplitSpan prefill_span(const DecodeArgs& a, int b, in
   r.begin = r.lo;
   r.end = r.L;
   r.nsplit = 1;
+  r.clamped = clamped;
   return r;
 }
 

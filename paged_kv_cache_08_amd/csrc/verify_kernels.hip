@@ -153,6 +153,7 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
     if (a.window == 0) stage_table(a, b, g, pages.p_first, pages.n, tbl);
     sp = split_span(a, b, s, q_len);
   }
+  flag_clamped(a, sp, lead && g == 0 && tid == 0);
 
   if (sp.begin >= sp.L) {
     if (s == 0)   // empty sequence: zeros (log-sum-exp -inf) for every row of this KV head

@@ -1,0 +1,45 @@
+"""Error bit 2 of the workspace error word: a sequence longer than the call can
+map (seq_lens above what the splits planned for max_seq_len cover) is cut to
+that range and reported, on the single-query and on the multi-row kernel."""
+import numpy as np
+import pytest
+
+import oracle.paged_attention as O
+from paged_kv_cache_08_amd import workloads as W
+from tests.gpu_helpers import assert_matches_oracle, log, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("q_len", [1, 4])
+def test_length_beyond_the_plan_sets_bit2(q_len):
+    import torch
+    import paged_kv_cache_08_amd as P
+    log(f"case: seq_lens 3000 with max_seq_len 1000, q_len {q_len}")
+    case = W.make_case(304, [3000], q_len=q_len, block_size=16, boost_frac=0.05)
+    q, k, v, table, lens = to_device(case)
+    p = P.make_params(q, k, v, table, 16, case.scale, max_seq_len=1000)
+    ws = torch.zeros(P.workspace_bytes(p, 0), dtype=torch.uint8, device="cuda")
+    out = P.paged_decode_attention(q, k, v, table, lens, 16, case.scale, max_seq_len=1000, workspace=ws)
+    torch.cuda.synchronize()
+    assert P.read_error_word(ws) == 4
+    # the splits planned for 1000 tokens cover the first S * chunk of them
+    S, chunk = P.plan_splits(p, P.device_cu_count())
+    kept = S * chunk
+    assert 1000 <= kept < 3000
+    ref = O.paged_attention_ref(case.q, case.k_cache, case.v_cache, case.block_table, np.array([kept]),
+                                16, case.scale)
+    assert_matches_oracle(out.cpu().numpy().astype(np.float64), ref, f"cut to {kept} tokens")
+
+
+def test_lengths_within_the_plan_set_no_bit():
+    import torch
+    import paged_kv_cache_08_amd as P
+    log("case: seq_lens at max_seq_len sets no error bit")
+    case = W.make_case(305, [2000, 1999], block_size=784, interleave=True)
+    q, k, v, table, lens = to_device(case)
+    p = P.make_params(q, k, v, table, 784, case.scale, max_seq_len=2000)
+    ws = torch.zeros(P.workspace_bytes(p, 0), dtype=torch.uint8, device="cuda")
+    P.paged_decode_attention(q, k, v, table, lens, 784, case.scale, max_seq_len=2000, workspace=ws)
+    torch.cuda.synchronize()
+    assert P.read_error_word(ws) == 0
