@@ -185,6 +185,35 @@ int pkv_paged_decode_attention(const pkv_decode_params* p,
                                void* stream);
 
 /*
+ * The decode call for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * pkv_paged_decode_attention without a workspace argument. The split partials
+ * live in a scratch array inside the library, a
+ * file-scope device array of PKV_NOALLOC_SCRATCH_BYTES per GPU, held from the
+ * library's first call on that GPU until the process ends; no call allocates
+ * or frees memory.
+ *   p, q, k_cache, v_cache, block_table, seq_lens, out, lse, stream: as for
+ *               pkv_paged_decode_attention (same kernels, same plan, so the
+ *               same bits in out).
+ *   error_word  device uint32, 4-byte aligned, or NULL: receives the error
+ *               bits described for the workspace's error word (ORed in; the
+ *               caller zeroes it). With NULL the bits go to the scratch
+ *               array's own word, which nobody reads.
+ * Returns PKV_ERR_WORKSPACE, before any device work, when the call would need
+ * more than PKV_NOALLOC_SCRATCH_BYTES (pkv_workspace_bytes(p, 0) bytes;
+ * e.g. 24 query heads, head_dim 256 and q_len 1 fit about 1,300 splits of
+ * 512 tokens). Every call on one GPU shares that GPU's scratch, which keeps
+ * the last call's contents: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must not be issued.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
+
+int pkv_paged_decode_attention_noalloc(const pkv_decode_params* p,
+                                       const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_table, const int32_t* seq_lens,
+                                       void* out, float* lse, uint32_t* error_word, void* stream);
+
+/*
  * Varlen multi-row call: sequence b has its own number of new query rows,
  * n_b = cu_seqlens_q[b + 1] - cu_seqlens_q[b] in [0, q_len], in one batched
  * call (batched speculative verify). The rows of all sequences are packed:

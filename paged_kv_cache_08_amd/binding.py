@@ -20,6 +20,7 @@ PKV_ERR_WORKSPACE = -3
 PKV_ERR_HIP = -4
 PKV_OUT_F32 = 0
 PKV_PREFILL_WORKSPACE_BYTES = 256   # prefill calls: the error-word header only
+PKV_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024   # the no-allocation call's scratch array per GPU
 PKV_OUT_BF16 = 1
 PKV_KV_BF16 = 0
 PKV_KV_FP8_E4M3 = 1
@@ -73,6 +74,7 @@ _SIGNATURES = {
     "pkv_device_cu_count": (ctypes.c_int, [_i32p]),
     "pkv_paged_decode_attention": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64,
                                                   _vp]),
+    "pkv_paged_decode_attention_noalloc": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "pkv_paged_varlen_attention": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                   ctypes.c_int64, _vp]),
     "pkv_paged_prefill_attention": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -245,6 +247,37 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, block_siz
         seq_lens.data_ptr(), out.data_ptr(), _lse_ptr(lse, q.shape[:-1]), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), stream)
     check(rc, "pkv_paged_decode_attention")
+    return out
+
+
+def paged_decode_attention_noalloc(q, k_cache, v_cache, block_table, seq_lens, block_size: int, scale: float,
+                                   *, max_seq_len: int, out, total_tokens: int = 0, num_splits: int = 0,
+                                   stream=None, window: int = 0, k_scale: float = 1.0, v_scale: float = 1.0,
+                                   lse=None, error_word=None):
+    """paged_decode_attention through the entry point that allocates nothing:
+    the split partials live in the library's scratch array, so there is no
+    workspace, and ``out`` (and ``lse``) must be given. error_word: optional
+    int32 tensor of one element on the GPU that receives the error bits."""
+    torch = _torch()
+    assert q.is_cuda and q.dtype == torch.bfloat16 and q.is_contiguous()
+    assert k_cache.dtype in _KV_DTYPES() and v_cache.dtype == k_cache.dtype
+    assert block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32
+    assert block_table.is_contiguous() and seq_lens.is_contiguous()
+    odt = PKV_OUT_BF16 if out.dtype == torch.bfloat16 else PKV_OUT_F32
+    assert out.dtype in (torch.float32, torch.bfloat16) and out.is_contiguous() and out.shape == q.shape
+    p = make_params(q, k_cache, v_cache, block_table, block_size, scale, max_seq_len=max_seq_len,
+                    num_splits=num_splits, total_tokens=total_tokens, out_dtype=odt, window=window,
+                    k_scale=k_scale, v_scale=v_scale)
+    err = None
+    if error_word is not None:
+        assert error_word.is_cuda and error_word.dtype == torch.int32 and error_word.numel() == 1
+        err = error_word.data_ptr()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib().pkv_paged_decode_attention_noalloc(
+        ctypes.byref(p), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+        seq_lens.data_ptr(), out.data_ptr(), _lse_ptr(lse, q.shape[:-1]), err, stream)
+    check(rc, "pkv_paged_decode_attention_noalloc")
     return out
 
 

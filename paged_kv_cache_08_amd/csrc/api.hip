@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "pkv.h"
@@ -246,7 +247,8 @@ int validate_any(const pkv_decode_params* p);
 // kernel.
 int launch_call(const pkv_decode_params* p, const void* q, const void* k_cache, const void* v_cache,
                 const int32_t* block_table, const int32_t* seq_lens, const int32_t* cu_q, void* out,
-                float* lse, void* workspace, int64_t workspace_bytes, void* stream) {
+                float* lse, void* workspace, int64_t workspace_bytes, void* stream,
+                uint32_t* error_word = nullptr) {
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out || !workspace)
     return fail(PKV_ERR_INVALID, "a device pointer is NULL");
   if ((reinterpret_cast<uintptr_t>(lse) & 3) != 0) return fail(PKV_ERR_INVALID, "lse must be 4-byte aligned");
@@ -274,7 +276,7 @@ int launch_call(const pkv_decode_params* p, const void* q, const void* k_cache, 
   a.lse = lse;
   char* ws = static_cast<char*>(workspace);
   const WsLayout wl = workspace_layout(p, S);
-  a.err = reinterpret_cast<uint32_t*>(ws);
+  a.err = error_word ? error_word : reinterpret_cast<uint32_t*>(ws);
   a.part_ml = reinterpret_cast<float*>(ws + wl.ml);
   a.part_acc = reinterpret_cast<float*>(ws + wl.acc);
   a.many_wg = int64_t(S) * p->num_kv_heads * p->num_seqs > cu ? 1 : 0;
@@ -299,6 +301,38 @@ int launch_call(const pkv_decode_params* p, const void* q, const void* k_cache, 
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
   }
   g_last_variant = VariantInfo{split_name, p->head_dim, group, p->q_len, window, S, chunk, p->block_size};
+  return PKV_OK;
+}
+
+// Scratch memory of the call that allocates nothing: a file-scope device
+// array (one copy per GPU, held until the process ends), laid out like a
+// workspace. Nothing in it has to start at zero: the partials are written
+// before they are read, and the error bits go to the caller's word (or to
+// the array's own first word, which nothing reads).
+constexpr int64_t kScratchBytes = PKV_NOALLOC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {nullptr};
+
+// The device address of `scratch` on the current device, found once per
+// device with hipGetSymbolAddress (the host-side name of the array is not a
+// device address).
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(PKV_ERR_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr || (reinterpret_cast<uintptr_t>(ptr) & 255) != 0)
+      return fail(PKV_ERR_HIP, "scratch array has no 256-byte aligned device address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
   return PKV_OK;
 }
 
@@ -363,6 +397,29 @@ int pkv_paged_decode_attention(const pkv_decode_params* p, const void* q, const 
   if (rc) return rc;
   return launch_call(p, q, k_cache, v_cache, block_table, seq_lens, nullptr, out, lse, workspace, workspace_bytes,
                      stream);
+}
+
+int pkv_paged_decode_attention_noalloc(const pkv_decode_params* p, const void* q, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                                       void* out, float* lse, uint32_t* error_word, void* stream) {
+  int rc = pkv_validate_params(p);
+  if (rc) return rc;
+  if ((reinterpret_cast<uintptr_t>(error_word) & 3) != 0)
+    return fail(PKV_ERR_INVALID, "error_word must be 4-byte aligned");
+  int32_t cu = 0;
+  rc = device_cu_count(&cu);
+  if (rc) return rc;
+  int32_t S = 0, chunk = 0;
+  plan(p, cu, &S, &chunk);
+  const int64_t need = workspace_for(p, S);
+  if (need > kScratchBytes)
+    return fail(PKV_ERR_WORKSPACE, "the call needs " + std::to_string(need) + " bytes of scratch; the library's "
+                "scratch holds " + std::to_string(kScratchBytes) + " (use pkv_paged_decode_attention with a workspace)");
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc) return rc;
+  return launch_call(p, q, k_cache, v_cache, block_table, seq_lens, nullptr, out, lse, ws, kScratchBytes, stream,
+                     error_word);
 }
 
 int pkv_paged_varlen_attention(const pkv_decode_params* p, const void* q, const void* k_cache,
