@@ -9,7 +9,16 @@ head_dim 256, page 784, context 32768, bf16 K/V with 5% of key rows x4.
 To measure HBM and not the 256 MB Infinity Cache, steps rotate through
 ``--pools`` independent copies of the KV pool (16 by default, about 2.7 GB, as
 16 full-attention layers of one decode step would). Timing uses HIP events on
-the stream the library launches on. One JSON line goes to stdout.
+the stream the library launches on. One JSON line goes to stdout; with
+``--ladder``, one line per context / page-size row and a summary line with the
+fit t(L) = a + b * L and the page-size check.
+
+Every run checks the timed output against the fp64 oracle (every element, or
+sampled rows for prefill) with max abs error <= 2e-3 and max relative error
+<= 1e-2 (relative to max(|oracle|, 1e-3)); the result is in the line's
+``parity`` field, and a failed or skipped check makes the run exit with
+status 3. The ``identity`` field carries the sha256 of the loaded libpkv.so,
+of the kernel sources and of the input bytes.
 """
 from __future__ import annotations
 
@@ -37,7 +46,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1000,
                     help="untimed steps first; fewer than about 500 leave the first timed region "
                          "about 5%% slow while the GPU settles (about 30 ms of work at the default size)")
-    ap.add_argument("--workload", default="hybrid", choices=["hybrid", "dense", "mixed", "verify", "varlen", "prefill"])
+    ap.add_argument("--workload", default="hybrid",
+                    choices=["hybrid", "single", "dense", "mixed", "verify", "varlen", "prefill"],
+                    help="hybrid: one 24/4/256 sequence (page --block-size, --context tokens); single: batch 1, "
+                         "page 16, 512 tokens, 32 of 64 pages; dense: 32/8/128, page 16; mixed: 16 sequences; "
+                         "verify: q_len 16; varlen: batched verify; prefill: one chunk of --chunk rows")
     ap.add_argument("--context", type=int, default=None,
                     help="tokens in the cache (default 32768; 8192 for prefill)")
     ap.add_argument("--chunk", type=int, default=4096, help="prefill: new query rows of the chunk")
@@ -55,8 +68,13 @@ def parse():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before timing, copy this many MiB once (a kernel of known traffic, used to "
                          "scale rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--ladder", action="store_true",
+                    help="the context ladder (1K, 4K, 16K, 32K at page 784; 32K at pages 832 and 16) of the "
+                         "hybrid decode: one JSON line per row, then the fit t(L) = a + b * L and the page-size check")
     args = ap.parse_args()
-    if args.context is None:
+    if args.workload == "single":
+        args.context = 512
+    elif args.context is None:
         args.context = 8192 if args.workload == "prefill" else 32768
     return args
 
@@ -91,7 +109,10 @@ class Hip:
 def make_workload(args):
     from paged_kv_cache_08_amd import workloads as W
     kv = dict(kv_dtype="fp8_e4m3") if args.kv_dtype == "fp8" else {}
-    if args.workload == "hybrid":
+    if args.workload == "single":
+        case = W.single_seq_b16(poison=False, **kv)
+        name = "single sequence: batch 1, q_len 1, 24 q / 4 KV heads, head_dim 256, page 16, 512 tokens, 32 of 64 pages"
+    elif args.workload == "hybrid":
         case = W.hybrid_long_context(args.context, block_size=args.block_size, poison=False, **kv)
         name = (f"hybrid decode: batch 1, q_len 1, 24 q / 4 KV heads, head_dim 256, page {args.block_size}, "
                 f"context {args.context}, 5% of keys x4")
@@ -239,22 +260,53 @@ def cpu_baseline(case, varlen, window, kv_bytes_per_call, seconds):
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards by sequence, KV head or context range; this harness measures one GPU's share)", file=sys.stderr)
-        sys.exit(2)
+PARITY_ATOL = 2e-3       # max |gpu - oracle|
+PARITY_RTOL = 1e-2       # max |gpu - oracle| / max(|oracle|, 1e-3)
+PARITY_REL_FLOOR = 1e-3
 
+
+def _sha256(*arrays) -> str:
+    import hashlib
+    import numpy as np
+    h = hashlib.sha256()
+    for a in arrays:
+        a = np.ascontiguousarray(a)
+        h.update(str(a.dtype).encode() + str(a.shape).encode())
+        h.update(a.view(np.uint8).reshape(-1).data)
+    return h.hexdigest()
+
+
+def _file_sha256(path: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    with open(path, "rb") as fh:
+        for chunk in iter(lambda: fh.read(1 << 20), b""):
+            h.update(chunk)
+    return h.hexdigest()
+
+
+def trace_from_profiles(kernel_src_hash: str, workload_key: str):
+    """The split kernel's average duration in the committed rocprofv3 kernel
+    trace of this workload, if that trace was taken on the current kernel
+    source; else None."""
+    path = os.path.join(ROOT, "profiles", "kernel_trace.json")
+    try:
+        rec = json.load(open(path)).get(workload_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_src_sha256") != kernel_src_hash:
+        return None
+    return rec
+
+
+def measure(args, dev, hip, emit_cpu=True):
+    """One workload: set up, warm up, time, check parity. Returns (record, parity_ok)."""
     import numpy as np
     import torch
 
     import paged_kv_cache_08_amd as P
     from paged_kv_cache_08_amd import workloads as W
 
-    assert torch.cuda.is_available(), "no GPU"
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     case, wl_name, varlen = make_workload(args)
     prefill = args.workload == "prefill"
     print(f"[bench] workload: {wl_name}", file=sys.stderr, flush=True)
@@ -277,6 +329,8 @@ def main():
         scales = {}
     table = torch.from_numpy(case.block_table).to(dev)
     lens = torch.from_numpy(case.seq_lens).to(dev)
+    input_sha = _sha256(case.q if varlen is None else varlen[0], case.k_cache, case.v_cache, case.block_table,
+                        case.seq_lens, *(() if varlen is None else (varlen[1],)))
     pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(max(args.pools, 1) - 1)]
     total_tokens = int(case.seq_lens.sum())
     rows = [case.q_len] * case.num_seqs if varlen is None else np.diff(varlen[1])
@@ -307,7 +361,6 @@ def main():
         print(f"[bench] calibration copy: {n} bytes read, {n} bytes written", file=sys.stderr, flush=True)
         del src, dst, flush
 
-    hip = Hip()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -379,20 +432,30 @@ def main():
         graph_us = statistics.median(graph_regions)
         del graph
 
-    # Spot parity on sampled heads of the timed output (pool 0 holds the seeded input).
+    # Parity on the timed output (pool 0 holds the seeded input): every element
+    # against the oracle, or sampled rows one by one for prefill (a whole
+    # prefill oracle call is minutes of CPU work). A failed or skipped check
+    # fails the run.
     step(0)
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
-    parity = None
+    parity = {"atol": PARITY_ATOL, "rtol": PARITY_RTOL, "rel_floor": PARITY_REL_FLOOR, "ok": False}
     try:
-        if prefill:   # sampled rows: a whole oracle call is minutes of CPU work
+        if prefill:
             sample = [0, 1, 2047, int(varlen[1][1]) - 1]
-            parity = float(np.abs(got[sample] - oracle_rows(case, varlen, sample, args.window)).max())
+            g, ref = got[sample], oracle_rows(case, varlen, sample, args.window)
+            parity["checked"] = f"rows {sample} of the chunk, every head and column"
         else:
-            ref = oracle_call(case, varlen, args.window)
-            parity = float(np.abs(got - ref).max())
-    except Exception as e:  # parity is reported, never required for the timing
-        print(f"[bench] parity check skipped: {e}", file=sys.stderr)
+            g, ref = got, oracle_call(case, varlen, args.window)
+            parity["checked"] = "every output element"
+        err = np.abs(g - ref)
+        parity["max_abs_err"] = float(err.max())
+        parity["max_rel_err"] = float((err / np.maximum(np.abs(ref), PARITY_REL_FLOOR)).max())
+        parity["ok"] = bool(np.all(np.isfinite(g)) and parity["max_abs_err"] <= PARITY_ATOL
+                            and parity["max_rel_err"] <= PARITY_RTOL)
+    except Exception as e:
+        parity["error"] = f"{type(e).__name__}: {e}"
+        print(f"[bench] parity check failed to run: {e}", file=sys.stderr)
 
     gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
     kern_gbs = kv_bytes / (kern_avg_us * 1e-6) / 1e9
@@ -402,27 +465,40 @@ def main():
               + (f":w{args.window}" if args.window else "")
               + (":fp8" if args.kv_dtype == "fp8" else ""))
     traffic = traffic_from_profiles(src_hash, wl_key)
+    trace = trace_from_profiles(src_hash, wl_key)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if emit_cpu and not args.no_cpu_baseline:
         if prefill:
             cpu = cpu_baseline_rows(case, varlen, args.window, args.cpu_seconds)
         else:
             cpu = cpu_baseline(case, varlen, args.window, kv_bytes, args.cpu_seconds)
 
+    kernel = ("verify_split_kernel (prefill blocks)" if prefill else
+              "verify_split_kernel" if (case.q_len > 1 or varlen is not None) else "decode_split_kernel")
+    timing_src = ("HIP events that the library records on its stream right around the split kernel "
+                  "(hipExtLaunchKernel), averaged over the K launches after the timed regions")
     if prefill:   # a dense contraction: priced against the bf16 MFMA peak
         tflops = flops / (ms_per_step * 1e-3) / 1e12
         kern_tflops = flops / (kern_avg_us * 1e-6) / 1e12
         value, unit = round(tflops, 2), "TFLOP/s"
-        roof = {"bound": "mfma", "kernel": "verify_split_kernel (prefill blocks)", "achieved": round(kern_tflops, 2),
+        roof = {"bound": "mfma", "kernel": kernel, "achieved": round(kern_tflops, 2),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+        per_us = lambda us: flops / (us * 1e-6) / 1e12  # noqa: E731
+        peak = MFMA_BF16_PEAK_TFLOPS
     else:
         value, unit = round(gbs, 1), "GB/s"
-        roof = {"bound": "hbm",
-                "kernel": "verify_split_kernel" if (case.q_len > 1 or varlen is not None) else "decode_split_kernel",
-                "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(kern_gbs / HBM_PEAK_GBS, 4)}
-    roof.update({"traffic": traffic, "kernel_us_avg": round(kern_avg_us, 2), "kernel_us_min": round(min(kern_us), 2)})
+        roof = {"bound": "hbm", "kernel": kernel, "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4)}
+        per_us = lambda us: kv_bytes / (us * 1e-6) / 1e9  # noqa: E731
+        peak = HBM_PEAK_GBS
+    roof.update({"traffic": traffic, "kernel_us_avg": round(kern_avg_us, 2), "kernel_us_min": round(min(kern_us), 2),
+                 "timing": timing_src})
+    if trace:
+        us = trace["kernel_us_avg"]
+        roof["trace"] = {"kernel_us_avg": us, "achieved": round(per_us(us), 1), "frac": round(per_us(us) / peak, 4),
+                         "source": f"profiles/kernel_trace.json [{wl_key}] (rocprofv3 --kernel-trace, "
+                                   f"{trace.get('calls', '?')} launches)"}
 
     med = statistics.median(region_us)
     rec = {
@@ -463,9 +539,84 @@ def main():
         "graph_us_per_step": None if graph_us is None else round(graph_us, 2),
         "graph_gbs": None if graph_us is None else round(kv_bytes / (graph_us * 1e-6) / 1e9, 1),
         "cpu_baseline": cpu,
-        "parity_max_abs_err": parity,
+        "parity": parity,
+        "identity": {
+            "libpkv_sha256": _file_sha256(P.binding.LIB_PATH),
+            "kernel_src_sha256": src_hash,
+            "input_sha256": input_sha,
+            "library": P.version(),
+        },
     }
-    print(json.dumps(rec))
+    del pools, call
+    torch.cuda.empty_cache()
+    return rec, parity["ok"]
+
+
+LADDER = [(1024, 784), (4096, 784), (16384, 784), (32768, 784), (32768, 832), (32768, 16)]
+
+
+def ladder(args, dev, hip):
+    """The hybrid decode over the context ladder and the page sizes: one JSON
+    line per row, then a summary line with the least-squares fit
+    t(L) = a + b * L over the page-784 contexts and the spread of the 32K
+    times across page sizes (the no-cliff check, within 5%)."""
+    import numpy as np
+    rows, ok_all = [], True
+    for ctx, bs in LADDER:
+        a = argparse.Namespace(**vars(args))
+        a.workload, a.context, a.block_size = "hybrid", ctx, bs
+        rec, ok = measure(a, dev, hip, emit_cpu=False)
+        ok_all &= ok
+        row = {"ladder_row": True, "context": ctx, "block_size": bs, "us_per_step": rec["us_per_step"],
+               "gbs": rec["value"], "pct_hbm_peak": rec["pct_hbm_peak"],
+               "kernel_us_avg": rec["roofline"]["kernel_us_avg"], "variant": rec["config"]["variant"],
+               "parity_ok": ok, "max_abs_err": rec["parity"].get("max_abs_err"),
+               "input_sha256": rec["identity"]["input_sha256"]}
+        print(json.dumps(row), flush=True)
+        rows.append(row)
+    fit = [(r["context"], r["us_per_step"]) for r in rows if r["block_size"] == 784]
+    L = np.array([f[0] for f in fit], dtype=np.float64)
+    t = np.array([f[1] for f in fit], dtype=np.float64)
+    b, a0 = np.polyfit(L, t, 1)
+    t32 = {r["block_size"]: r["us_per_step"] for r in rows if r["context"] == 32768}
+    spread = (max(t32.values()) - min(t32.values())) / min(t32.values())
+    summary = {
+        "ladder_summary": True,
+        "fit": {"a_us": round(float(a0), 3), "b_ns_per_token": round(float(b) * 1e3, 4),
+                "points": [[int(x), float(y)] for x, y in fit],
+                "b_16_layers_us_per_token": round(16 * float(b), 6),
+                "pages_context_us_per_token": {"hybrid_dual_radeon": 4.840, "dense_8b_dual_radeon": 0.118}},
+        "page_sizes_at_32k_us": {str(k): v for k, v in t32.items()},
+        "page_size_spread_pct": round(100.0 * spread, 2),
+        "no_cliff": bool(spread <= 0.05),
+        "parity_ok": bool(ok_all),
+        "steps": args.steps, "warmup": args.warmup,
+    }
+    print(json.dumps(summary), flush=True)
+    return ok_all
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence, KV head or context range; this harness measures one GPU's share)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    assert torch.cuda.is_available(), "no GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hip = Hip()
+    if args.ladder:
+        ok = ladder(args, dev, hip)
+    else:
+        rec, ok = measure(args, dev, hip)
+        print(json.dumps(rec), flush=True)
+    if not ok:
+        print("[bench] parity against the oracle failed or did not run: see the parity field", file=sys.stderr)
+        sys.exit(3)
 
 
 if __name__ == "__main__":

@@ -176,6 +176,16 @@ def _torch():
     return torch
 
 
+def _alloc(shape, dtype, device, fill=None):
+    """Device buffers the binding allocates for the caller (out, workspace,
+    debug outputs): uninitialised, or filled with `fill`. A module-level
+    function so that tests can put every such buffer between guard zones."""
+    torch = _torch()
+    if fill is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    return torch.full(shape, fill, dtype=dtype, device=device)
+
+
 def make_params(q, k_cache, v_cache, block_table, block_size: int, scale: float, *, max_seq_len: int,
                 num_splits: int = 0, total_tokens: int = 0, out_dtype: int = PKV_OUT_F32,
                 window: int = 0, k_scale: float = 1.0, v_scale: float = 1.0) -> DecodeParams:
@@ -231,7 +241,7 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, block_siz
     if max_seq_len is None:
         max_seq_len = int(seq_lens.max().item()) if seq_lens.numel() else 0
     if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+        out = _alloc(q.shape, out_dtype or torch.float32, q.device)
     odt = PKV_OUT_BF16 if out.dtype == torch.bfloat16 else PKV_OUT_F32
     assert out.dtype in (torch.float32, torch.bfloat16) and out.is_contiguous() and out.shape == q.shape
     p = make_params(q, k_cache, v_cache, block_table, block_size, scale, max_seq_len=max_seq_len,
@@ -239,7 +249,7 @@ def paged_decode_attention(q, k_cache, v_cache, block_table, seq_lens, block_siz
                     k_scale=k_scale, v_scale=v_scale)
     need = workspace_bytes(p, 0)
     if workspace is None:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        workspace = _alloc((need,), torch.uint8, q.device, 0)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     rc = lib().pkv_paged_decode_attention(
@@ -315,7 +325,7 @@ def paged_varlen_attention(q, k_cache, v_cache, block_table, seq_lens, cu_seqlen
     ns = seq_lens.shape[0]
     assert cu_seqlens_q.shape[0] == ns + 1 and block_table.shape[0] == ns
     if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+        out = _alloc(q.shape, out_dtype or torch.float32, q.device)
     odt = PKV_OUT_BF16 if out.dtype == torch.bfloat16 else PKV_OUT_F32
     assert out.dtype in (torch.float32, torch.bfloat16) and out.is_contiguous() and out.shape == q.shape
     shape4 = torch.empty((ns, int(max_q_len), q.shape[1], q.shape[2]), device="meta")
@@ -324,7 +334,7 @@ def paged_varlen_attention(q, k_cache, v_cache, block_table, seq_lens, cu_seqlen
                     k_scale=k_scale, v_scale=v_scale)
     need = workspace_bytes(p, 0)
     if workspace is None:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        workspace = _alloc((need,), torch.uint8, q.device, 0)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     rc = lib().pkv_paged_varlen_attention(
@@ -352,14 +362,14 @@ def paged_prefill_attention(q, k_cache, v_cache, block_table, seq_lens, cu_seqle
     ns = seq_lens.shape[0]
     assert cu_seqlens_q.shape[0] == ns + 1 and block_table.shape[0] == ns
     if out is None:
-        out = torch.empty(q.shape, dtype=out_dtype or torch.float32, device=q.device)
+        out = _alloc(q.shape, out_dtype or torch.float32, q.device)
     odt = PKV_OUT_BF16 if out.dtype == torch.bfloat16 else PKV_OUT_F32
     assert out.dtype in (torch.float32, torch.bfloat16) and out.is_contiguous() and out.shape == q.shape
     shape4 = torch.empty((ns, int(max_q_len), q.shape[1], q.shape[2]), device="meta")
     p = make_params(shape4, k_cache, v_cache, block_table, block_size, scale, max_seq_len=max_seq_len,
                     out_dtype=odt, window=window, k_scale=k_scale, v_scale=v_scale)
     if workspace is None:
-        workspace = torch.zeros(PKV_PREFILL_WORKSPACE_BYTES, dtype=torch.uint8, device=q.device)
+        workspace = _alloc((PKV_PREFILL_WORKSPACE_BYTES,), torch.uint8, q.device, 0)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     rc = lib().pkv_paged_prefill_attention(
@@ -375,8 +385,8 @@ def debug_token_offsets(p: DecodeParams, block_table, seq_lens, kv_head: int):
     -2 for an invalid page entry, -3 where the staged-table and direct-table paths disagree)."""
     torch = _torch()
     shape = (p.num_seqs, max(p.max_seq_len, 1))
-    k_off = torch.empty(shape, dtype=torch.int64, device=block_table.device)
-    v_off = torch.empty(shape, dtype=torch.int64, device=block_table.device)
+    k_off = _alloc(shape, torch.int64, block_table.device)
+    v_off = _alloc(shape, torch.int64, block_table.device)
     stream = torch.cuda.current_stream(block_table.device).cuda_stream
     check(lib().pkv_debug_token_offsets(ctypes.byref(p), block_table.data_ptr(), seq_lens.data_ptr(), kv_head,
                                         k_off.data_ptr(), v_off.data_ptr(), stream), "pkv_debug_token_offsets")
@@ -387,7 +397,7 @@ def debug_split_ranges(p: DecodeParams, seq_lens):
     """[num_seqs, S, 2] contiguous split ranges as the multi-row kernel derives them."""
     torch = _torch()
     S, _ = plan_splits(p, device_cu_count())
-    r = torch.empty((p.num_seqs, S, 2), dtype=torch.int32, device=seq_lens.device)
+    r = _alloc((p.num_seqs, S, 2), torch.int32, seq_lens.device)
     stream = torch.cuda.current_stream(seq_lens.device).cuda_stream
     check(lib().pkv_debug_split_ranges(ctypes.byref(p), seq_lens.data_ptr(), r.data_ptr(), stream),
           "pkv_debug_split_ranges")
@@ -398,7 +408,7 @@ def debug_token_splits(p: DecodeParams, seq_lens):
     """[num_seqs, max_seq_len, 2] int32 (split, window slot) with which the single-query
     split kernel reads each token; (-1, -1) for tokens no split reads. q_len must be 1."""
     torch = _torch()
-    r = torch.empty((p.num_seqs, max(p.max_seq_len, 1), 2), dtype=torch.int32, device=seq_lens.device)
+    r = _alloc((p.num_seqs, max(p.max_seq_len, 1), 2), torch.int32, seq_lens.device)
     stream = torch.cuda.current_stream(seq_lens.device).cuda_stream
     check(lib().pkv_debug_token_splits(ctypes.byref(p), seq_lens.data_ptr(), r.data_ptr(), stream),
           "pkv_debug_token_splits")
@@ -430,7 +440,7 @@ class PreparedDecode:
         assert q.is_cuda and q.dtype == torch.bfloat16 and q.is_contiguous()
         assert block_table.is_contiguous() and seq_lens.is_contiguous()
         if out is None:
-            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+            out = _alloc(q.shape, torch.float32, q.device)
         odt = PKV_OUT_BF16 if out.dtype == torch.bfloat16 else PKV_OUT_F32
         self.varlen = cu_seqlens_q is not None
         assert self.varlen or not prefill, "prefill calls take packed rows and cu_seqlens_q"
@@ -447,7 +457,7 @@ class PreparedDecode:
             check(validate(self.params), "pkv_validate_params")
         need = PKV_PREFILL_WORKSPACE_BYTES if prefill else workspace_bytes(self.params, 0)
         if workspace is None:
-            workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+            workspace = _alloc((need,), torch.uint8, q.device, 0)
         assert workspace.numel() * workspace.element_size() >= need
         if stream is None:
             stream = torch.cuda.current_stream(q.device).cuda_stream

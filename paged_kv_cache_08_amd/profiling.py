@@ -12,6 +12,12 @@
         __amd_rocclr_copyBuffer dispatch, which copies N bytes). The record is
         stored under KEY with the hash of the kernel sources it was taken on.
 
+    python -m paged_kv_cache_08_amd.profiling trace --kernel NAME --key KEY --out profiles/kernel_trace.json DB...
+        The average, min and max duration of kernel NAME (and of the merge
+        kernel, if it ran) in one --kernel-trace run, stored under KEY with
+        the hash of the kernel sources it was taken on (bench.py reports it
+        next to its event-timed figure while the sources still match).
+
     python -m paged_kv_cache_08_amd.profiling counters --kernel NAME DB...
         Shader counters of kernel NAME from one or more --pmc runs (each with
         GRBM_GUI_ACTIVE), averaged over dispatches, and the busy / utilisation
@@ -161,6 +167,42 @@ def stats_table(paths) -> str:
     return "\n".join(rows)
 
 
+def trace_record(paths, kernel: str) -> dict:
+    """Duration statistics of `kernel` (and of the LSE merge) over kernel-trace runs."""
+    durs = collections.defaultdict(list)
+    for p in paths:
+        for name, d in kernel_durations(p).items():
+            durs[name].extend(d)
+
+    def pick(sub):
+        ks = [k for k in durs if sub in k]
+        if not ks:
+            return None
+        d = [x for k in ks for x in durs[k]]
+        return d
+
+    d = pick(kernel)
+    if d is None:
+        raise KeyError(f"no dispatches of {kernel}")
+    rec = {"kernel": kernel, "calls": len(d), "kernel_us_avg": round(sum(d) / len(d), 2),
+           "kernel_us_min": round(min(d), 2), "kernel_us_max": round(max(d), 2),
+           "kernel_src_sha256": kernel_source_hash()}
+    m = pick("lse_merge")
+    if m:
+        rec["merge_us_avg"] = round(sum(m) / len(m), 2)
+    return rec
+
+
+def _store(out: str, key: str, rec: dict) -> None:
+    data = {}
+    if os.path.exists(out):
+        with open(out) as fh:
+            data = json.load(fh)
+    data[key] = rec
+    with open(out, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+
+
 def traffic(fetch_db: str, write_db: str, kernel: str, calib_bytes: int) -> dict:
     f = pmc_per_dispatch(fetch_db, "FETCH_SIZE")
     w = pmc_per_dispatch(write_db, "WRITE_SIZE")
@@ -205,6 +247,11 @@ def main(argv=None):
     t.add_argument("--calib-bytes", type=int, required=True)
     t.add_argument("--key", required=True)
     t.add_argument("--out", required=True)
+    r = sub.add_parser("trace")
+    r.add_argument("--kernel", required=True)
+    r.add_argument("--key", required=True)
+    r.add_argument("--out", required=True)
+    r.add_argument("db", nargs="+")
     c = sub.add_parser("counters")
     c.add_argument("--kernel", required=True)
     c.add_argument("db", nargs="+")
@@ -212,18 +259,18 @@ def main(argv=None):
     if a.cmd == "stats":
         print(stats_table(a.db))
         return 0
+    if a.cmd == "trace":
+        paths = [p for pat in a.db for p in (glob.glob(pat) or [pat])]
+        rec = trace_record(paths, a.kernel)
+        _store(a.out, a.key, rec)
+        print(json.dumps(rec, indent=1))
+        return 0
     if a.cmd == "counters":
         paths = [p for pat in a.db for p in (glob.glob(pat) or [pat])]
         print(counter_table(counter_summary(paths, a.kernel)))
         return 0
     rec = traffic(a.fetch_db, a.write_db, a.kernel, a.calib_bytes)
-    data = {}
-    if os.path.exists(a.out):
-        with open(a.out) as fh:
-            data = json.load(fh)
-    data[a.key] = rec
-    with open(a.out, "w") as fh:
-        json.dump(data, fh, indent=1, sort_keys=True)
+    _store(a.out, a.key, rec)
     print(json.dumps(rec, indent=1))
     return 0
 

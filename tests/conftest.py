@@ -26,3 +26,21 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _guard_zones(request):
+    """GPU tests: the binding allocates out / workspace / debug buffers between
+    guard zones, and every zone is checked when the test ends."""
+    if "gpu" not in request.keywords:
+        yield
+        return
+    import paged_kv_cache_08_amd.binding as B
+    from tests import gpu_helpers as H
+    saved = B._alloc
+    B._alloc = H.guarded
+    try:
+        yield
+    finally:
+        B._alloc = saved
+        H.check_guards()

@@ -9,6 +9,45 @@ RTOL = 1e-2        # max |gpu - oracle| / max(|oracle|, REL_FLOOR)
 REL_FLOOR = 1e-3
 
 
+# Guard zones: every device buffer a GPU test hands to the library for writing
+# (out, lse, workspace, error word, debug outputs; the binding's own
+# allocations go through the same allocator during GPU tests) sits between two
+# GUARD_BYTES regions filled with GUARD_BYTE; after each GPU test the regions
+# are checked, so a kernel that writes past either end of a buffer fails the
+# test that ran it.
+GUARD_BYTES = 4096
+GUARD_BYTE = 0xA5
+_guarded = []
+
+
+def guarded(shape, dtype, device="cuda", fill=None):
+    """A tensor of `shape` / `dtype` inside a guard-zone slab; uninitialised
+    (the guard pattern) unless `fill` is given."""
+    import torch
+    shape = tuple(int(x) for x in (shape if isinstance(shape, (tuple, list)) else (shape,)))
+    n = int(np.prod(shape, dtype=np.int64)) * torch.empty((), dtype=dtype).element_size()
+    slab = torch.full((2 * GUARD_BYTES + n,), GUARD_BYTE, dtype=torch.uint8, device=device)
+    t = slab[GUARD_BYTES:GUARD_BYTES + n].view(dtype).view(shape)
+    if fill is not None:
+        t.fill_(fill)
+    _guarded.append((slab, n))
+    return t
+
+
+def check_guards():
+    """Synchronise and check every guard zone handed out since the last check."""
+    import torch
+    torch.cuda.synchronize()
+    bad = []
+    for slab, n in _guarded:
+        head = slab[:GUARD_BYTES].cpu().numpy()
+        tail = slab[GUARD_BYTES + n:].cpu().numpy()
+        if np.any(head != GUARD_BYTE) or np.any(tail != GUARD_BYTE):
+            bad.append((n, int(np.count_nonzero(head != GUARD_BYTE)), int(np.count_nonzero(tail != GUARD_BYTE))))
+    _guarded.clear()
+    assert not bad, f"writes into guard zones (buffer bytes, bytes changed before, after): {bad}"
+
+
 def log(msg: str) -> None:
     print(msg, flush=True)
     sys.stdout.flush()
@@ -102,7 +141,7 @@ def run_gpu_varlen(case, q_packed, cu, *, out=None, workspace=None, **kw):
         p = P.make_params(torch.empty((case.num_seqs, max(max_q, 1), q.shape[1], q.shape[2]), device="meta"),
                           k, v, table, case.block_size, case.scale, max_seq_len=case.max_seq_len,
                           num_splits=kw.get("num_splits", 0))
-        workspace = torch.zeros(P.workspace_bytes(p, 0), dtype=torch.uint8, device="cuda")
+        workspace = guarded(P.workspace_bytes(p, 0), torch.uint8, fill=0)
     got = P.paged_varlen_attention(q, k, v, table, lens, cu_t, case.block_size, case.scale,
                                    max_q_len=max(max_q, 1), max_seq_len=case.max_seq_len, out=out,
                                    workspace=workspace, **kv_kwargs(case), **kw)

@@ -6,6 +6,7 @@ import pytest
 import oracle.paged_attention as O
 from paged_kv_cache_08_amd import workloads as W
 from tests.gpu_helpers import ATOL, REL_FLOOR, assert_matches_oracle, bf16_ulp_distance, log, run_gpu, to_device
+from tests import gpu_helpers as H
 
 pytestmark = pytest.mark.gpu
 
@@ -198,8 +199,8 @@ def test_invalid_table_entry_is_skipped_and_flagged():
     case = W.make_case(82, [100], block_size=16, poison=False)
     q, k, v, table, lens = to_device(case)
     table[0, 2] = case.num_pages + 5          # page 2 (tokens 32..47) is now invalid
-    ws = torch.zeros(P.workspace_bytes(P.make_params(q, k, v, table, 16, case.scale, max_seq_len=100), 0),
-                     dtype=torch.uint8, device="cuda")
+    ws = H.guarded(P.workspace_bytes(P.make_params(q, k, v, table, 16, case.scale, max_seq_len=100), 0),
+                   torch.uint8, fill=0)
     out = P.paged_decode_attention(q, k, v, table, lens, 16, case.scale, max_seq_len=100, workspace=ws)
     torch.cuda.synchronize()
     assert P.read_error_word(ws) & 1

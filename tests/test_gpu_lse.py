@@ -9,6 +9,7 @@ import pytest
 import oracle.paged_attention as O
 from paged_kv_cache_08_amd import workloads as W
 from tests.gpu_helpers import ATOL, assert_matches_oracle, bf16_tensor, kv_kwargs, log, oracle_kv, to_device
+from tests import gpu_helpers as H
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +38,7 @@ def decode_twice(case, **kw):
     import torch
     import paged_kv_cache_08_amd as P
     q, k, v, table, lens = to_device(case)
-    lse = torch.full(q.shape[:-1], float("nan"), dtype=torch.float32, device="cuda")
+    lse = H.guarded(q.shape[:-1], torch.float32, fill=float("nan"))
     args = (q, k, v, table, lens, case.block_size, case.scale)
     kw = dict(max_seq_len=case.max_seq_len, **kv_kwargs(case), **kw)
     out = P.paged_decode_attention(*args, lse=lse, **kw)
@@ -96,7 +97,7 @@ def test_varlen_lse():
     _, k, v, table, lens = to_device(case)
     q = bf16_tensor(q_packed)
     cu_t = torch.from_numpy(np.ascontiguousarray(cu, dtype=np.int32)).cuda()
-    lse = torch.full(q.shape[:-1], float("nan"), dtype=torch.float32, device="cuda")
+    lse = H.guarded(q.shape[:-1], torch.float32, fill=float("nan"))
     out = P.paged_varlen_attention(q, k, v, table, lens, cu_t, case.block_size, case.scale, max_q_len=5,
                                    max_seq_len=case.max_seq_len, lse=lse)
     torch.cuda.synchronize()
@@ -119,7 +120,7 @@ def test_prefill_lse(rows, lens, window):
     _, k, v, table, lens_t = to_device(case)
     q = bf16_tensor(q_packed)
     cu_t = torch.from_numpy(np.ascontiguousarray(cu, dtype=np.int32)).cuda()
-    lse = torch.full(q.shape[:-1], float("nan"), dtype=torch.float32, device="cuda")
+    lse = H.guarded(q.shape[:-1], torch.float32, fill=float("nan"))
     P.paged_prefill_attention(q, k, v, table, lens_t, cu_t, case.block_size, case.scale, max_q_len=max(rows),
                               max_seq_len=case.max_seq_len, window=window, lse=lse)
     torch.cuda.synchronize()

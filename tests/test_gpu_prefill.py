@@ -6,6 +6,7 @@ import pytest
 
 import oracle.paged_attention as O
 from paged_kv_cache_08_amd import workloads as W
+from tests import gpu_helpers as H
 from tests.gpu_helpers import (assert_matches_oracle, bf16_tensor, kv_kwargs, log, oracle_kv, ref_without_tokens,
                                run_gpu_varlen, to_device)
 
@@ -21,7 +22,7 @@ def run_prefill(case, q_packed, cu, *, workspace=None, out=None, max_q_len=None,
     cu_t = torch.from_numpy(np.ascontiguousarray(cu, dtype=np.int32)).cuda()
     mq = max_q_len if max_q_len is not None else max(int(np.diff(cu).max(initial=1)), 1)
     if workspace is None:
-        workspace = torch.zeros(P.binding.PKV_PREFILL_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+        workspace = H.guarded(P.binding.PKV_PREFILL_WORKSPACE_BYTES, torch.uint8, fill=0)
     got = P.paged_prefill_attention(q, k, v, table, lens, cu_t, case.block_size, case.scale, max_q_len=mq,
                                     max_seq_len=case.max_seq_len, workspace=workspace, out=out,
                                     **kv_kwargs(case), **kw)
@@ -151,7 +152,7 @@ def test_invalid_table_entry_is_skipped_and_flagged():
     q, cu = W.pack_varlen(case, [120])
     _, k, v, table, lens = to_device(case)
     table[0, 8] = case.num_pages + 3
-    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    ws = H.guarded(256, torch.uint8, fill=0)
     got = P.paged_prefill_attention(bf16_tensor(q), k, v, table, lens,
                                     torch.from_numpy(cu).cuda(), 16, case.scale, max_q_len=120, max_seq_len=200,
                                     workspace=ws)
@@ -174,7 +175,7 @@ def test_inconsistent_rows_are_flagged_and_skipped():
     log("case: prefill rows [25, 40, 10] with max_q_len 30")
     case = W.make_case(1126, [900, 700, 1300], q_len=40, block_size=784, interleave=True)
     q, cu = W.pack_varlen(case, [25, 40, 10])
-    out = torch.full((q.shape[0], q.shape[1], q.shape[2]), 7.0, device="cuda")
+    out = H.guarded((q.shape[0], q.shape[1], q.shape[2]), torch.float32, fill=7.0)
     got, ws = run_prefill(case, q, cu, max_q_len=30, out=out)
     assert P.read_error_word(ws) & 2
     ref = oracle_prefill(case, q, cu)

@@ -9,6 +9,7 @@ import pytest
 import oracle.paged_attention as O
 from paged_kv_cache_08_amd import workloads as W
 from tests.gpu_helpers import assert_matches_oracle, log, ref_without_tokens, run_gpu, run_gpu_varlen
+from tests import gpu_helpers as H
 
 pytestmark = pytest.mark.gpu
 
@@ -78,7 +79,7 @@ def test_inconsistent_row_counts_are_flagged_and_skipped():
     log("case: varlen with one sequence above max_q_len")
     case = W.make_case(978, [900, 700, 1300], q_len=16, block_size=784, interleave=True)
     q, cu = W.pack_varlen(case, [3, 5, 2])
-    full = torch.full((q.shape[0] + 4, q.shape[1], q.shape[2]), 7.0, device="cuda")
+    full = H.guarded((q.shape[0] + 4, q.shape[1], q.shape[2]), torch.float32, fill=7.0)
     got, ws = run_gpu_varlen(case, q, cu, max_q_len=4, out=full[:q.shape[0]])
     ref = oracle_varlen(case, q, cu)
     assert P.read_error_word(ws) & 2

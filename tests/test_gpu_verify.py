@@ -6,6 +6,7 @@ import pytest
 import oracle.paged_attention as O
 from paged_kv_cache_08_amd import workloads as W
 from tests.gpu_helpers import assert_matches_oracle, log, ref_without_tokens, run_gpu, to_device
+from tests import gpu_helpers as H
 
 pytestmark = pytest.mark.gpu
 
@@ -115,7 +116,7 @@ def test_invalid_table_entry_is_skipped_and_flagged(splits):
     q, k, v, table, lens = to_device(case)
     table[0, 8] = case.num_pages + 3
     p = P.make_params(q, k, v, table, 16, case.scale, max_seq_len=200, num_splits=splits)
-    ws = torch.zeros(P.workspace_bytes(p, 0), dtype=torch.uint8, device="cuda")
+    ws = H.guarded(P.workspace_bytes(p, 0), torch.uint8, fill=0)
     out = P.paged_decode_attention(q, k, v, table, lens, 16, case.scale, max_seq_len=200, num_splits=splits,
                                    workspace=ws)
     torch.cuda.synchronize()

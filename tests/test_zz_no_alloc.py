@@ -8,6 +8,7 @@ import pytest
 import oracle.paged_attention as O
 from paged_kv_cache_08_amd import workloads as W
 from tests.gpu_helpers import assert_matches_oracle, log, to_device
+from tests import gpu_helpers as H
 
 pytestmark = pytest.mark.gpu
 
@@ -26,8 +27,8 @@ def _both(case, **kw):
                                    max_seq_len=case.max_seq_len, **kw)
     torch.cuda.synchronize()
     v_ws = P.last_variant()
-    out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
-    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = H.guarded(q.shape, torch.float32, fill=float("nan"))
+    err = H.guarded(1, torch.int32, fill=0)
     P.paged_decode_attention_noalloc(q, k, v, table, lens, case.block_size, case.scale,
                                      max_seq_len=case.max_seq_len, out=out, error_word=err, **kw)
     torch.cuda.synchronize()
@@ -68,7 +69,7 @@ def test_noalloc_twice_in_a_row_second_smaller():
     for case in (big, small):
         log(f"case: no-alloc call, lengths {case.seq_lens.tolist()}")
         q, k, v, table, lens = to_device(case)
-        out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+        out = H.guarded(q.shape, torch.float32)
         P.paged_decode_attention_noalloc(q, k, v, table, lens, case.block_size, case.scale,
                                          max_seq_len=case.max_seq_len, out=out)
         outs.append((case, out))
@@ -88,7 +89,7 @@ def test_noalloc_rejects_calls_beyond_its_scratch():
     k = torch.zeros((1, 784, 4, 256), dtype=torch.bfloat16, device="cuda")
     table = torch.zeros((1, 84), dtype=torch.int32, device="cuda")
     lens = torch.full((1,), 65536, dtype=torch.int32, device="cuda")
-    out = torch.full(q.shape, 5.0, dtype=torch.float32, device="cuda")
+    out = H.guarded(q.shape, torch.float32, fill=5.0)
     p = P.make_params(q, k, k, table, 784, 0.0625, max_seq_len=65536)
     assert P.workspace_bytes(p, 0) > P.binding.PKV_NOALLOC_SCRATCH_BYTES
     with pytest.raises(RuntimeError, match="scratch"):
@@ -104,8 +105,8 @@ def test_noalloc_reports_errors_in_the_callers_word():
     case = W.make_case(307, [100], block_size=16, poison=False)
     q, k, v, table, lens = to_device(case)
     table[0, 2] = case.num_pages + 5
-    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
-    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = H.guarded(q.shape, torch.float32)
+    err = H.guarded(1, torch.int32, fill=0)
     P.paged_decode_attention_noalloc(q, k, v, table, lens, 16, case.scale, max_seq_len=100, out=out,
                                      error_word=err)
     torch.cuda.synchronize()
