@@ -559,8 +559,15 @@ int pkv_debug_token_splits(const pkv_decode_params* p, const int32_t* seq_lens, 
 int64_t pkv_magic_div_check(int32_t divisor, int64_t n_max) {
   if (divisor < 1 || n_max < 0 || n_max > 0xffffffffLL) return -2;
   const pkv::MagicDiv md = pkv::make_magic(uint32_t(divisor));
+  // The reference quotient and remainder are carried along n (no division
+  // per step), so whole ranges of 2^30 numbers take about a second.
+  uint32_t q = 0, r = 0;
   for (int64_t n = 0; n <= n_max; ++n) {
-    if (pkv::magic_div(uint32_t(n), md) != uint32_t(n / divisor)) return n;
+    if (pkv::magic_div(uint32_t(n), md) != q) return n;
+    if (++r == uint32_t(divisor)) {
+      r = 0;
+      ++q;
+    }
   }
   return -1;
 }

@@ -196,8 +196,19 @@ def test_invariant_divisor_division_token_range(d):
 
 
 def test_invariant_divisor_division_all_divisors_to_1024():
-    for d in range(1, 1025):
-        assert P.magic_div_check(d, 1 << 16) == -1, d
+    # every token index below 2^24 for every page size up to 1024 (the checks
+    # run in C and release the GIL, so threads share the 1024 divisors)
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        bad = [d for d, r in zip(range(1, 1025), ex.map(lambda d: P.magic_div_check(d, (1 << 24) - 1),
+                                                           range(1, 1025))) if r != -1]
+    assert bad == []
+
+
+@pytest.mark.parametrize("d", [16, 784, 832])
+def test_invariant_divisor_division_to_2_30(d):
+    # the whole range of token indices the host accepts (max_seq_len <= 2^30)
+    assert P.magic_div_check(d, 1 << 30) == -1
 
 
 def test_bad_divisor_is_rejected():
