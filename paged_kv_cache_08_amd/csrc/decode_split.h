@@ -437,9 +437,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   }
   __syncthreads();
 
+  // One thread per 4 consecutive outputs (G * D / 4 <= kThreads threads):
+  // vector LDS reads and one 16-byte store each, every load issued up front.
   const int64_t prow0 = int64_t(b) * a.q_len * a.hq + int64_t(g) * G;   // partial row of head 0, query row 0
-  for (int i = tid; i < G * D; i += kThreads) {
-    const int h = i / D, d = i - h * D;
+  static_assert(G * D / 4 <= kThreads, "one thread per 4 outputs");
+  if (tid < G * D / 4) {
+    const int h = (4 * tid) / D, d = 4 * tid - h * D;
     float mw[kWaves], lw[kWaves];
 #pragma unroll
     for (int w = 0; w < kWaves; w += 4) {
@@ -454,25 +457,31 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
       lw[w + 2] = y.z;
       lw[w + 3] = y.w;
     }
+    float4 acc4[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) acc4[w] = *reinterpret_cast<const float4*>(&mrg_acc[w][h][d]);
     float M = mw[0];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mw[w]);
-    float num = 0.0f, den = 0.0f;
+    float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float den = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float f = fast_exp2(mw[w] - M);
-      num = fmaf(f, mrg_acc[w][h][d], num);
+      num.x = fmaf(f, acc4[w].x, num.x);
+      num.y = fmaf(f, acc4[w].y, num.y);
+      num.z = fmaf(f, acc4[w].z, num.z);
+      num.w = fmaf(f, acc4[w].w, num.w);
       den = fmaf(f, lw[w], den);
     }
     if (sp.nsplit == 1) {
-      store_out(a, out_row0 + i, den > 0.0f ? num / den : 0.0f);
+      const float4 o = den > 0.0f ? make_float4(num.x / den, num.y / den, num.z / den, num.w / den)
+                                  : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      store_out4(a, out_row0 + 4 * tid, o);
     } else {
       const int64_t pr = (prow0 + h) * a.num_splits + s;
-      a.part_acc[pr * D + d] = num;
-      if (d == 0) {
-        a.part_ml[pr * 2] = M;
-        a.part_ml[pr * 2 + 1] = den;
-      }
+      *reinterpret_cast<float4*>(a.part_acc + pr * D + d) = num;
+      if (d == 0) *reinterpret_cast<float2*>(a.part_ml + pr * 2) = make_float2(M, den);
     }
   }
   // A single-split sequence's optional log-sum-exp, one thread per head, from

@@ -91,6 +91,22 @@ __device__ __forceinline__ void store_out(const DecodeArgs& a, int64_t idx, floa
     static_cast<float*>(a.out)[idx] = x;
 }
 
+// Four consecutive outputs from element idx (a multiple of 4): one 16-byte
+// store, or 8 bytes of bf16.
+__device__ __forceinline__ void store_out4(const DecodeArgs& a, int64_t idx, float4 x) {
+  x.x *= a.out_scale;
+  x.y *= a.out_scale;
+  x.z *= a.out_scale;
+  x.w *= a.out_scale;
+  if (a.out_bf16) {
+    const uint2 v = make_uint2(uint32_t(f32_to_bf16_rne(x.x)) | (uint32_t(f32_to_bf16_rne(x.y)) << 16),
+                               uint32_t(f32_to_bf16_rne(x.z)) | (uint32_t(f32_to_bf16_rne(x.w)) << 16));
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + idx) = v;
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(a.out) + idx) = x;
+  }
+}
+
 // Optional log-sum-exp output of output row `row` (= query row * hq + head):
 // ln sum_j e^(score_j) from the row's (m, l) in log2 units, l = sum_j
 // 2^(score_j * log2(e) - m): (m + log2 l) * ln 2; -inf for a row that saw no
