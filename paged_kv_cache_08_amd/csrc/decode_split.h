@@ -1,9 +1,10 @@
 // The single-query split kernel for gfx950 (wave64, CDNA4), templated on
-// head_dim D, group size G (query heads per KV head) and window NS (sub-steps
-// of 32 tokens; a split holds at most NS * 32 tokens) and the cache type
-// (bf16 or FP8 E4M3). Each window size and cache type is instantiated in its
-// own source file (decode_w64.hip .. decode_w512_fp8.hip) so the fully
-// unrolled kernels compile in parallel.
+// head_dim D, group size G (query heads per KV head), window NBLK (strided
+// blocks of 32 tokens; a split holds at most NBLK * 32 tokens), the cache
+// type (bf16 or FP8 E4M3) and the waves per workgroup (8, or 4 for grids of
+// several workgroups per CU). Each window size and cache type is
+// instantiated in its own source file (decode_w64.hip .. decode_w512_fp8.hip,
+// decode_w512_many.hip) so the fully unrolled kernels compile in parallel.
 //
 // What is computed follows "DCU page832 attention" (luanjiahao.me): §1 and §5
 // for the address of a token row (logical page = t / B, offset = t % B,
@@ -19,9 +20,10 @@
 //     so the n workgroups of a (sequence, KV head) stream neighbouring blocks
 //     at the same time. (Bare reads of the same bytes finish about 3% sooner
 //     when the whole chip streams one band than with n bands far apart.)
-//   * 8 waves (2 per SIMD) x 4 token rows per wave: one block of 32
-//     consecutive logical tokens per sub-step, one token row per 16-lane DPP
-//     row. Each lane owns D/16 head-dim elements of its row and loads them
+//   * W waves x 4 token rows per wave (W = 8: 2 waves per SIMD and one
+//     workgroup per CU; W = 4: several workgroups per CU): 4 * W consecutive
+//     logical tokens of one strided block per sub-step, one token row per
+//     16-lane DPP row. Each lane owns D/16 head-dim elements of its row and loads them
 //     with 16-byte global loads (a 512-byte K row of D = 256 is read by 16
 //     lanes in two fully used 256-byte segments). The G query heads of the group all use the row held
 //     in registers, so K and V are fetched once per group. The K/V loads are
@@ -37,7 +39,8 @@
 //   * V pass: with the exact maximum of the lane's own window scores, each
 //     probability is computed once per (token, head), broadcast to the row with
 //     DPP row_newbcast, and accumulated with fp32 FMAs.
-//   * Token offsets: one thread per window slot divides its token index by
+//   * Token offsets: one thread per window slot (two slots per thread in
+//     4-wave workgroups) divides its token index by
 //     the page size (multiply-high), reads the block-table entry and stores
 //     the token's K and V row offsets in LDS, once per split (without a
 //     sliding window, while seq_lens is still in flight, for the stride of a
@@ -46,7 +49,7 @@
 //     row, instead of every lane of a row repeating the division and the
 //     table lookup.
 //   * Epilogue: the 4 token rows of a wave are merged by a reduce-scatter over
-//     lane swaps (v_permlane32_swap, v_permlane16_swap); the 8 waves publish
+//     lane swaps (v_permlane32_swap, v_permlane16_swap); the W waves publish
 //     their sums with their reference max in LDS and, after one barrier, are
 //     rescaled to the workgroup max and added in a fixed order; the split's
 //     (max, sum, accumulator) go to the workspace, or the normalised output
@@ -66,23 +69,29 @@ namespace pkv {
 namespace {
 
 
-constexpr int kWaves = 8;                      // 2 waves per SIMD
-constexpr int kThreads = 64 * kWaves;
+// Workgroup shapes. A split workgroup has W waves of 4 token rows (16 lanes
+// per row); a sub-step reads 4 * W consecutive tokens of one strided block.
+//   * W = 8 (2 waves per SIMD, one workgroup per CU): grids of at most one
+//     workgroup per CU (a batch-1 decode step).
+//   * W = 4 (one wave per SIMD, several workgroups per CU): bf16 grids of
+//     more workgroups than the device has CUs. Measured on a 16-sequence mixed
+//     batch 81.6 -> 74.4 us and on the 32 / 8-head dense control 29.1 ->
+//     27.0 us against 8-wave workgroups; the batch-1 32K step is faster with
+//     8 waves (28.8 against 29.4 us with 4 waves and a ring of 8).
+constexpr int kMaxWaves = 8;
+constexpr int kMaxThreads = 64 * kMaxWaves;
 constexpr int kLanesPerRow = 16;
 constexpr int kRowsPerWave = 64 / kLanesPerRow;
-constexpr int kStep = kWaves * kRowsPerWave;   // tokens per workgroup sub-step
-static_assert(kStep == kBlockTokens, "a sub-step reads one strided block of the split");
+static_assert(kBlockTokens % (4 * kRowsPerWave) == 0, "sub-steps tile a strided block");
 // Register ring depth (steps in flight + 1); shallower where G * D leaves
 // fewer registers. Measured at G = 6, D = 256 with non-temporal loads:
 // bf16 depth 4 / 6 / 8 gave 29.85 / 29.61 / 29.93 us on a 32K step; the FP8
 // rows are half as long and depth 4 is about 1% faster than 6 there.
 constexpr int ring_depth(int D, int G, bool fp8) { return (D == 256 && G >= 7) ? 3 : fp8 ? 4 : 6; }
-// The shallow variant (at most 4) serves grids of several waves of
-// workgroups: on a 16-sequence mixed batch depth 4 measured 82.3 against
-// 83.3 us at depth 6, on the single-wave 32K step 29.85 against 29.61 us.
-constexpr int ring_depth(int D, int G, bool fp8, bool shallow) {
-  return shallow && ring_depth(D, G, fp8) > 4 ? 4 : ring_depth(D, G, fp8);
-}
+// The 4-wave workgroups (several per CU) keep 3: on the mixed batch depth 3,
+// 4 and 6 gave 74.4, 74.4 and 75.8 us, on the dense control 27.0, 27.4 and
+// 28.2 us.
+constexpr int ring_depth(int D, int G, bool fp8, int waves) { return waves == 4 ? 3 : ring_depth(D, G, fp8); }
 constexpr float kMinit = -1.0e30f;             // floor of a row's max (finite: no inf - inf)
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -156,18 +165,23 @@ __device__ __forceinline__ int elem_d(int col, int e) {
   return FP8 ? col * kEpl + e : (e / 8) * 128 + col * 8 + (e % 8);
 }
 
-template <int D, int G, int kSubSteps, bool FP8, bool SHALLOW>
-__global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a) {
+template <int D, int G, int NBLK, bool FP8, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void decode_split_kernel(DecodeArgs a) {
+  constexpr int kWaves = WAVES;
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int kStep = kWaves * kRowsPerWave;          // tokens per workgroup sub-step
+  constexpr int kSubSteps = NBLK * (kBlockTokens / kStep);
   constexpr int kEpl = D / kLanesPerRow;   // head-dim elements per lane: 16 or 8
   constexpr int kCq = kEpl / 8;            // 16-byte pieces of q per lane: 2 or 1
   constexpr int kCpl = FP8 ? 1 : kCq;      // 16-byte K/V loads per lane and row (FP8 at D = 128: 8 bytes)
   constexpr int kSteps = 2 * kSubSteps;    // K pass, then V pass
-  constexpr int kRing = ring_depth(D, G, FP8, SHALLOW);
+  constexpr int kRing = ring_depth(D, G, FP8, kWaves);
   constexpr int kWin = kSubSteps * kStep;  // tokens of the window
   constexpr int kEsz = FP8 ? 1 : 2;        // bytes per cache element
   static_assert(kCpl >= 1 && kEpl % 8 == 0, "head_dim must be a multiple of 128");
   static_assert(G <= 8, "at most 8 query heads per KV head");
-  static_assert(kSubSteps >= 1 && kWin <= kMaxChunk && kWin <= kThreads, "window of at most kMaxChunk tokens");
+  static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves");
+  static_assert(kSubSteps >= 1 && kWin <= kMaxChunk, "window of at most kMaxChunk tokens");
 
   __shared__ int64_t tok_k[kWin];   // element offset of each window token's K row (a masked token: the q row)
   __shared__ int64_t tok_v[kWin];
@@ -199,10 +213,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   // the mapped range, so the load needs no branch); a sequence with fewer
   // splits, or a window, fetches it again once the length is known.
   const int L_in = a.seq_lens[b];
-  int e_tok = -1;
-  if (a.window == 0) {
-    const int t = min(strided_token(0, a.num_splits, s, min(tid, kWin - 1)), planned_cap(a) - 1);
-    e_tok = table_entry(a, b, t);
+  constexpr int kPer = (kWin + kThreads - 1) / kThreads;   // window slots per thread
+  int e_tok[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    e_tok[r] = -1;
+    if (a.window == 0) {
+      const int t = min(strided_token(0, a.num_splits, s, min(tid + r * kThreads, kWin - 1)), planned_cap(a) - 1);
+      e_tok[r] = table_entry(a, b, t);
+    }
   }
 
   const SplitSpan sp = split_span_len(a, L_in, s, 1);
@@ -214,17 +233,23 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
     }
     return;
   }
-  const int t_tok = strided_token(sp.lo, sp.nsplit, s, min(tid, kWin - 1));
-  const bool live = tid < kWin && t_tok < sp.L;
-  if ((a.window > 0 || sp.nsplit != a.num_splits) && live) e_tok = table_entry(a, b, t_tok);
-  int64_t ko = kmask, vo = vmask;
-  const bool entry_ok = token_row_entry(a, e_tok, g, t_tok, ko, vo);
-  if (tid < kWin) {
-    const bool ok = live && entry_ok;
-    tok_k[tid] = ok ? ko : kmask;
-    tok_v[tid] = ok ? vo : vmask;
+  bool bad_entry = false;
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int slot = tid + r * kThreads;
+    const int t_tok = strided_token(sp.lo, sp.nsplit, s, min(slot, kWin - 1));
+    const bool live = slot < kWin && t_tok < sp.L;
+    if ((a.window > 0 || sp.nsplit != a.num_splits) && live) e_tok[r] = table_entry(a, b, t_tok);
+    int64_t ko = kmask, vo = vmask;
+    const bool entry_ok = token_row_entry(a, e_tok[r], g, t_tok, ko, vo);
+    if (slot < kWin) {
+      const bool ok = live && entry_ok;
+      tok_k[slot] = ok ? ko : kmask;
+      tok_v[slot] = ok ? vo : vmask;
+    }
+    bad_entry |= live && !entry_ok;
   }
-  if (a.err && __any(live && !entry_ok) && lane == 0) atomicOr(a.err, 1u);
+  if (a.err && __any(bad_entry) && lane == 0) atomicOr(a.err, 1u);
   __syncthreads();
   // q is loaded only now, with the first K rows (it is needed no earlier),
   // so the start-up above waits for nothing but the sequence length and the
@@ -241,7 +266,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   // (one strided block each); row `row` of wave `wave` owns window slots
   // j * kStep + my.
   const int my = wave * kRowsPerWave + row;
-  const int n_sub = strided_blocks(sp, s);   // uniform, <= kSubSteps
+  const int n_sub = strided_blocks(sp, s) * (kBlockTokens / kStep);   // uniform, <= kSubSteps
 
   float acc[G][kEpl];
 #pragma unroll
@@ -437,12 +462,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   }
   __syncthreads();
 
-  // One thread per 4 consecutive outputs (G * D / 4 <= kThreads threads):
-  // vector LDS reads and one 16-byte store each, every load issued up front.
+  // One thread per 4 consecutive outputs: vector LDS reads and one 16-byte
+  // store each, every load issued up front.
   const int64_t prow0 = int64_t(b) * a.q_len * a.hq + int64_t(g) * G;   // partial row of head 0, query row 0
-  static_assert(G * D / 4 <= kThreads, "one thread per 4 outputs");
-  if (tid < G * D / 4) {
-    const int h = (4 * tid) / D, d = 4 * tid - h * D;
+  for (int i4 = tid; i4 < G * D / 4; i4 += kThreads) {
+    const int h = (4 * i4) / D, d = 4 * i4 - h * D;
     float mw[kWaves], lw[kWaves];
 #pragma unroll
     for (int w = 0; w < kWaves; w += 4) {
@@ -477,7 +501,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
     if (sp.nsplit == 1) {
       const float4 o = den > 0.0f ? make_float4(num.x / den, num.y / den, num.z / den, num.w / den)
                                   : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      store_out4(a, out_row0 + 4 * tid, o);
+      store_out4(a, out_row0 + 4 * i4, o);
     } else {
       const int64_t pr = (prow0 + h) * a.num_splits + s;
       *reinterpret_cast<float4*>(a.part_acc + pr * D + d) = num;
@@ -498,41 +522,41 @@ __global__ __launch_bounds__(kThreads, 1) void decode_split_kernel(DecodeArgs a)
   }
 }
 
-template <int D, int G, int NS, bool FP8, bool SHALLOW>
+template <int D, int G, int NS, bool FP8, int WAVES>
 hipError_t launch_decode_k(const DecodeArgs& a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   dim3 grid(a.num_splits, a.hkv, a.num_seqs);
   if (e0 && e1)
-    hipExtLaunchKernelGGL((decode_split_kernel<D, G, NS, FP8, SHALLOW>), grid, dim3(kThreads), 0, st, e0, e1, 0,
+    hipExtLaunchKernelGGL((decode_split_kernel<D, G, NS, FP8, WAVES>), grid, dim3(64 * WAVES), 0, st, e0, e1, 0,
                           a);
   else
-    hipLaunchKernelGGL((decode_split_kernel<D, G, NS, FP8, SHALLOW>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, G, NS, FP8, WAVES>), grid, dim3(64 * WAVES), 0, st, a);
   return hipGetLastError();
 }
 
-template <int D, int NS, bool FP8, bool SHALLOW>
+template <int D, int NS, bool FP8, int WAVES>
 hipError_t launch_decode_d(const DecodeArgs& a, int group, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   switch (group) {
-    case 1: return launch_decode_k<D, 1, NS, FP8, SHALLOW>(a, st, e0, e1);
-    case 2: return launch_decode_k<D, 2, NS, FP8, SHALLOW>(a, st, e0, e1);
-    case 3: return launch_decode_k<D, 3, NS, FP8, SHALLOW>(a, st, e0, e1);
-    case 4: return launch_decode_k<D, 4, NS, FP8, SHALLOW>(a, st, e0, e1);
-    case 5: return launch_decode_k<D, 5, NS, FP8, SHALLOW>(a, st, e0, e1);
-    case 6: return launch_decode_k<D, 6, NS, FP8, SHALLOW>(a, st, e0, e1);
-    case 7: return launch_decode_k<D, 7, NS, FP8, SHALLOW>(a, st, e0, e1);
-    case 8: return launch_decode_k<D, 8, NS, FP8, SHALLOW>(a, st, e0, e1);
+    case 1: return launch_decode_k<D, 1, NS, FP8, WAVES>(a, st, e0, e1);
+    case 2: return launch_decode_k<D, 2, NS, FP8, WAVES>(a, st, e0, e1);
+    case 3: return launch_decode_k<D, 3, NS, FP8, WAVES>(a, st, e0, e1);
+    case 4: return launch_decode_k<D, 4, NS, FP8, WAVES>(a, st, e0, e1);
+    case 5: return launch_decode_k<D, 5, NS, FP8, WAVES>(a, st, e0, e1);
+    case 6: return launch_decode_k<D, 6, NS, FP8, WAVES>(a, st, e0, e1);
+    case 7: return launch_decode_k<D, 7, NS, FP8, WAVES>(a, st, e0, e1);
+    case 8: return launch_decode_k<D, 8, NS, FP8, WAVES>(a, st, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }
 
-// Launch the split kernel with a window of NS sub-steps (a.chunk <= NS * 32)
-// for bf16 (FP8 = false) or FP8 caches; SHALLOW selects the shallow register
-// ring (ring_depth()).
-template <int NS, bool FP8, bool SHALLOW = false>
+// Launch the split kernel with a window of NS strided blocks of 32 tokens
+// (a.chunk <= NS * 32) for bf16 (FP8 = false) or FP8 caches, with WAVES
+// waves per workgroup.
+template <int NS, bool FP8, int WAVES = 8>
 hipError_t launch_decode_window(const DecodeArgs& a, int head_dim, int group, hipStream_t st, hipEvent_t e0,
                                 hipEvent_t e1) {
-  if (a.chunk > NS * kStep || bool(a.kv_fp8) != FP8) return hipErrorInvalidValue;
-  if (head_dim == 256) return launch_decode_d<256, NS, FP8, SHALLOW>(a, group, st, e0, e1);
-  if (head_dim == 128) return launch_decode_d<128, NS, FP8, SHALLOW>(a, group, st, e0, e1);
+  if (a.chunk > NS * kBlockTokens || bool(a.kv_fp8) != FP8) return hipErrorInvalidValue;
+  if (head_dim == 256) return launch_decode_d<256, NS, FP8, WAVES>(a, group, st, e0, e1);
+  if (head_dim == 128) return launch_decode_d<128, NS, FP8, WAVES>(a, group, st, e0, e1);
   return hipErrorInvalidValue;
 }
 

@@ -86,8 +86,8 @@ struct DecodeArgs {
 int decode_window(int chunk);
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
                                hipEvent_t ev_start, hipEvent_t ev_stop);
-hipError_t launch_decode_split_w512_shallow(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
-                                            hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_decode_split_w512_many(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
+                                         hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_decode_split_w64(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
                                    hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_decode_split_w64_fp8(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
