@@ -269,16 +269,17 @@ int decode_window(int chunk) {
 
 hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int group, hipStream_t st, hipEvent_t e0,
                                hipEvent_t e1) {
-  const bool fp8 = a.kv_fp8 != 0;
+  // FP8 caches: q.k and p.v on MFMA (the VALU kernel would be bound by
+  // widening the codes). Measured per step on one MI355X against the VALU
+  // kernel: 32K 20.5 vs 23.0 us, 16K 14.4 vs 16.3 us, 4K 10.3 vs 11.0 us,
+  // 16-sequence mixed batch 48.3 vs 61.4 us.
+  if (a.kv_fp8) return launch_decode_mfma_fp8(a, head_dim, group, st, e0, e1);
   switch (decode_window(a.chunk)) {
-    case 64: return (fp8 ? launch_decode_split_w64_fp8 : launch_decode_split_w64)(a, head_dim, group, st, e0, e1);
-    case 128: return (fp8 ? launch_decode_split_w128_fp8 : launch_decode_split_w128)(a, head_dim, group, st, e0, e1);
-    case 256: return (fp8 ? launch_decode_split_w256_fp8 : launch_decode_split_w256)(a, head_dim, group, st, e0, e1);
+    case 64: return launch_decode_split_w64(a, head_dim, group, st, e0, e1);
+    case 128: return launch_decode_split_w128(a, head_dim, group, st, e0, e1);
+    case 256: return launch_decode_split_w256(a, head_dim, group, st, e0, e1);
     default:
-      // bf16 grids of several workgroups per CU run the 4-wave workgroups (FP8
-      // measured slower with them: mixed batch 61.4 -> 62.5 us, dense control
-      // 22.3 -> 24.3 us).
-      if (fp8) return launch_decode_split_w512_fp8(a, head_dim, group, st, e0, e1);
+      // Grids of several workgroups per CU run the 4-wave workgroups.
       return (a.many_wg ? launch_decode_split_w512_many : launch_decode_split_w512)(a, head_dim, group, st, e0, e1);
   }
 }

@@ -1,10 +1,11 @@
-// The single-query split kernel for gfx950 (wave64, CDNA4), templated on
-// head_dim D, group size G (query heads per KV head), window NBLK (strided
-// blocks of 32 tokens; a split holds at most NBLK * 32 tokens), the cache
-// type (bf16 or FP8 E4M3) and the waves per workgroup (8, or 4 for grids of
-// several workgroups per CU). Each window size and cache type is
-// instantiated in its own source file (decode_w64.hip .. decode_w512_fp8.hip,
-// decode_w512_many.hip) so the fully unrolled kernels compile in parallel.
+// The single-query split kernel for bf16 caches on gfx950 (wave64, CDNA4),
+// templated on head_dim D, group size G (query heads per KV head), window
+// NBLK (strided blocks of 32 tokens; a split holds at most NBLK * 32 tokens)
+// and the waves per workgroup (8, or 4 for grids of several workgroups per
+// CU). Each window size is instantiated in its own source file
+// (decode_w64.hip .. decode_w512.hip, decode_w512_many.hip) so the fully
+// unrolled kernels compile in parallel. FP8 caches run the MFMA kernel of
+// decode_mfma.h, which the code widening would otherwise make VALU-bound.
 //
 // What is computed follows "DCU page832 attention" (luanjiahao.me): §1 and §5
 // for the address of a token row (logical page = t / B, offset = t % B,
@@ -85,13 +86,12 @@ constexpr int kRowsPerWave = 64 / kLanesPerRow;
 static_assert(kBlockTokens % (4 * kRowsPerWave) == 0, "sub-steps tile a strided block");
 // Register ring depth (steps in flight + 1); shallower where G * D leaves
 // fewer registers. Measured at G = 6, D = 256 with non-temporal loads:
-// bf16 depth 4 / 6 / 8 gave 29.85 / 29.61 / 29.93 us on a 32K step; the FP8
-// rows are half as long and depth 4 is about 1% faster than 6 there.
-constexpr int ring_depth(int D, int G, bool fp8) { return (D == 256 && G >= 7) ? 3 : fp8 ? 4 : 6; }
+// depth 4 / 6 / 8 gave 29.85 / 29.61 / 29.93 us on a 32K step.
+constexpr int ring_depth(int D, int G) { return (D == 256 && G >= 7) ? 3 : 6; }
 // The 4-wave workgroups (several per CU) keep 3: on the mixed batch depth 3,
 // 4 and 6 gave 74.4, 74.4 and 75.8 us, on the dense control 27.0, 27.4 and
 // 28.2 us.
-constexpr int ring_depth(int D, int G, bool fp8, int waves) { return waves == 4 ? 3 : ring_depth(D, G, fp8); }
+constexpr int ring_depth(int D, int G, int waves) { return waves == 4 ? 3 : ring_depth(D, G); }
 constexpr float kMinit = -1.0e30f;             // floor of a row's max (finite: no inf - inf)
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -156,16 +156,11 @@ __device__ __forceinline__ float reduce_scatter16(const float (&x)[G], int col) 
   return w + dpp_move<0xB1>(w);            // quad_perm [1,0,3,2]
 }
 
-// Head-dim element of lane column col's e-th element. bf16 caches: two
-// 16-byte pieces per 512-byte row, lane col holds [k * 128 + col * 8, +8) of
-// piece k. FP8 caches: lane col holds the kEpl contiguous elements
-// [col * kEpl, +kEpl) (one 16-byte load at D = 256).
-template <bool FP8, int kEpl>
-__device__ __forceinline__ int elem_d(int col, int e) {
-  return FP8 ? col * kEpl + e : (e / 8) * 128 + col * 8 + (e % 8);
-}
+// Head-dim element of lane column col's e-th element: two 16-byte pieces per
+// 512-byte row (D = 256), lane col holds [k * 128 + col * 8, +8) of piece k.
+__device__ __forceinline__ int elem_d(int col, int e) { return (e / 8) * 128 + col * 8 + (e % 8); }
 
-template <int D, int G, int NBLK, bool FP8, int WAVES>
+template <int D, int G, int NBLK, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void decode_split_kernel(DecodeArgs a) {
   constexpr int kWaves = WAVES;
   constexpr int kThreads = 64 * kWaves;
@@ -173,11 +168,11 @@ __global__ __launch_bounds__(64 * WAVES) void decode_split_kernel(DecodeArgs a) 
   constexpr int kSubSteps = NBLK * (kBlockTokens / kStep);
   constexpr int kEpl = D / kLanesPerRow;   // head-dim elements per lane: 16 or 8
   constexpr int kCq = kEpl / 8;            // 16-byte pieces of q per lane: 2 or 1
-  constexpr int kCpl = FP8 ? 1 : kCq;      // 16-byte K/V loads per lane and row (FP8 at D = 128: 8 bytes)
+  constexpr int kCpl = kCq;                // 16-byte K/V loads per lane and row
   constexpr int kSteps = 2 * kSubSteps;    // K pass, then V pass
-  constexpr int kRing = ring_depth(D, G, FP8, kWaves);
+  constexpr int kRing = ring_depth(D, G, kWaves);
   constexpr int kWin = kSubSteps * kStep;  // tokens of the window
-  constexpr int kEsz = FP8 ? 1 : 2;        // bytes per cache element
+  constexpr int kEsz = 2;                  // bytes per cache element
   static_assert(kCpl >= 1 && kEpl % 8 == 0, "head_dim must be a multiple of 128");
   static_assert(G <= 8, "at most 8 query heads per KV head");
   static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves");
@@ -202,8 +197,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_split_kernel(DecodeArgs a) 
   const int64_t kmask = (qrow_addr - int64_t(reinterpret_cast<uintptr_t>(a.k))) / kEsz;
   const int64_t vmask = (qrow_addr - int64_t(reinterpret_cast<uintptr_t>(a.v))) / kEsz;
   // The lane's first element of any row, as a byte address relative to a row start.
-  const uint8_t* const kbase = reinterpret_cast<const uint8_t*>(a.k) + elem_d<FP8, kEpl>(col, 0) * kEsz;
-  const uint8_t* const vbase = reinterpret_cast<const uint8_t*>(a.v) + elem_d<FP8, kEpl>(col, 0) * kEsz;
+  const uint8_t* const kbase = reinterpret_cast<const uint8_t*>(a.k) + elem_d(col, 0) * kEsz;
+  const uint8_t* const vbase = reinterpret_cast<const uint8_t*>(a.v) + elem_d(col, 0) * kEsz;
 
   // One thread per window slot finds its token's K and V rows. The loads the
   // start-up waits on are issued together: the sequence length and the
@@ -260,7 +255,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_split_kernel(DecodeArgs a) 
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int k = 0; k < kCq; ++k)
-      qv[h][k] = *reinterpret_cast<const uint4*>(a.q + out_row0 + h * D + elem_d<FP8, kEpl>(col, 8 * k));
+      qv[h][k] = *reinterpret_cast<const uint4*>(a.q + out_row0 + h * D + elem_d(col, 8 * k));
 
   // The split is one window of at most kSubSteps sub-steps of kStep tokens
   // (one strided block each); row `row` of wave `wave` owns window slots
@@ -279,21 +274,11 @@ __global__ __launch_bounds__(64 * WAVES) void decode_split_kernel(DecodeArgs a) 
   float m_row = kMinit, l_row = 0.0f;
 
   uint4 ring[kRing][kCpl];
-  // One lane's piece of a K or V row: bf16 kCpl 16-byte loads; FP8 kEpl
-  // bytes. Every K/V byte is read once per call, so the loads are
-  // non-temporal (streaming cache policy).
+  // One lane's piece of a K or V row: kCpl 16-byte loads. Every K/V byte is
+  // read once per call, so the loads are non-temporal (streaming cache policy).
   auto load_row = [&](const uint8_t* p, uint4 (&buf)[kCpl]) {
-    if constexpr (FP8) {
-      if constexpr (kEpl == 16) {
-        buf[0] = load_stream16(p);
-      } else {
-        const u32x2_t h = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
-        buf[0] = make_uint4(h[0], h[1], 0u, 0u);
-      }
-    } else {
 #pragma unroll
-      for (int k = 0; k < kCpl; ++k) buf[k] = load_stream16(p + k * 256);
-    }
+    for (int k = 0; k < kCpl; ++k) buf[k] = load_stream16(p + k * 256);
   };
   // K step j: the token's K row (branch-free: a masked token reads the q row).
   auto fetch_k = [&](int j, uint4 (&buf)[kCpl]) {
@@ -306,43 +291,20 @@ __global__ __launch_bounds__(64 * WAVES) void decode_split_kernel(DecodeArgs a) 
   // q.k of the G heads; lanes 2h, 2h+1 keep head h's score.
   auto consume_k = [&](int j, const uint4 (&kk)[kCpl]) {
     float dq[G];
-    if constexpr (FP8) {
-      // Each 32-bit word holds 4 FP8 codes: two exact bf16 pairs, elements
-      // 4w .. 4w + 3 of the lane, i.e. q words 2w and 2w + 1.
-      constexpr int kWords = kEpl / 4;
-      const uint32_t w4[4] = {kk[0].x, kk[0].y, kk[0].z, kk[0].w};
-      uint32_t kb[2 * kWords];
 #pragma unroll
-      for (int w = 0; w < kWords; ++w) {
-        kb[2 * w] = fp8x2_to_bf16x2<false>(w4[w]);
-        kb[2 * w + 1] = fp8x2_to_bf16x2<true>(w4[w]);
+    for (int h = 0; h < G; ++h) {
+      float d0 = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kCpl; ++k) {
+        d0 = dot2_bf16(qv[h][k].x, kk[k].x, d0);
+        d0 = dot2_bf16(qv[h][k].y, kk[k].y, d0);
+        d0 = dot2_bf16(qv[h][k].z, kk[k].z, d0);
+        d0 = dot2_bf16(qv[h][k].w, kk[k].w, d0);
       }
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const uint32_t qw[8] = {qv[h][0].x, qv[h][0].y, qv[h][0].z, qv[h][0].w,
-                                qv[h][kCq - 1].x, qv[h][kCq - 1].y, qv[h][kCq - 1].z, qv[h][kCq - 1].w};
-        float d0 = 0.0f;
-#pragma unroll
-        for (int m = 0; m < 2 * kWords; ++m) d0 = dot2_bf16(qw[m], kb[m], d0);
-        dq[h] = d0;
-      }
-    } else {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float d0 = 0.0f;
-#pragma unroll
-        for (int k = 0; k < kCpl; ++k) {
-          d0 = dot2_bf16(qv[h][k].x, kk[k].x, d0);
-          d0 = dot2_bf16(qv[h][k].y, kk[k].y, d0);
-          d0 = dot2_bf16(qv[h][k].z, kk[k].z, d0);
-          d0 = dot2_bf16(qv[h][k].w, kk[k].w, d0);
-        }
-        dq[h] = d0;
-      }
+      dq[h] = d0;
     }
     // sc[j] is +inf (live) or -inf (masked): the minimum keeps the score of a
-    // live token and gives -inf for a masked one whatever its q-row score is
-    // (NaN included: FP8 codes read from the q row may decode to NaN).
+    // live token and gives -inf for a masked one whatever its q-row score is.
     sc[j] = fminf(sc[j], reduce_scatter16<G>(dq, col) * a.scale_log2);
   };
   // p of head (col / 2), broadcast to the row, V accumulation.
@@ -351,36 +313,17 @@ __global__ __launch_bounds__(64 * WAVES) void decode_split_kernel(DecodeArgs a) 
     l_row += pl;
     float p[G];
     head_bcast<G>(pl, p);
-    if constexpr (FP8) {
-      // A masked token read the q row's bytes, which may decode to NaN, and
-      // 0 * NaN is NaN: its codes are replaced by zeros. (A live token's
-      // score is finite.)
-      const bool ok = sc[j] != -INFINITY;
-      constexpr int kWords = kEpl / 4;
-      const uint32_t w4[4] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w};
 #pragma unroll
-      for (int w = 0; w < kWords; ++w) {
-        const uint32_t word = ok ? w4[w] : 0u;
-        const float2 lo = fp8x2_to_f32x2<false>(word), hi = fp8x2_to_f32x2<true>(word);
-        const float v4[4] = {lo.x, lo.y, hi.x, hi.y};
+    for (int k = 0; k < kCpl; ++k) {
+      const uint32_t w4[4] = {vv[k].x, vv[k].y, vv[k].z, vv[k].w};
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+      for (int w = 0; w < 4; ++w) {
+        const float v0 = bf16_lo(w4[w]), v1 = bf16_hi(w4[w]);
+        const int e = k * 8 + w * 2;
 #pragma unroll
-          for (int h = 0; h < G; ++h) acc[h][4 * w + c] = fmaf(p[h], v4[c], acc[h][4 * w + c]);
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < kCpl; ++k) {
-        const uint32_t w4[4] = {vv[k].x, vv[k].y, vv[k].z, vv[k].w};
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float v0 = bf16_lo(w4[w]), v1 = bf16_hi(w4[w]);
-          const int e = k * 8 + w * 2;
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            acc[h][e] = fmaf(p[h], v0, acc[h][e]);
-            acc[h][e + 1] = fmaf(p[h], v1, acc[h][e + 1]);
-          }
+        for (int h = 0; h < G; ++h) {
+          acc[h][e] = fmaf(p[h], v0, acc[h][e]);
+          acc[h][e + 1] = fmaf(p[h], v1, acc[h][e + 1]);
         }
       }
     }
@@ -443,7 +386,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_split_kernel(DecodeArgs a) 
   // probabilities; one barrier; the final pass rescales each wave to the
   // workgroup max while it adds the waves (fixed order).
   {
-    const int d0 = elem_d<FP8, kEpl>(col, row * kE4);     // kE4 contiguous elements
+    const int d0 = elem_d(col, row * kE4);     // kE4 contiguous elements
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float* dst = &mrg_acc[wave][h][d0];
@@ -522,41 +465,40 @@ __global__ __launch_bounds__(64 * WAVES) void decode_split_kernel(DecodeArgs a) 
   }
 }
 
-template <int D, int G, int NS, bool FP8, int WAVES>
+template <int D, int G, int NS, int WAVES>
 hipError_t launch_decode_k(const DecodeArgs& a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   dim3 grid(a.num_splits, a.hkv, a.num_seqs);
   if (e0 && e1)
-    hipExtLaunchKernelGGL((decode_split_kernel<D, G, NS, FP8, WAVES>), grid, dim3(64 * WAVES), 0, st, e0, e1, 0,
+    hipExtLaunchKernelGGL((decode_split_kernel<D, G, NS, WAVES>), grid, dim3(64 * WAVES), 0, st, e0, e1, 0,
                           a);
   else
-    hipLaunchKernelGGL((decode_split_kernel<D, G, NS, FP8, WAVES>), grid, dim3(64 * WAVES), 0, st, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, G, NS, WAVES>), grid, dim3(64 * WAVES), 0, st, a);
   return hipGetLastError();
 }
 
-template <int D, int NS, bool FP8, int WAVES>
+template <int D, int NS, int WAVES>
 hipError_t launch_decode_d(const DecodeArgs& a, int group, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   switch (group) {
-    case 1: return launch_decode_k<D, 1, NS, FP8, WAVES>(a, st, e0, e1);
-    case 2: return launch_decode_k<D, 2, NS, FP8, WAVES>(a, st, e0, e1);
-    case 3: return launch_decode_k<D, 3, NS, FP8, WAVES>(a, st, e0, e1);
-    case 4: return launch_decode_k<D, 4, NS, FP8, WAVES>(a, st, e0, e1);
-    case 5: return launch_decode_k<D, 5, NS, FP8, WAVES>(a, st, e0, e1);
-    case 6: return launch_decode_k<D, 6, NS, FP8, WAVES>(a, st, e0, e1);
-    case 7: return launch_decode_k<D, 7, NS, FP8, WAVES>(a, st, e0, e1);
-    case 8: return launch_decode_k<D, 8, NS, FP8, WAVES>(a, st, e0, e1);
+    case 1: return launch_decode_k<D, 1, NS, WAVES>(a, st, e0, e1);
+    case 2: return launch_decode_k<D, 2, NS, WAVES>(a, st, e0, e1);
+    case 3: return launch_decode_k<D, 3, NS, WAVES>(a, st, e0, e1);
+    case 4: return launch_decode_k<D, 4, NS, WAVES>(a, st, e0, e1);
+    case 5: return launch_decode_k<D, 5, NS, WAVES>(a, st, e0, e1);
+    case 6: return launch_decode_k<D, 6, NS, WAVES>(a, st, e0, e1);
+    case 7: return launch_decode_k<D, 7, NS, WAVES>(a, st, e0, e1);
+    case 8: return launch_decode_k<D, 8, NS, WAVES>(a, st, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }
 
 // Launch the split kernel with a window of NS strided blocks of 32 tokens
-// (a.chunk <= NS * 32) for bf16 (FP8 = false) or FP8 caches, with WAVES
-// waves per workgroup.
-template <int NS, bool FP8, int WAVES = 8>
+// (a.chunk <= NS * 32) for bf16 caches, with WAVES waves per workgroup.
+template <int NS, int WAVES = 8>
 hipError_t launch_decode_window(const DecodeArgs& a, int head_dim, int group, hipStream_t st, hipEvent_t e0,
                                 hipEvent_t e1) {
-  if (a.chunk > NS * kBlockTokens || bool(a.kv_fp8) != FP8) return hipErrorInvalidValue;
-  if (head_dim == 256) return launch_decode_d<256, NS, FP8, WAVES>(a, group, st, e0, e1);
-  if (head_dim == 128) return launch_decode_d<128, NS, FP8, WAVES>(a, group, st, e0, e1);
+  if (a.chunk > NS * kBlockTokens || a.kv_fp8) return hipErrorInvalidValue;
+  if (head_dim == 256) return launch_decode_d<256, NS, WAVES>(a, group, st, e0, e1);
+  if (head_dim == 128) return launch_decode_d<128, NS, WAVES>(a, group, st, e0, e1);
   return hipErrorInvalidValue;
 }
 

@@ -5,7 +5,7 @@ namespace pkv {
 
 hipError_t launch_decode_split_w256(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
                                     hipEvent_t e0, hipEvent_t e1) {
-  return launch_decode_window<8, false>(a, head_dim, group, st, e0, e1);
+  return launch_decode_window<8>(a, head_dim, group, st, e0, e1);
 }
 
 }  // namespace pkv

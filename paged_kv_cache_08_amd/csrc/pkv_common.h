@@ -78,7 +78,8 @@ struct DecodeArgs {
   int32_t many_wg;          // the split grid holds more workgroups than the device has CUs
 };
 
-// Launchers (decode_kernels.hip, decode_w*.hip, verify_kernels.hip). Return
+// Launchers (decode_kernels.hip, decode_w*.hip, decode_mfma_fp8.hip,
+// verify_kernels.hip). Return
 // hipError_t. The split launchers take optional start/stop events, stamped at
 // the start and end of the kernel's execution (hipExtLaunchKernel) when both
 // are non-null. launch_decode_split picks the smallest window (64, 128, 256 or
@@ -90,20 +91,15 @@ hipError_t launch_decode_split_w512_many(const DecodeArgs& a, int head_dim, int 
                                          hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_decode_split_w64(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
                                    hipEvent_t ev_start, hipEvent_t ev_stop);
-hipError_t launch_decode_split_w64_fp8(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
-                                       hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_decode_split_w128(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
                                     hipEvent_t ev_start, hipEvent_t ev_stop);
-hipError_t launch_decode_split_w128_fp8(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
-                                        hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_decode_split_w256(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
                                     hipEvent_t ev_start, hipEvent_t ev_stop);
-hipError_t launch_decode_split_w256_fp8(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
-                                        hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_decode_split_w512(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
                                     hipEvent_t ev_start, hipEvent_t ev_stop);
-hipError_t launch_decode_split_w512_fp8(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
-                                        hipEvent_t ev_start, hipEvent_t ev_stop);
+// The single-query split kernel on MFMA for FP8 caches (decode_mfma_fp8.hip).
+hipError_t launch_decode_mfma_fp8(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
+                                  hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_verify_split(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
                                hipEvent_t ev_start, hipEvent_t ev_stop);
 // Prefill: blocks of a.pf_rows query positions per workgroup, each over its

@@ -62,7 +62,10 @@ DECODE_CASES = [
     ("window 2048", lambda: W.make_case(1205, [5000, 100], block_size=784, interleave=True, boost_frac=0.05),
      {"window": 2048}, ("decode_valu",)),
     ("FP8 K/V", lambda: W.make_case(1206, [3000, 17, 0], block_size=784, interleave=True, boost_frac=0.05,
-                                    kv_dtype="fp8_e4m3"), {}, ("decode_valu",)),
+                                    kv_dtype="fp8_e4m3"), {}, ("decode_mfma",)),
+    ("FP8 K/V, one split", lambda: W.make_case(1210, [300, 64, 0], block_size=16, interleave=True,
+                                               boost_frac=0.05, kv_dtype="fp8_e4m3"), {"num_splits": 1},
+     ("decode_mfma", "splits=1")),
     ("group 12 on MFMA", lambda: W.make_case(1207, [2500, 0, 33], num_q_heads=24, num_kv_heads=2, block_size=784,
                                              interleave=True, boost_frac=0.05), {}, ("verify_mfma",)),
     ("verify q16", lambda: W.make_case(1208, [3000, 20, 0], q_len=16, block_size=784, interleave=True,
