@@ -442,7 +442,8 @@ def measure(args, dev, hip, emit_cpu=True):
     parity = {"atol": PARITY_ATOL, "rtol": PARITY_RTOL, "rel_floor": PARITY_REL_FLOOR, "ok": False}
     try:
         if prefill:
-            sample = [0, 1, 2047, int(varlen[1][1]) - 1]
+            n_rows = int(varlen[1][1])
+            sample = sorted({0, 1, n_rows // 2 - 1, n_rows - 1} & set(range(n_rows)))
             g, ref = got[sample], oracle_rows(case, varlen, sample, args.window)
             parity["checked"] = f"rows {sample} of the chunk, every head and column"
         else:
@@ -475,7 +476,8 @@ def measure(args, dev, hip, emit_cpu=True):
             cpu = cpu_baseline(case, varlen, args.window, kv_bytes, args.cpu_seconds)
 
     kernel = ("verify_split_kernel (prefill blocks)" if prefill else
-              "verify_split_kernel" if (case.q_len > 1 or varlen is not None) else "decode_split_kernel")
+              "verify_split_kernel" if (case.q_len > 1 or varlen is not None) else
+              "decode_mfma_kernel" if args.kv_dtype == "fp8" else "decode_split_kernel")
     timing_src = ("HIP events that the library records on its stream right around the split kernel "
                   "(hipExtLaunchKernel), averaged over the K launches after the timed regions")
     if prefill:   # a dense contraction: priced against the bf16 MFMA peak

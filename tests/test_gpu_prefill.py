@@ -68,6 +68,18 @@ def test_chunk_4096_of_8192_prompt_sampled_rows():
     assert_matches_oracle(got[rows], oracle_rows(case, q, cu, 0, rows), "prefill 4096/8192 sampled")
 
 
+def test_chunk_1024_of_4096_every_row():
+    # A mid-size chunk compared in full: 1024 new rows on a 4096-token cache
+    # (24/4/256, page 784), every row, head and column against the oracle's
+    # whole varlen call (49 blocks of 21 positions, the last one ragged).
+    log("case: prefill chunk 1024 rows, context 4096, 24/4/256, page 784, every row")
+    case, q, cu = W.chunked_prefill(chunk=1024, context=4096)
+    got, ws = run_prefill(case, q, cu)
+    import paged_kv_cache_08_amd as P
+    assert P.read_error_word(ws) == 0
+    assert_matches_oracle(got, oracle_prefill(case, q, cu), "prefill 1024/4096 every row")
+
+
 @pytest.mark.parametrize("rows,lens,hq,hkv,d,bs", [
     ([200], [1000], 24, 4, 256, 784),                          # 21 positions per block, ragged last block
     ([37, 0, 130, 1, 21, 22], [37, 500, 900, 1, 21, 2100], 24, 4, 256, 16),   # whole prompts, empty, one row
