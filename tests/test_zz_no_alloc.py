@@ -7,7 +7,7 @@ import pytest
 
 import oracle.paged_attention as O
 from paged_kv_cache_08_amd import workloads as W
-from tests.gpu_helpers import assert_matches_oracle, log, to_device
+from tests.gpu_helpers import assert_matches_oracle, kv_kwargs, log, oracle_kv, to_device
 from tests import gpu_helpers as H
 
 pytestmark = pytest.mark.gpu
@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 
 def _oracle(case):
     return O.paged_attention_ref(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
-                                 case.block_size, case.scale)
+                                 case.block_size, case.scale, **oracle_kv(case))
 
 
 def _both(case, **kw):
@@ -23,6 +23,7 @@ def _both(case, **kw):
     import torch
     import paged_kv_cache_08_amd as P
     q, k, v, table, lens = to_device(case)
+    kw = dict(kw, **kv_kwargs(case))
     ref = P.paged_decode_attention(q, k, v, table, lens, case.block_size, case.scale,
                                    max_seq_len=case.max_seq_len, **kw)
     torch.cuda.synchronize()
@@ -40,7 +41,9 @@ def _both(case, **kw):
 # Consecutive calls of different shapes on the one scratch array: it keeps the
 # previous call's partials, which the next call must not read.
 SEQUENCE = [
-    ("L32768 B784 (merge in the split kernel)", lambda: W.hybrid_long_context(32768), {}),
+    ("L32768 B784 (split kernel, merge kernel)", lambda: W.hybrid_long_context(32768), {}),
+    ("L32768 B784 FP8 (MFMA split kernel, merge kernel)",
+     lambda: W.hybrid_long_context(32768, kv_dtype="fp8_e4m3"), {}),
     ("mixed batch (merge kernel)", lambda: W.mixed_batch(), "total"),
     ("L4096 B784", lambda: W.hybrid_long_context(4096), {}),
     ("verify q16 L4096 (MFMA kernel, merge kernel)", lambda: W.spec_verify(4096), {}),
