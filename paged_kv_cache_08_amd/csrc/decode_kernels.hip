@@ -141,6 +141,119 @@ __global__ __launch_bounds__(64 * MW) void lse_merge_kernel(DecodeArgs a) {
   }
 }
 
+// The same merge for head_dim 256 with whole rows per workgroup: workgroup =
+// (query head, query row x sequence), MW waves, lane l holds columns
+// 4l .. 4l + 3 and loads them with one 16-byte load per split, wave w sums
+// splits w, w + MW, .... A quarter of the workgroups and of the load
+// instructions of lse_merge_kernel for the same bytes (the grids of
+// multi-row calls read tens of MB of partials). Same rule and order of
+// additions per column as lse_merge_kernel.
+template <int MW, bool AHEAD>
+__global__ __launch_bounds__(64 * MW) void lse_merge_row_kernel(DecodeArgs a) {
+  constexpr int D = 256;
+  constexpr int kPerWave = 64 / MW;   // accumulator loads in flight per thread per pass
+  constexpr int kPass = MW * kPerWave;
+  __shared__ float sm_w[MW][kMergeSplitsLds];
+  __shared__ __attribute__((aligned(16))) float4 part[MW][64];
+  const int h = blockIdx.y;
+  const int i = blockIdx.x % a.q_len, b = blockIdx.x / a.q_len;
+  const QRows qr = seq_q_rows(a, b);
+  if (i >= qr.n) return;          // no such row in a varlen batch
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t prow = (int64_t(qr.base) + i) * a.hq + h;
+  const float* ml = a.part_ml + prow * a.num_splits * 2;
+  const float* ac = a.part_acc + prow * a.num_splits * D + 4 * lane;
+  float4 vals[kPerWave];
+  float2 ml0;
+  auto load_first = [&](int n) {
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j) {
+      const int sidx = wave + MW * j;
+      vals[j] = sidx < n ? *reinterpret_cast<const float4*>(ac + int64_t(sidx) * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    ml0 = lane < n ? reinterpret_cast<const float2*>(ml)[lane] : make_float2(0.0f, 0.0f);
+  };
+  if constexpr (AHEAD) load_first(a.num_splits);
+  const SplitSpan sp = split_span(a, b, 0, qr.n);
+  const int ns = sp.nsplit;      // <= 1: the split kernel wrote the output
+  if constexpr (!AHEAD) {
+    if (ns <= 1) return;
+    load_first(ns);
+  } else {
+    if (ns <= 1) return;
+  }
+  float mloc = lane < ns && ml0.y > 0.0f ? ml0.x : -INFINITY;
+  for (int t = lane + 64; t < ns; t += 64) {
+    const float2 v = reinterpret_cast<const float2*>(ml)[t];
+    mloc = fmaxf(mloc, v.y > 0.0f ? v.x : -INFINITY);
+  }
+  const float M = wave_max64(mloc);
+  float dloc = 0.0f;
+  for (int t = lane; t < ns; t += 64) {
+    const float2 v = t < 64 ? ml0 : reinterpret_cast<const float2*>(ml)[t];
+    const float f = v.y > 0.0f ? fast_exp2(v.x - M) : 0.0f;
+    dloc += f * v.y;
+    if (t < kMergeSplitsLds) sm_w[wave][t] = f;
+  }
+  const float den = wave_sum64(dloc);
+  const float inv_den = 1.0f / den;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  auto add = [&](float f, const float4& v) {
+    num.x += f * v.x;
+    num.y += f * v.y;
+    num.z += f * v.z;
+    num.w += f * v.w;
+  };
+#pragma unroll
+  for (int j = 0; j < kPerWave; ++j) {
+    const int sidx = wave + MW * j;
+    const float f = sidx < ns ? sm_w[wave][sidx] : 0.0f;
+    add(f, sidx < ns ? vals[j] : make_float4(0.f, 0.f, 0.f, 0.f));
+  }
+  for (int s0 = kPass; s0 < ns; s0 += kPass) {
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j) {
+      const int sidx = s0 + wave + MW * j;
+      vals[j] = sidx < ns ? *reinterpret_cast<const float4*>(ac + int64_t(sidx) * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < kPerWave; ++j) {
+      const int sidx = s0 + wave + MW * j;
+      if (sidx < ns) {
+        float f;
+        if (sidx < kMergeSplitsLds) {
+          f = sm_w[wave][sidx];
+        } else {
+          const float2 v = reinterpret_cast<const float2*>(ml)[sidx];
+          f = v.y > 0.0f ? fast_exp2(v.x - M) : 0.0f;
+        }
+        add(f, vals[j]);
+      }
+    }
+  }
+  part[wave][lane] = num;
+  __syncthreads();
+  if (wave == 0) {
+    float4 t = part[0][lane];
+#pragma unroll
+    for (int w = 1; w < MW; ++w) {
+      const float4 u = part[w][lane];
+      t.x += u.x;
+      t.y += u.y;
+      t.z += u.z;
+      t.w += u.w;
+    }
+    const float4 o = M == -INFINITY ? make_float4(0.f, 0.f, 0.f, 0.f)
+                                    : make_float4(t.x * inv_den, t.y * inv_den, t.z * inv_den, t.w * inv_den);
+    store_out4(a, prow * D + 4 * lane, o);
+    if (lane == 0) store_lse(a, prow, M, M == -INFINITY ? 0.0f : den);
+  }
+}
+
 // The merge for plans of at most kFewSplits splits (short contexts, batched
 // verify): workgroup = (query row slot, 4 query heads), one wave per head, each
 // lane D / 64 columns, so the grid is not 64-column blocks times heads times
@@ -298,6 +411,14 @@ hipError_t launch_lse_merge(const DecodeArgs& a, int head_dim, hipStream_t st) {
   dim3 grid(a.q_len * a.num_seqs, a.hq, head_dim / 64);
   const bool small = int64_t(a.q_len) * a.num_seqs * a.hq < 128;
   const bool one_seq = a.num_seqs == 1 && a.cu_q == nullptr;
+  if (head_dim == 256 && !small && a.q_len > 1) {
+    dim3 rgrid(a.q_len * a.num_seqs, a.hq);
+    if (one_seq)
+      hipLaunchKernelGGL((lse_merge_row_kernel<4, true>), rgrid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((lse_merge_row_kernel<4, false>), rgrid, dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   if (head_dim == 256) {
     if (small)
       hipLaunchKernelGGL((lse_merge_kernel<256, 8, true>), grid, dim3(512), 0, st, a);
