@@ -1,10 +1,10 @@
 // The single-query split kernel for bf16 caches on gfx950 (wave64, CDNA4),
 // templated on head_dim D, group size G (query heads per KV head), window
 // NBLK (strided blocks of 32 tokens; a split holds at most NBLK * 32 tokens)
-// and the waves per workgroup (8, or 4 for grids of several workgroups per
-// CU). Each window size is instantiated in its own source file
-// (decode_w64.hip .. decode_w512.hip, decode_w512_many.hip) so the fully
-// unrolled kernels compile in parallel. FP8 caches run the MFMA kernel of
+// and the waves per workgroup (8 for 512-token windows in grids of at most
+// one workgroup per CU, else 4). Each window size is instantiated in its own
+// source file (decode_w64.hip .. decode_w512.hip, decode_w512_many.hip) so the
+// fully unrolled kernels compile in parallel. FP8 caches run the MFMA kernel of
 // decode_mfma.h, which the code widening would otherwise make VALU-bound.
 //
 // What is computed follows "DCU page832 attention" (luanjiahao.me): §1 and §5
@@ -72,13 +72,15 @@ namespace {
 
 // Workgroup shapes. A split workgroup has W waves of 4 token rows (16 lanes
 // per row); a sub-step reads 4 * W consecutive tokens of one strided block.
-//   * W = 8 (2 waves per SIMD, one workgroup per CU): grids of at most one
-//     workgroup per CU (a batch-1 decode step).
-//   * W = 4 (one wave per SIMD, several workgroups per CU): bf16 grids of
-//     more workgroups than the device has CUs. Measured on a 16-sequence mixed
-//     batch 81.6 -> 74.4 us and on the 32 / 8-head dense control 29.1 ->
-//     27.0 us against 8-wave workgroups; the batch-1 32K step is faster with
-//     8 waves (28.8 against 29.4 us with 4 waves and a ring of 8).
+//   * W = 8 (2 waves per SIMD, one workgroup per CU): 512-token windows in
+//     grids of at most one workgroup per CU (the batch-1 32K step: 28.8 us
+//     against 29.4 us with 4 waves and a ring of 8).
+//   * W = 4 (one wave per SIMD, several workgroups per CU): 512-token windows
+//     in grids of more workgroups than the device has CUs (16-sequence mixed
+//     batch 81.6 -> 74.4 us, 32 / 8-head dense control 29.1 -> 27.0 us
+//     against 8 waves) and every shorter window (per step 1K 10.04 -> 9.68
+//     us, 4K 11.35 -> 10.98, 16K 18.68 -> 18.55, a 2048-token sliding
+//     window 10.38 -> 10.1).
 constexpr int kMaxWaves = 8;
 constexpr int kMaxThreads = 64 * kMaxWaves;
 constexpr int kLanesPerRow = 16;
