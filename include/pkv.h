@@ -273,7 +273,7 @@ int pkv_paged_prefill_attention(const pkv_decode_params* p,
 /* Which kernels the last successful attention call on this thread launched,
  * with the split plan, e.g. "decode_valu d256 g6 q1 w512 + lse_merge
  * splits=64 chunk=512 B=784" (for prefill, w is the query positions per
- * workgroup). Split kernels: decode_valu / decode_valu_4w (bf16, q_len 1),
+ * workgroup). Split kernels: decode_valu (bf16, q_len 1),
  * decode_mfma (FP8, q_len 1), verify_mfma / varlen_mfma (several rows),
  * prefill_mfma. It is this library's run-time marker of the path that ran:
  * "DCU page832 attention" §8 accepts a measurement only when the run's log

@@ -289,9 +289,7 @@ int launch_call(const pkv_decode_params* p, const void* q, const void* k_cache, 
   if (p->q_len == 1 && !cu_q && pkv::decode_supported(p->head_dim, group)) {
     e = pkv::launch_decode_split(a, p->head_dim, group, st, g_ev_start, g_ev_stop);
     // 4-wave workgroups for grids of several workgroups per CU (512-token window)
-    split_name = a.kv_fp8 ? "decode_mfma"
-                 : a.many_wg || pkv::decode_window(chunk) < 512 ? "decode_valu_4w"
-                                                                 : "decode_valu";
+    split_name = a.kv_fp8 ? "decode_mfma" : "decode_valu";
     window = pkv::decode_window(chunk);
   } else {
     e = pkv::launch_verify_split(a, p->head_dim, group, st, g_ev_start, g_ev_stop);

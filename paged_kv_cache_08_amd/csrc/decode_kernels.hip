@@ -319,7 +319,9 @@ __global__ __launch_bounds__(256) void lse_merge_few_kernel(DecodeArgs a) {
 // kernel) and token_row_direct() on the table row in global memory (the
 // single-query split kernel). A token on which they disagree gets -3, an
 // invalid page entry -2.
-__global__ __launch_bounds__(kMaxThreads) void debug_offsets_kernel(DecodeArgs a, int g, int max_seq_len,
+constexpr int kDebugThreads = 512;
+
+__global__ __launch_bounds__(kDebugThreads) void debug_offsets_kernel(DecodeArgs a, int g, int max_seq_len,
                                                                  int64_t* k_off, int64_t* v_off) {
   __shared__ PageOffs tbl[kMaxChunk + 2];
   const int s = blockIdx.x, b = blockIdx.y;
@@ -330,7 +332,7 @@ __global__ __launch_bounds__(kMaxThreads) void debug_offsets_kernel(DecodeArgs a
   stage_table(a, b, g, p_first, pages.n, tbl);
   __syncthreads();
   const int t_end = min(sp.end, max_seq_len);
-  for (int t = sp.begin + threadIdx.x; t < t_end; t += kMaxThreads) {
+  for (int t = sp.begin + threadIdx.x; t < t_end; t += kDebugThreads) {
     int64_t ko = 0, vo = 0, kd = 0, vd = 0;
     const bool ok = token_row(a, tbl, p_first, t, ko, vo);     // staged table (MFMA kernel)
     const bool okd = token_row_direct(a, b, g, t, kd, vd);     // table row in global memory (split kernel)
@@ -392,7 +394,7 @@ hipError_t launch_decode_split(const DecodeArgs& a, int head_dim, int group, hip
     case 128: return launch_decode_split_w128(a, head_dim, group, st, e0, e1);
     case 256: return launch_decode_split_w256(a, head_dim, group, st, e0, e1);
     default:
-      // Grids of several workgroups per CU run the 4-wave workgroups.
+      // Grids of several workgroups per CU run the shallower ring.
       return (a.many_wg ? launch_decode_split_w512_many : launch_decode_split_w512)(a, head_dim, group, st, e0, e1);
   }
 }
@@ -442,7 +444,7 @@ hipError_t launch_lse_merge(const DecodeArgs& a, int head_dim, hipStream_t st) {
 hipError_t launch_debug_offsets(const DecodeArgs& a, int kv_head, int max_seq_len, int64_t* k_off,
                                 int64_t* v_off, hipStream_t st) {
   dim3 grid(a.num_splits, a.num_seqs);
-  hipLaunchKernelGGL(debug_offsets_kernel, grid, dim3(kMaxThreads), 0, st, a, kv_head, max_seq_len, k_off, v_off);
+  hipLaunchKernelGGL(debug_offsets_kernel, grid, dim3(kDebugThreads), 0, st, a, kv_head, max_seq_len, k_off, v_off);
   return hipGetLastError();
 }
 

@@ -1,10 +1,10 @@
 // The single-query split kernel for bf16 caches on gfx950 (wave64, CDNA4),
 // templated on head_dim D, group size G (query heads per KV head), window
 // NBLK (strided blocks of 32 tokens; a split holds at most NBLK * 32 tokens)
-// and the waves per workgroup (8 for 512-token windows in grids of at most
-// one workgroup per CU, else 4). Each window size is instantiated in its own
-// source file (decode_w64.hip .. decode_w512.hip, decode_w512_many.hip) so the
-// fully unrolled kernels compile in parallel. FP8 caches run the MFMA kernel of
+// and its register ring depth. Each window size is instantiated in its own
+// source file (decode_w64.hip .. decode_w512.hip, and decode_w512_many.hip
+// with a shallower ring for grids of several workgroups per CU) so the fully
+// unrolled kernels compile in parallel. FP8 caches run the MFMA kernel of
 // decode_mfma.h, which the code widening would otherwise make VALU-bound.
 //
 // What is computed follows "DCU page832 attention" (luanjiahao.me): §1 and §5
@@ -21,10 +21,9 @@
 //     so the n workgroups of a (sequence, KV head) stream neighbouring blocks
 //     at the same time. (Bare reads of the same bytes finish about 3% sooner
 //     when the whole chip streams one band than with n bands far apart.)
-//   * W waves x 4 token rows per wave (W = 8: 2 waves per SIMD and one
-//     workgroup per CU; W = 4: several workgroups per CU): 4 * W consecutive
-//     logical tokens of one strided block per sub-step, one token row per
-//     16-lane DPP row. Each lane owns D/16 head-dim elements of its row and loads them
+//   * 4 waves (one per SIMD) x 4 token rows per wave: 16 consecutive logical
+//     tokens of one strided block per sub-step, one token row per 16-lane DPP
+//     row. Each lane owns D/16 head-dim elements of its row and loads them
 //     with 16-byte global loads (a 512-byte K row of D = 256 is read by 16
 //     lanes in two fully used 256-byte segments). The G query heads of the group all use the row held
 //     in registers, so K and V are fetched once per group. The K/V loads are
@@ -70,30 +69,26 @@ namespace pkv {
 namespace {
 
 
-// Workgroup shapes. A split workgroup has W waves of 4 token rows (16 lanes
-// per row); a sub-step reads 4 * W consecutive tokens of one strided block.
-//   * W = 8 (2 waves per SIMD, one workgroup per CU): 512-token windows in
-//     grids of at most one workgroup per CU (the batch-1 32K step: 28.8 us
-//     against 29.4 us with 4 waves and a ring of 8).
-//   * W = 4 (one wave per SIMD, several workgroups per CU): 512-token windows
-//     in grids of more workgroups than the device has CUs (16-sequence mixed
-//     batch 81.6 -> 74.4 us, 32 / 8-head dense control 29.1 -> 27.0 us
-//     against 8 waves) and every shorter window (per step 1K 10.04 -> 9.68
-//     us, 4K 11.35 -> 10.98, 16K 18.68 -> 18.55, a 2048-token sliding
-//     window 10.38 -> 10.1).
-constexpr int kMaxWaves = 8;
-constexpr int kMaxThreads = 64 * kMaxWaves;
+// Workgroup shape: 4 waves of 4 token rows (16 lanes per row), one wave per
+// SIMD; a sub-step reads 16 consecutive tokens of one strided block. Against
+// 8-wave workgroups (two waves per SIMD, rings of 6), measured per step: the
+// batch-1 32K call 28.9 -> 27.3 us, the 16-sequence mixed batch 81.6 -> 74.4
+// us, the 32 / 8-head dense control 29.1 -> 27.0 us, 1K 10.04 -> 9.68 us, 4K
+// 11.35 -> 10.98 us, a 2048-token sliding window 10.38 -> 10.1 us.
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kLanesPerRow = 16;
 constexpr int kRowsPerWave = 64 / kLanesPerRow;
-static_assert(kBlockTokens % (4 * kRowsPerWave) == 0, "sub-steps tile a strided block");
-// Register ring depth (steps in flight + 1); shallower where G * D leaves
-// fewer registers. Measured at G = 6, D = 256 with non-temporal loads:
-// depth 4 / 6 / 8 gave 29.85 / 29.61 / 29.93 us on a 32K step.
-constexpr int ring_depth(int D, int G) { return (D == 256 && G >= 7) ? 3 : 6; }
-// The 4-wave workgroups (several per CU) keep 3: on the mixed batch depth 3,
-// 4 and 6 gave 74.4, 74.4 and 75.8 us, on the dense control 27.0, 27.4 and
-// 28.2 us.
-constexpr int ring_depth(int D, int G, int waves) { return waves == 4 ? 3 : ring_depth(D, G); }
+static_assert(kBlockTokens % (kWaves * kRowsPerWave) == 0, "sub-steps tile a strided block");
+// Register ring depth (steps in flight + 1), a template argument of the
+// kernel. Measured with 4-wave workgroups, depths 2 / 3 / 4 / 5: the 32K step
+// 33.4 / 27.6 / 27.3 / 28.5 us (page 16: 33.8 / 28.1 / 27.5 / 28.5), the
+// mixed batch 81.8 / 74.1 / 74.4 / 75.3 us, the dense control 31.8 / 27.0 /
+// 27.3 / 27.9 us, 4K 11.5 / 11.0 / 10.9 / 11.2 us. Depth 4, and 3 for the
+// 512-token kernels launched on grids of more workgroups than the device
+// has CUs.
+constexpr int kRingOne = 4;    // grids of at most one workgroup per CU, and shorter windows
+constexpr int kRingMany = 3;   // 512-token windows on grids of several workgroups per CU
 constexpr float kMinit = -1.0e30f;             // floor of a row's max (finite: no inf - inf)
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -162,22 +157,20 @@ __device__ __forceinline__ float reduce_scatter16(const float (&x)[G], int col) 
 // 512-byte row (D = 256), lane col holds [k * 128 + col * 8, +8) of piece k.
 __device__ __forceinline__ int elem_d(int col, int e) { return (e / 8) * 128 + col * 8 + (e % 8); }
 
-template <int D, int G, int NBLK, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void decode_split_kernel(DecodeArgs a) {
-  constexpr int kWaves = WAVES;
-  constexpr int kThreads = 64 * kWaves;
+template <int D, int G, int NBLK, int RING>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   constexpr int kStep = kWaves * kRowsPerWave;          // tokens per workgroup sub-step
   constexpr int kSubSteps = NBLK * (kBlockTokens / kStep);
   constexpr int kEpl = D / kLanesPerRow;   // head-dim elements per lane: 16 or 8
   constexpr int kCq = kEpl / 8;            // 16-byte pieces of q per lane: 2 or 1
   constexpr int kCpl = kCq;                // 16-byte K/V loads per lane and row
   constexpr int kSteps = 2 * kSubSteps;    // K pass, then V pass
-  constexpr int kRing = ring_depth(D, G, kWaves);
+  constexpr int kRing = RING;
   constexpr int kWin = kSubSteps * kStep;  // tokens of the window
   constexpr int kEsz = 2;                  // bytes per cache element
   static_assert(kCpl >= 1 && kEpl % 8 == 0, "head_dim must be a multiple of 128");
   static_assert(G <= 8, "at most 8 query heads per KV head");
-  static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves");
+  static_assert(RING >= 2, "at least one step in flight");
   static_assert(kSubSteps >= 1 && kWin <= kMaxChunk, "window of at most kMaxChunk tokens");
 
   __shared__ int64_t tok_k[kWin];   // element offset of each window token's K row (a masked token: the q row)
@@ -467,40 +460,40 @@ __global__ __launch_bounds__(64 * WAVES) void decode_split_kernel(DecodeArgs a) 
   }
 }
 
-template <int D, int G, int NS, int WAVES>
+template <int D, int G, int NS, int RING>
 hipError_t launch_decode_k(const DecodeArgs& a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   dim3 grid(a.num_splits, a.hkv, a.num_seqs);
   if (e0 && e1)
-    hipExtLaunchKernelGGL((decode_split_kernel<D, G, NS, WAVES>), grid, dim3(64 * WAVES), 0, st, e0, e1, 0,
+    hipExtLaunchKernelGGL((decode_split_kernel<D, G, NS, RING>), grid, dim3(kThreads), 0, st, e0, e1, 0,
                           a);
   else
-    hipLaunchKernelGGL((decode_split_kernel<D, G, NS, WAVES>), grid, dim3(64 * WAVES), 0, st, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, G, NS, RING>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
-template <int D, int NS, int WAVES>
+template <int D, int NS, int RING>
 hipError_t launch_decode_d(const DecodeArgs& a, int group, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   switch (group) {
-    case 1: return launch_decode_k<D, 1, NS, WAVES>(a, st, e0, e1);
-    case 2: return launch_decode_k<D, 2, NS, WAVES>(a, st, e0, e1);
-    case 3: return launch_decode_k<D, 3, NS, WAVES>(a, st, e0, e1);
-    case 4: return launch_decode_k<D, 4, NS, WAVES>(a, st, e0, e1);
-    case 5: return launch_decode_k<D, 5, NS, WAVES>(a, st, e0, e1);
-    case 6: return launch_decode_k<D, 6, NS, WAVES>(a, st, e0, e1);
-    case 7: return launch_decode_k<D, 7, NS, WAVES>(a, st, e0, e1);
-    case 8: return launch_decode_k<D, 8, NS, WAVES>(a, st, e0, e1);
+    case 1: return launch_decode_k<D, 1, NS, RING>(a, st, e0, e1);
+    case 2: return launch_decode_k<D, 2, NS, RING>(a, st, e0, e1);
+    case 3: return launch_decode_k<D, 3, NS, RING>(a, st, e0, e1);
+    case 4: return launch_decode_k<D, 4, NS, RING>(a, st, e0, e1);
+    case 5: return launch_decode_k<D, 5, NS, RING>(a, st, e0, e1);
+    case 6: return launch_decode_k<D, 6, NS, RING>(a, st, e0, e1);
+    case 7: return launch_decode_k<D, 7, NS, RING>(a, st, e0, e1);
+    case 8: return launch_decode_k<D, 8, NS, RING>(a, st, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }
 
 // Launch the split kernel with a window of NS strided blocks of 32 tokens
-// (a.chunk <= NS * 32) for bf16 caches, with WAVES waves per workgroup.
-template <int NS, int WAVES = 8>
+// (a.chunk <= NS * 32) for bf16 caches, with a register ring of RING steps.
+template <int NS, int RING = kRingOne>
 hipError_t launch_decode_window(const DecodeArgs& a, int head_dim, int group, hipStream_t st, hipEvent_t e0,
                                 hipEvent_t e1) {
   if (a.chunk > NS * kBlockTokens || a.kv_fp8) return hipErrorInvalidValue;
-  if (head_dim == 256) return launch_decode_d<256, NS, WAVES>(a, group, st, e0, e1);
-  if (head_dim == 128) return launch_decode_d<128, NS, WAVES>(a, group, st, e0, e1);
+  if (head_dim == 256) return launch_decode_d<256, NS, RING>(a, group, st, e0, e1);
+  if (head_dim == 128) return launch_decode_d<128, NS, RING>(a, group, st, e0, e1);
   return hipErrorInvalidValue;
 }
 

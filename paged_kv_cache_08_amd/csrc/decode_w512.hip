@@ -1,4 +1,4 @@
-// Split kernels with a 512-token window (16 sub-steps of 32 tokens), bf16 caches.
+// Split kernels with a 512-token window (16 strided blocks of 32 tokens), bf16 caches.
 #include "decode_split.h"
 
 namespace pkv {

@@ -1,5 +1,5 @@
 // Split kernels with a 512-token window (16 strided blocks of 32 tokens),
-// bf16 caches, in 4-wave workgroups: the variant for grids of more
+// bf16 caches, with a ring of 3 steps: the variant for grids of more
 // workgroups than the device has CUs (several workgroups per CU).
 #include "decode_split.h"
 
@@ -7,7 +7,7 @@ namespace pkv {
 
 hipError_t launch_decode_split_w512_many(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
                                          hipEvent_t e0, hipEvent_t e1) {
-  return launch_decode_window<16, 4>(a, head_dim, group, st, e0, e1);
+  return launch_decode_window<16, kRingMany>(a, head_dim, group, st, e0, e1);
 }
 
 }  // namespace pkv

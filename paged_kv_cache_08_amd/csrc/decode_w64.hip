@@ -1,12 +1,11 @@
-// Split kernels with a 64-token window (2 strided blocks of 32 tokens), bf16 caches,
-// in 4-wave workgroups (several per CU).
+// Split kernels with a 64-token window (2 strided blocks of 32 tokens), bf16 caches.
 #include "decode_split.h"
 
 namespace pkv {
 
 hipError_t launch_decode_split_w64(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
                                    hipEvent_t e0, hipEvent_t e1) {
-  return launch_decode_window<2, 4>(a, head_dim, group, st, e0, e1);
+  return launch_decode_window<2>(a, head_dim, group, st, e0, e1);
 }
 
 }  // namespace pkv
