@@ -23,10 +23,14 @@
 //     each). All K and V loads of the wave go through a register ring and are
 //     issued ahead of their use; the wave never waits at a barrier before the
 //     epilogue.
+//   * K and V rows are loaded whole: 16 lanes read one row's 16-byte chunks
+//     with one instruction (A/B: loads of 16 rows x 64 bytes per instruction,
+//     read straight into the MFMA layout, were slower: 32K 20.6 against 19.6
+//     us, 16-sequence mixed batch 48.3 against 43.9 us).
 //   * The G query heads of the group are the rows of a 16-row MFMA tile (rows
-//     past G carry no weight). S^T = K Q^T per 16 tokens: the A operand is K (lane l:
-//     token l % 16, 8 head-dim elements of k slot l / 16), read straight from
-//     the cache with 16-byte loads; B is Q (lane l: head l % 16), held in
+//     past G carry no weight). S^T = K Q^T per 16 tokens: the A operand is K
+//     (lane l: token l % 16, 8 head-dim elements of k slot l / 16), read back
+//     from the wave's LDS tile; B is Q (lane l: head l % 16), held in
 //     registers. Since q.k sums over the head dim, the order in which head-dim
 //     elements meet the k slots only has to agree between K and Q: lane
 //     group g takes 16-byte chunks g, g + 4, g + 8, ... of a row.
@@ -35,11 +39,12 @@
 //     4 (l / 16) .. + 3 and 16 + 4 (l / 16) .. + 3 of the block), so P never
 //     leaves registers. It is split into bf16 hi + lo parts (two MFMAs per
 //     column block), so the bf16 operand costs about 2^-16 relative error.
-//   * V needs the token index along k: the wave writes the block's V rows to a
-//     private LDS tile (rows padded by 16 bytes) and reads them back
-//     transposed, ds_read_b64_tr_b8 for codes (lane i of a 16-lane group gets
-//     column i of the 8 rows its group points at) or ds_read_b64_tr_b16 for
-//     bf16 (4 rows per read, two reads).
+//   * The wave writes each block's K rows, later its V rows, to a private LDS
+//     tile (rows padded by 16 bytes). K comes back as 16-byte A operands. V
+//     needs the token index along k: it comes back transposed,
+//     ds_read_b64_tr_b8 for codes (lane i of a 16-lane group gets column i of
+//     the 8 rows its group points at) or ds_read_b64_tr_b16 for bf16 (4 rows
+//     per read, two reads).
 //   * Exact softmax per wave: a K pass over all the wave's blocks keeps every
 //     score (log2 units), the wave's maximum is taken once, and the V pass
 //     uses it, so O is never rescaled. Masked tokens (past the split, or
@@ -121,7 +126,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(DecodeArgs a
   constexpr int kEsz = FP8 ? 1 : 2;             // bytes per cache element
   constexpr int kRowB = D * kEsz;               // bytes per K or V row
   constexpr int kChunks = kRowB / 16;           // 16-byte chunks per row
-  constexpr int kKLd = kChunks / 4;             // K loads per lane per 16 tokens
+  constexpr int kKLd = kChunks / 4;             // 16-byte K chunks per lane per 16 tokens
   constexpr int kStepLd = kChunks / 2;          // loads per lane per step (32 tokens of K, or of V)
   constexpr int kKSteps = D / 32;               // k steps of one S^T tile
   constexpr int kDBlocks = D / 16;              // 16-column blocks of O
@@ -215,10 +220,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(DecodeArgs a
   const uint8_t* const vb8 = reinterpret_cast<const uint8_t*>(a.v);
   uint8_t* const my_vt = vt[wave];
 
-  // Step j < kBpw: K rows of the wave's block i = j (two 16-token halves,
-  // kKLd loads each: lane token ln of the half, chunks 4c + grp). Step
-  // kBpw + i: V rows of block i (kStepLd loads: flat 16-byte piece
-  // f = 64 c + lane is chunk f % kChunks of row f / kChunks).
+  // Step j < kBpw: K rows of the wave's block i = j; step kBpw + i: V rows
+  // of block i. kStepLd loads each: flat 16-byte piece f = 64 c + lane is
+  // chunk f % kChunks of row f / kChunks.
   uint4 ring[kRing][kStepLd];
   auto fetch = [&](int j, uint4 (&buf)[kStepLd]) __attribute__((always_inline)) {
     const int i = j < kBpw ? j : j - kBpw;
@@ -229,11 +233,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(DecodeArgs a
     const int sl = past ? 0 : slot0;
     if (j < kBpw) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int64_t off = past ? kstand : tok_k[sl + 16 * h + ln];
-        const uint8_t* p = kb8 + off * kEsz + 16 * grp;
-#pragma unroll
-        for (int c = 0; c < kKLd; ++c) buf[h * kKLd + c] = m_load16(p + 64 * c);
+      for (int c = 0; c < kStepLd; ++c) {
+        const int f = 64 * c + lane;
+        const int64_t off = past ? kstand : tok_k[sl + f / kChunks];
+        buf[c] = m_load16(kb8 + off * kEsz + 16 * (f % kChunks));
       }
     } else {
 #pragma unroll
@@ -252,12 +255,19 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(DecodeArgs a
   float m_w = kMMinit, l_w = 0.0f;   // head ln: the wave's max and sum of probabilities
 
   auto consume_k = [&](int i, const uint4 (&buf)[kStepLd]) __attribute__((always_inline)) {
+    // Whole K rows into the wave's tile, then each lane reads its token's
+    // 16-byte chunks 4 c + grp back as MFMA A operands.
+#pragma unroll
+    for (int c = 0; c < kStepLd; ++c) {
+      const int f = 64 * c + lane;
+      *reinterpret_cast<uint4*>(my_vt + (f / kChunks) * kPitch + 16 * (f % kChunks)) = buf[c];
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       mfloat4_t acc = mfloat4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int c = 0; c < kKLd; ++c) {
-        const uint4 x = buf[h * kKLd + c];
+        const uint4 x = *reinterpret_cast<const uint4*>(my_vt + (16 * h + ln) * kPitch + 16 * (4 * c + grp));
         if constexpr (FP8) {
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(m_as_bf16x8(m_fp8x8_to_bf16(x.x, x.y)),
                                                         m_as_bf16x8(qb[2 * c]), acc, 0, 0, 0);
