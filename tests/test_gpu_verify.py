@@ -31,6 +31,11 @@ def test_spec_verify_16_rows_32k_page784():
     (4, 32, 8, 128, 16, [777, 31]),
     (8, 16, 2, 256, 1, [200]),
     (16, 4, 4, 256, 784, [2500]),
+    # 65 to 84 rows per KV head: five or six row tiles of 16, the last one partly filled.
+    (13, 24, 4, 256, 784, [3000]),
+    (10, 16, 2, 256, 16, [900, 33]),
+    (11, 12, 2, 256, 7, [40, 11]),
+    (14, 24, 4, 256, 784, [1200]),
 ])
 def test_verify_shapes(ql, hq, hkv, d, bs, lens):
     log(f"case: verify q_len {ql}, {hq}/{hkv}/{d}, page {bs}, lengths {lens}")
