@@ -157,7 +157,7 @@ __device__ __forceinline__ float reduce_scatter16(const float (&x)[G], int col) 
 // 512-byte row (D = 256), lane col holds [k * 128 + col * 8, +8) of piece k.
 __device__ __forceinline__ int elem_d(int col, int e) { return (e / 8) * 128 + col * 8 + (e % 8); }
 
-template <int D, int G, int NBLK, int RING>
+template <int D, int G, int NBLK, int RING, bool WT>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   constexpr int kStep = kWaves * kRowsPerWave;          // tokens per workgroup sub-step
   constexpr int kSubSteps = NBLK * (kBlockTokens / kStep);
@@ -442,8 +442,23 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
       store_out4(a, out_row0 + 4 * i4, o);
     } else {
       const int64_t pr = (prow0 + h) * a.num_splits + s;
-      *reinterpret_cast<float4*>(a.part_acc + pr * D + d) = num;
-      if (d == 0) *reinterpret_cast<float2*>(a.part_ml + pr * 2) = make_float2(M, den);
+      if constexpr (WT) {
+        // Written through to memory (agent-scope relaxed stores): the merge
+        // kernel reads them from another XCD, and the kernel's end has no
+        // dirty partial lines left to write back.
+        uint64_t* const pa = reinterpret_cast<uint64_t*>(a.part_acc + pr * D + d);
+        __hip_atomic_store(pa, __builtin_bit_cast(uint64_t, make_float2(num.x, num.y)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(pa + 1, __builtin_bit_cast(uint64_t, make_float2(num.z, num.w)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0)
+          __hip_atomic_store(reinterpret_cast<uint64_t*>(a.part_ml + pr * 2),
+                             __builtin_bit_cast(uint64_t, make_float2(M, den)), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        *reinterpret_cast<float4*>(a.part_acc + pr * D + d) = num;
+        if (d == 0) *reinterpret_cast<float2*>(a.part_ml + pr * 2) = make_float2(M, den);
+      }
     }
   }
   // A single-split sequence's optional log-sum-exp, one thread per head, from
@@ -460,40 +475,41 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
-template <int D, int G, int NS, int RING>
+template <int D, int G, int NS, int RING, bool WT>
 hipError_t launch_decode_k(const DecodeArgs& a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   dim3 grid(a.num_splits, a.hkv, a.num_seqs);
   if (e0 && e1)
-    hipExtLaunchKernelGGL((decode_split_kernel<D, G, NS, RING>), grid, dim3(kThreads), 0, st, e0, e1, 0,
+    hipExtLaunchKernelGGL((decode_split_kernel<D, G, NS, RING, WT>), grid, dim3(kThreads), 0, st, e0, e1, 0,
                           a);
   else
-    hipLaunchKernelGGL((decode_split_kernel<D, G, NS, RING>), grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_split_kernel<D, G, NS, RING, WT>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
-template <int D, int NS, int RING>
+template <int D, int NS, int RING, bool WT>
 hipError_t launch_decode_d(const DecodeArgs& a, int group, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   switch (group) {
-    case 1: return launch_decode_k<D, 1, NS, RING>(a, st, e0, e1);
-    case 2: return launch_decode_k<D, 2, NS, RING>(a, st, e0, e1);
-    case 3: return launch_decode_k<D, 3, NS, RING>(a, st, e0, e1);
-    case 4: return launch_decode_k<D, 4, NS, RING>(a, st, e0, e1);
-    case 5: return launch_decode_k<D, 5, NS, RING>(a, st, e0, e1);
-    case 6: return launch_decode_k<D, 6, NS, RING>(a, st, e0, e1);
-    case 7: return launch_decode_k<D, 7, NS, RING>(a, st, e0, e1);
-    case 8: return launch_decode_k<D, 8, NS, RING>(a, st, e0, e1);
+    case 1: return launch_decode_k<D, 1, NS, RING, WT>(a, st, e0, e1);
+    case 2: return launch_decode_k<D, 2, NS, RING, WT>(a, st, e0, e1);
+    case 3: return launch_decode_k<D, 3, NS, RING, WT>(a, st, e0, e1);
+    case 4: return launch_decode_k<D, 4, NS, RING, WT>(a, st, e0, e1);
+    case 5: return launch_decode_k<D, 5, NS, RING, WT>(a, st, e0, e1);
+    case 6: return launch_decode_k<D, 6, NS, RING, WT>(a, st, e0, e1);
+    case 7: return launch_decode_k<D, 7, NS, RING, WT>(a, st, e0, e1);
+    case 8: return launch_decode_k<D, 8, NS, RING, WT>(a, st, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }
 
 // Launch the split kernel with a window of NS strided blocks of 32 tokens
-// (a.chunk <= NS * 32) for bf16 caches, with a register ring of RING steps.
-template <int NS, int RING = kRingOne>
+// (a.chunk <= NS * 32) for bf16 caches, with a register ring of RING steps;
+// WT: partials written through to memory.
+template <int NS, int RING = kRingOne, bool WT = false>
 hipError_t launch_decode_window(const DecodeArgs& a, int head_dim, int group, hipStream_t st, hipEvent_t e0,
                                 hipEvent_t e1) {
   if (a.chunk > NS * kBlockTokens || a.kv_fp8) return hipErrorInvalidValue;
-  if (head_dim == 256) return launch_decode_d<256, NS, RING>(a, group, st, e0, e1);
-  if (head_dim == 128) return launch_decode_d<128, NS, RING>(a, group, st, e0, e1);
+  if (head_dim == 256) return launch_decode_d<256, NS, RING, WT>(a, group, st, e0, e1);
+  if (head_dim == 128) return launch_decode_d<128, NS, RING, WT>(a, group, st, e0, e1);
   return hipErrorInvalidValue;
 }
 
