@@ -102,7 +102,7 @@ constexpr int kRowPad = D >= 256 ? 32 : 16;
 // or 8 divides it, and every XCD gets a balanced share. Token offsets come
 // from the block table in global memory, one lane per token, staged in LDS
 // two tiles ahead (the range can exceed what the LDS table holds).
-template <int D, bool FP8, bool PF>
+template <int D, bool FP8, bool PF, bool WT>
 __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a) {
   constexpr int kPitch = D * 2 + kRowPad<D>;         // LDS bytes per token row (padded)
   constexpr int kElems = FP8 ? 16 : 8;            // elements per 16-byte chunk of a cache row
@@ -414,33 +414,51 @@ __global__ __launch_bounds__(kVThreads, 1) void verify_split_kernel(DecodeArgs a
       if (ln == 0) store_lse(a, prow, mr, lr);
     } else {
       const int64_t pr = prow * a.num_splits + s;
+      if constexpr (WT) {   // written through to memory (agent-scope relaxed stores)
 #pragma unroll
-      for (int db = 0; db < kDBlocks; ++db) a.part_acc[pr * D + 16 * db + ln] = o[db][r];
-      if (ln == 0) {
-        a.part_ml[pr * 2] = mr;
-        a.part_ml[pr * 2 + 1] = lr;
+        for (int db = 0; db < kDBlocks; ++db)
+          __hip_atomic_store(a.part_acc + pr * D + 16 * db + ln, o[db][r], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        if (ln == 0)
+          __hip_atomic_store(reinterpret_cast<uint64_t*>(a.part_ml + pr * 2),
+                             __builtin_bit_cast(uint64_t, make_float2(mr, lr)), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+#pragma unroll
+        for (int db = 0; db < kDBlocks; ++db) a.part_acc[pr * D + 16 * db + ln] = o[db][r];
+        if (ln == 0) {
+          a.part_ml[pr * 2] = mr;
+          a.part_ml[pr * 2 + 1] = lr;
+        }
       }
     }
   }
 }
 
-template <int D, bool FP8, bool PF>
+template <int D, bool FP8, bool PF, bool WT>
 hipError_t launch_verify_k(const DecodeArgs& a, dim3 grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   if (e0 && e1)
-    hipExtLaunchKernelGGL((verify_split_kernel<D, FP8, PF>), grid, dim3(kVThreads), 0, st, e0, e1, 0, a);
+    hipExtLaunchKernelGGL((verify_split_kernel<D, FP8, PF, WT>), grid, dim3(kVThreads), 0, st, e0, e1, 0, a);
   else
-    hipLaunchKernelGGL((verify_split_kernel<D, FP8, PF>), grid, dim3(kVThreads), 0, st, a);
+    hipLaunchKernelGGL((verify_split_kernel<D, FP8, PF, WT>), grid, dim3(kVThreads), 0, st, a);
   return hipGetLastError();
 }
 
 template <bool PF>
 hipError_t launch_verify_any(const DecodeArgs& a, int head_dim, dim3 grid, hipStream_t st, hipEvent_t e0,
                              hipEvent_t e1) {
-  if (head_dim == 256)
-    return a.kv_fp8 ? launch_verify_k<256, true, PF>(a, grid, st, e0, e1)
-                    : launch_verify_k<256, false, PF>(a, grid, st, e0, e1);
-  return a.kv_fp8 ? launch_verify_k<128, true, PF>(a, grid, st, e0, e1)
-                  : launch_verify_k<128, false, PF>(a, grid, st, e0, e1);
+  // Split grids of at most one workgroup per CU (head_dim 256) write their
+  // partials through to memory: the whole grid ends at once and the merge
+  // reads them next. Larger grids keep ordinary stores.
+  if (head_dim == 256) {
+    if (!PF && !a.many_wg)
+      return a.kv_fp8 ? launch_verify_k<256, true, false, true>(a, grid, st, e0, e1)
+                      : launch_verify_k<256, false, false, true>(a, grid, st, e0, e1);
+    return a.kv_fp8 ? launch_verify_k<256, true, PF, false>(a, grid, st, e0, e1)
+                    : launch_verify_k<256, false, PF, false>(a, grid, st, e0, e1);
+  }
+  return a.kv_fp8 ? launch_verify_k<128, true, PF, false>(a, grid, st, e0, e1)
+                  : launch_verify_k<128, false, PF, false>(a, grid, st, e0, e1);
 }
 
 }  // namespace
