@@ -50,10 +50,11 @@ def parse():
                     choices=["hybrid", "single", "dense", "mixed", "verify", "varlen", "prefill"],
                     help="hybrid: one 24/4/256 sequence (page --block-size, --context tokens); single: batch 1, "
                          "page 16, 512 tokens, 32 of 64 pages; dense: 32/8/128, page 16; mixed: 16 sequences; "
-                         "verify: q_len 16; varlen: batched verify; prefill: one chunk of --chunk rows")
+                         "verify: --q-len causal rows; varlen: batched verify; prefill: one chunk of --chunk rows")
     ap.add_argument("--context", type=int, default=None,
                     help="tokens in the cache (default 32768; 8192 for prefill)")
     ap.add_argument("--chunk", type=int, default=4096, help="prefill: new query rows of the chunk")
+    ap.add_argument("--q-len", type=int, default=16, help="verify: query rows per sequence (1..16)")
     ap.add_argument("--block-size", type=int, default=784)
     ap.add_argument("--pools", type=int, default=16)
     ap.add_argument("--splits", type=int, default=0, help="force a split count (0 = planner)")
@@ -133,8 +134,8 @@ def make_workload(args):
                 "head_dim 256, page 784, contexts log-uniform 512..2048")
         return case, name, (qp, cu)
     else:
-        case = W.spec_verify(args.context, poison=False, **kv)
-        name = (f"speculative verify: batch 1, q_len 16 causal rows, 24 q / 4 KV heads, head_dim 256, "
+        case = W.spec_verify(args.context, q_len=args.q_len, poison=False, **kv)
+        name = (f"speculative verify: batch 1, q_len {args.q_len} causal rows, 24 q / 4 KV heads, head_dim 256, "
                 f"page 784, context {args.context}")
     return case, name, None
 
@@ -463,6 +464,7 @@ def measure(args, dev, hip, emit_cpu=True):
     from paged_kv_cache_08_amd.profiling import kernel_source_hash
     src_hash = kernel_source_hash()
     wl_key = (f"{args.workload}:{args.context}:{case.block_size}" + (f":q{args.chunk}" if prefill else "")
+              + (f":q{args.q_len}" if args.workload == "verify" and args.q_len != 16 else "")
               + (f":w{args.window}" if args.window else "")
               + (":fp8" if args.kv_dtype == "fp8" else ""))
     traffic = traffic_from_profiles(src_hash, wl_key)

@@ -274,8 +274,9 @@ int pkv_paged_prefill_attention(const pkv_decode_params* p,
  * with the split plan, e.g. "decode_valu d256 g6 q1 w512 + lse_merge
  * splits=64 chunk=512 B=784" (for prefill, w is the query positions per
  * workgroup). Split kernels: decode_valu (bf16, q_len 1),
- * decode_mfma (FP8, q_len 1), verify_mfma / varlen_mfma (several rows),
- * prefill_mfma. It is this library's run-time marker of the path that ran:
+ * decode_mfma (FP8, q_len 1), verify_rows / varlen_rows (several rows, at
+ * most 32 per KV head, splits of more than 256 tokens), verify_mfma /
+ * varlen_mfma (several rows, otherwise), prefill_mfma. It is this library's run-time marker of the path that ran:
  * "DCU page832 attention" §8 accepts a measurement only when the run's log
  * shows the decode marker of the kernel under test, and §11.3 asks to print
  * that marker and to check that no fallback ran instead. Copies at most

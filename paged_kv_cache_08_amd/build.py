@@ -15,7 +15,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
 # The 512-token split kernels are the slowest to compile: listed first.
-SOURCES = ["decode_w512.hip", "decode_w512_many.hip", "decode_mfma_fp8.hip", "decode_w256.hip",
+SOURCES = ["decode_w512.hip", "decode_w512_many.hip", "decode_mfma_fp8.hip", "decode_mfma_rows.hip", "decode_w256.hip",
            "verify_kernels.hip", "decode_w128.hip", "decode_w64.hip",
            "decode_kernels.hip", "api.hip"]
 ARCH = "gfx950"

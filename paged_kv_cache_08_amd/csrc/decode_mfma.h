@@ -119,7 +119,10 @@ __device__ __forceinline__ uint4 m_fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
                     fp8x2_to_bf16x2<true>(w1));
 }
 
-template <int D, int NBLK, bool FP8, int WAVES, int RING>
+// MR: several query rows per sequence (uniform q_len or varlen rows), at
+// most 32 rows (G x rows) per KV head in two 16-row tiles; each row keeps its
+// own causal (and window) bound.
+template <int D, int NBLK, bool FP8, int WAVES, int RING, bool MR = false>
 __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int kMWaves = WAVES;
   constexpr int kMThreads = 64 * WAVES;
@@ -135,15 +138,17 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(DecodeArgs a
   constexpr int kBpw = (NBLK + kMWaves - 1) / kMWaves;   // blocks per wave
   constexpr int kSteps = 2 * kBpw;              // K steps, then V steps
   constexpr int kRing = kSteps < RING ? kSteps : RING;   // ring depth: steps in flight + 1
+  constexpr int kNT = MR ? 2 : 1;               // 16-row MFMA tiles
+  constexpr int kMrgRows = MR ? 16 : kMMaxG;    // rows merged across the waves at a time
   static_assert(kChunks % 4 == 0 && kStepLd * 64 * 16 == kBlockTokens * kRowB, "rows split evenly");
   static_assert(kWin <= kMaxChunk, "window of at most kMaxChunk tokens");
 
   __shared__ int64_t tok_k[kWin];   // element offset of each window token's K row (masked: the NaN row)
   __shared__ int64_t tok_v[kWin];
   __shared__ __attribute__((aligned(16))) uint8_t vt[kMWaves][kBlockTokens * kPitch];
-  __shared__ __attribute__((aligned(16))) float mrg_acc[kMWaves][kMMaxG][D];
-  __shared__ __attribute__((aligned(16))) float mrg_m[kMMaxG][kMWaves];
-  __shared__ __attribute__((aligned(16))) float mrg_l[kMMaxG][kMWaves];
+  __shared__ __attribute__((aligned(16))) float mrg_acc[kMWaves][kMrgRows][D];
+  __shared__ __attribute__((aligned(16))) float mrg_m[kMrgRows][kMWaves];
+  __shared__ __attribute__((aligned(16))) float mrg_l[kMrgRows][kMWaves];
   static_assert(kMWaves % 4 == 0, "whole float4 rows of (max, sum)");
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -151,6 +156,22 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(DecodeArgs a
   const int grp = lane >> 4, ln = lane & 15;
   const int G = a.hq / a.hkv;
   const int64_t out_row0 = (int64_t(b) * a.hq + int64_t(g) * G) * D;   // q_len == 1
+  // MR: the sequence's query rows [row_base, row_base + n_rows); row f of the
+  // KV head is head f / n_rows at position f % n_rows.
+  int n_rows = 1, row_base = b;
+  if constexpr (MR) {
+    const QRows qr = seq_q_rows(a, b);
+    if (qr.n <= 0) {   // no rows, or inconsistent cu_seqlens_q
+      if (!qr.ok && s == 0 && g == 0 && tid == 0 && a.err) atomicOr(a.err, 2u);
+      return;
+    }
+    n_rows = qr.n;
+    row_base = qr.base;
+  }
+  const int R = G * n_rows;   // rows of this KV head
+  auto prow_of = [&](int f) {
+    return (int64_t(row_base) + f % n_rows) * a.hq + int64_t(g) * G + f / n_rows;
+  };
 
   // Stand-in rows as element offsets from the cache bases (all 16-byte aligned).
   const int64_t kstand =
@@ -174,12 +195,20 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(DecodeArgs a
       e_tok[r] = table_entry(a, b, t);
     }
   }
-  const SplitSpan sp = split_span_len(a, L_in, s, 1);
+  const SplitSpan sp = split_span_len(a, L_in, s, n_rows);
   flag_clamped(a, sp, s == 0 && g == 0 && tid == 0);
   if (sp.begin >= sp.L) {
     if (s == 0) {   // empty sequence: zeros (log-sum-exp -inf)
-      for (int i = tid; i < G * D; i += kMThreads) store_out(a, out_row0 + i, 0.0f);
-      if (tid < G) store_lse(a, out_row0 / D + tid, 0.0f, 0.0f);
+      if constexpr (MR) {
+        for (int i = tid; i < R * D; i += kMThreads) {
+          const int f = i / D, d = i - f * D;
+          store_out(a, prow_of(f) * D + d, 0.0f);
+          if (d == 0) store_lse(a, prow_of(f), 0.0f, 0.0f);
+        }
+      } else {
+        for (int i = tid; i < G * D; i += kMThreads) store_out(a, out_row0 + i, 0.0f);
+        if (tid < G) store_lse(a, out_row0 / D + tid, 0.0f, 0.0f);
+      }
     }
     return;
   }
@@ -208,11 +237,27 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(DecodeArgs a
   auto q_dim = [&](int kk) {
     return FP8 ? 16 * (4 * (kk / 2) + grp) + 8 * (kk % 2) : 8 * (4 * kk + grp);
   };
-  uint4 qb[kKSteps];
-  const int q_head = ln < G ? ln : 0;
+  uint4 qb[kNT][kKSteps];
+  bool rvalid[kNT];    // lane's row (ln of tile t) exists
+  int pos_row[kNT];    // MR: last token the row sees
 #pragma unroll
-  for (int kk = 0; kk < kKSteps; ++kk)
-    qb[kk] = *reinterpret_cast<const uint4*>(a.q + out_row0 + int64_t(q_head) * D + q_dim(kk));
+  for (int t = 0; t < kNT; ++t) {
+    int64_t q_off;
+    if constexpr (MR) {
+      const int f = 16 * t + ln;
+      rvalid[t] = f < R;
+      const int fv = rvalid[t] ? f : 0;
+      q_off = prow_of(fv) * D;
+      pos_row[t] = sp.L - n_rows + fv % n_rows;
+    } else {
+      rvalid[t] = ln < G;
+      q_off = out_row0 + int64_t(rvalid[t] ? ln : 0) * D;
+      pos_row[t] = 0;
+    }
+#pragma unroll
+    for (int kk = 0; kk < kKSteps; ++kk) qb[t][kk] = *reinterpret_cast<const uint4*>(a.q + q_off + q_dim(kk));
+  }
+  const bool win = MR && a.window > 0 && a.window < (1 << 30);
   __syncthreads();   // offsets staged
 
   const int n_blk = strided_blocks(sp, s);   // <= NBLK
@@ -248,11 +293,18 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(DecodeArgs a
     }
   };
 
-  mfloat4_t st[kBpw][2];   // scores (log2 units) of head ln, tokens 16 h + 4 grp + r of block i
-  mfloat4_t o[kDBlocks];
+  mfloat4_t st[kBpw][2][kNT];   // scores (log2 units) of row ln of tile t, tokens 16 h + 4 grp + r of block i
+  mfloat4_t o[kNT][kDBlocks];
 #pragma unroll
-  for (int db = 0; db < kDBlocks; ++db) o[db] = mfloat4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_w = kMMinit, l_w = 0.0f;   // head ln: the wave's max and sum of probabilities
+  for (int t = 0; t < kNT; ++t)
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db) o[t][db] = mfloat4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_w[kNT], l_w[kNT];   // row ln of tile t: the wave's max and sum of probabilities
+#pragma unroll
+  for (int t = 0; t < kNT; ++t) {
+    m_w[t] = kMMinit;
+    l_w[t] = 0.0f;
+  }
 
   auto consume_k = [&](int i, const uint4 (&buf)[kStepLd]) __attribute__((always_inline)) {
     // Whole K rows into the wave's tile, then each lane reads its token's
@@ -264,28 +316,44 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(DecodeArgs a
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      mfloat4_t acc = mfloat4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      mfloat4_t acc[kNT];
+#pragma unroll
+      for (int t = 0; t < kNT; ++t) acc[t] = mfloat4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int c = 0; c < kKLd; ++c) {
         const uint4 x = *reinterpret_cast<const uint4*>(my_vt + (16 * h + ln) * kPitch + 16 * (4 * c + grp));
         if constexpr (FP8) {
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(m_as_bf16x8(m_fp8x8_to_bf16(x.x, x.y)),
-                                                        m_as_bf16x8(qb[2 * c]), acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(m_as_bf16x8(m_fp8x8_to_bf16(x.z, x.w)),
-                                                        m_as_bf16x8(qb[2 * c + 1]), acc, 0, 0, 0);
+          const uint4 xa = m_fp8x8_to_bf16(x.x, x.y), xb = m_fp8x8_to_bf16(x.z, x.w);
+#pragma unroll
+          for (int t = 0; t < kNT; ++t) {
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(m_as_bf16x8(xa), m_as_bf16x8(qb[t][2 * c]), acc[t], 0, 0, 0);
+            acc[t] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(m_as_bf16x8(xb), m_as_bf16x8(qb[t][2 * c + 1]), acc[t], 0, 0, 0);
+          }
         } else {
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(m_as_bf16x8(x), m_as_bf16x8(qb[c]), acc, 0, 0, 0);
+#pragma unroll
+          for (int t = 0; t < kNT; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(m_as_bf16x8(x), m_as_bf16x8(qb[t][c]), acc[t], 0, 0, 0);
         }
       }
-      // A stand-in key gives NaN: the token does not count.
+      // A stand-in key gives NaN: the token does not count; with several
+      // rows, nor does a token past the row's position (or before its window).
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float sc = acc[r];
-        const float x = sc == sc ? sc * a.scale_log2 : -INFINITY;
-        acc[r] = x;
-        m_w = fmaxf(m_w, x);
+        int tok = 0;
+        if constexpr (MR) tok = strided_token(sp.lo, sp.nsplit, s, (wave + kMWaves * i) * kBlockTokens + 16 * h + 4 * grp + r);
+#pragma unroll
+        for (int t = 0; t < kNT; ++t) {
+          const float sc = acc[t][r];
+          bool vis = sc == sc;
+          if constexpr (MR) vis = vis && tok <= pos_row[t] && (!win || tok > pos_row[t] - a.window);
+          const float x = vis ? sc * a.scale_log2 : -INFINITY;
+          acc[t][r] = x;
+          m_w[t] = fmaxf(m_w[t], x);
+        }
       }
-      st[i][h] = acc;
+#pragma unroll
+      for (int t = 0; t < kNT; ++t) st[i][h][t] = acc[t];
     }
   };
 
@@ -298,23 +366,27 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(DecodeArgs a
       const int f = 64 * c + lane;
       *reinterpret_cast<uint4*>(my_vt + (f / kChunks) * kPitch + 16 * (f % kChunks)) = buf[c];
     }
-    // P = 2^(s - m) of head ln (zero past G), as hi + lo bf16 A operands; k
-    // slot grp holds tokens 4 grp .. + 3 and 16 + 4 grp .. + 3.
-    uint32_t hi[4], lo[4];
-    float ls = 0.0f;
+    // P = 2^(s - m) of row ln of each tile (zero past the rows), as hi + lo
+    // bf16 A operands; k slot grp holds tokens 4 grp .. + 3 and 16 + 4 grp .. + 3.
+    mbf16x8_t ph[kNT], pl[kNT];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int h = t >> 1, r0 = (t & 1) * 2;
-      const float p0 = ln < G ? fast_exp2(st[i][h][r0] - m_w) : 0.0f;
-      const float p1 = ln < G ? fast_exp2(st[i][h][r0 + 1] - m_w) : 0.0f;
-      ls += p0 + p1;
-      const uint32_t w = m_bf16_pair(p0, p1);
-      hi[t] = w;
-      lo[t] = m_bf16_pair(p0 - bf16_lo(w), p1 - bf16_hi(w));
+    for (int tt = 0; tt < kNT; ++tt) {
+      uint32_t hi[4], lo[4];
+      float ls = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int h = t >> 1, r0 = (t & 1) * 2;
+        const float p0 = rvalid[tt] ? fast_exp2(st[i][h][tt][r0] - m_w[tt]) : 0.0f;
+        const float p1 = rvalid[tt] ? fast_exp2(st[i][h][tt][r0 + 1] - m_w[tt]) : 0.0f;
+        ls += p0 + p1;
+        const uint32_t w = m_bf16_pair(p0, p1);
+        hi[t] = w;
+        lo[t] = m_bf16_pair(p0 - bf16_lo(w), p1 - bf16_hi(w));
+      }
+      l_w[tt] += ls;
+      ph[tt] = m_as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
+      pl[tt] = m_as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
     }
-    l_w += ls;
-    const mbf16x8_t ph = m_as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
-    const mbf16x8_t pl = m_as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
 #pragma unroll
     for (int db = 0; db < kDBlocks; ++db) {
       uint4 vu;
@@ -339,8 +411,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(DecodeArgs a
                         uint32_t(uint16_t(vb[0])) | (uint32_t(uint16_t(vb[1])) << 16),
                         uint32_t(uint16_t(vb[2])) | (uint32_t(uint16_t(vb[3])) << 16));
       }
-      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, m_as_bf16x8(vu), o[db], 0, 0, 0);
-      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, m_as_bf16x8(vu), o[db], 0, 0, 0);
+#pragma unroll
+      for (int tt = 0; tt < kNT; ++tt) {
+        o[tt][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph[tt], m_as_bf16x8(vu), o[tt][db], 0, 0, 0);
+        o[tt][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl[tt], m_as_bf16x8(vu), o[tt][db], 0, 0, 0);
+      }
     }
   };
 
@@ -365,9 +440,69 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(DecodeArgs a
       if constexpr (j < kBpw) consume_k(i, ring[j % kRing]);
       else consume_v(i, ring[j % kRing]);
     }
-    if constexpr (j == kBpw - 1) m_w = rows_max(m_w);   // head ln's max over the wave's tokens
+    if constexpr (j == kBpw - 1) {   // row ln's max over the wave's tokens
+#pragma unroll
+      for (int t = 0; t < kNT; ++t) m_w[t] = rows_max(m_w[t]);
+    }
   });
-  l_w = rows_sum(l_w);
+#pragma unroll
+  for (int t = 0; t < kNT; ++t) l_w[t] = rows_sum(l_w[t]);
+
+  if constexpr (MR) {
+    // One 16-row tile at a time: each wave publishes O of the tile's rows
+    // with its (max, sum) per row; after a barrier the workgroup rescales the
+    // waves to a common max, adds them in wave order and writes the rows'
+    // partials (or normalised outputs and log-sum-exp for a single split).
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) {
+      if (16 * t >= R) break;   // uniform
+#pragma unroll
+      for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mrg_acc[wave][4 * grp + r][16 * db + ln] = o[t][db][r];
+      if (grp == 0) {
+        mrg_m[ln][wave] = m_w[t];
+        mrg_l[ln][wave] = l_w[t];
+      }
+      __syncthreads();
+      for (int i4 = tid; i4 < 16 * D / 4; i4 += kMThreads) {
+        const int rl = (4 * i4) / D, d = 4 * i4 - rl * D;
+        const int f = 16 * t + rl;
+        if (f >= R) continue;
+        const float4 mv = *reinterpret_cast<const float4*>(&mrg_m[rl][0]);
+        const float4 lv = *reinterpret_cast<const float4*>(&mrg_l[rl][0]);
+        const float mw[4] = {mv.x, mv.y, mv.z, mv.w}, lw[4] = {lv.x, lv.y, lv.z, lv.w};
+        float M = mw[0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) M = fmaxf(M, mw[w]);
+        float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        float den = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float4 v4 = *reinterpret_cast<const float4*>(&mrg_acc[w][rl][d]);
+          const float fw = fast_exp2(mw[w] - M);
+          num.x = fmaf(fw, v4.x, num.x);
+          num.y = fmaf(fw, v4.y, num.y);
+          num.z = fmaf(fw, v4.z, num.z);
+          num.w = fmaf(fw, v4.w, num.w);
+          den = fmaf(fw, lw[w], den);
+        }
+        const int64_t prow = prow_of(f);
+        if (sp.nsplit == 1) {
+          const float4 o4 = den > 0.0f ? make_float4(num.x / den, num.y / den, num.z / den, num.w / den)
+                                       : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+          store_out4(a, prow * D + d, o4);
+          if (d == 0) store_lse(a, prow, M, den);
+        } else {
+          const int64_t pr = prow * a.num_splits + s;
+          *reinterpret_cast<float4*>(a.part_acc + pr * D + d) = num;
+          if (d == 0) *reinterpret_cast<float2*>(a.part_ml + pr * 2) = make_float2(M, den);
+        }
+      }
+      __syncthreads();   // the tile's LDS rows are read before the next tile's
+    }
+    return;
+  }
 
   // Publish O of the G heads (lane: column 16 db + ln of heads 4 grp + r)
   // with the wave's (max, sum) per head.
@@ -376,11 +511,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(DecodeArgs a
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = 4 * grp + r;
-      if (h < G) mrg_acc[wave][h][16 * db + ln] = o[db][r];
+      if (h < G) mrg_acc[wave][h][16 * db + ln] = o[0][db][r];
     }
   if (grp == 0 && ln < G) {
-    mrg_m[ln][wave] = m_w;
-    mrg_l[ln][wave] = l_w;
+    mrg_m[ln][wave] = m_w[0];
+    mrg_l[ln][wave] = l_w[0];
   }
   __syncthreads();
 
@@ -444,11 +579,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(DecodeArgs a
 // Launch the MFMA split kernel with a window of NBLK strided blocks of 32
 // tokens (a.chunk <= NBLK * 32), WAVES waves per workgroup and a register
 // ring of RING steps.
-template <int NBLK, bool FP8, int WAVES, int RING>
+template <int NBLK, bool FP8, int WAVES, int RING, bool MR = false>
 hipError_t launch_decode_mfma_window(const DecodeArgs& a, int head_dim, int group, hipStream_t st, hipEvent_t e0,
                                      hipEvent_t e1) {
-  if (a.chunk > NBLK * kBlockTokens || bool(a.kv_fp8) != FP8 || group < 1 || group > kMMaxG)
+  if (a.chunk > NBLK * kBlockTokens || bool(a.kv_fp8) != FP8 || group < 1)
     return hipErrorInvalidValue;
+  if (MR ? int64_t(group) * a.q_len > 32 : group > kMMaxG) return hipErrorInvalidValue;
   dim3 grid(a.num_splits, a.hkv, a.num_seqs);
   auto go = [&](auto kern) {
     if (e0 && e1)
@@ -457,8 +593,9 @@ hipError_t launch_decode_mfma_window(const DecodeArgs& a, int head_dim, int grou
       hipLaunchKernelGGL(kern, grid, dim3(64 * WAVES), 0, st, a);
     return hipGetLastError();
   };
-  if (head_dim == 256) return go(decode_mfma_kernel<256, NBLK, FP8, WAVES, RING>);
-  if (head_dim == 128) return go(decode_mfma_kernel<128, NBLK, FP8, WAVES, RING>);
+  if (head_dim == 256) return go(decode_mfma_kernel<256, NBLK, FP8, WAVES, RING, MR>);
+  if constexpr (!MR)   // several rows: head_dim 256 only
+    if (head_dim == 128) return go(decode_mfma_kernel<128, NBLK, FP8, WAVES, RING, MR>);
   return hipErrorInvalidValue;
 }
 

@@ -100,6 +100,10 @@ hipError_t launch_decode_split_w512(const DecodeArgs& a, int head_dim, int group
 // The single-query split kernel on MFMA for FP8 caches (decode_mfma_fp8.hip).
 hipError_t launch_decode_mfma_fp8(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
                                   hipEvent_t ev_start, hipEvent_t ev_stop);
+// Several query rows, at most 32 per KV head, on the single-query MFMA
+// kernel's structure (decode_mfma_rows.hip).
+hipError_t launch_decode_mfma_rows(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
+                                   hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_verify_split(const DecodeArgs& a, int head_dim, int group, hipStream_t st,
                                hipEvent_t ev_start, hipEvent_t ev_stop);
 // Prefill: blocks of a.pf_rows query positions per workgroup, each over its
@@ -113,5 +117,6 @@ hipError_t launch_debug_ranges(const DecodeArgs& a, int32_t* ranges, hipStream_t
 hipError_t launch_debug_token_splits(const DecodeArgs& a, int max_seq_len, int32_t* slots, hipStream_t st);
 bool decode_supported(int head_dim, int group);
 bool verify_supported(int head_dim, int group, int q_len);
+bool rows_mfma_supported(int head_dim, int group, int q_len);
 
 }  // namespace pkv

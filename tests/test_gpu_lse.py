@@ -72,6 +72,8 @@ DECODE_CASES = [
                                        boost_frac=0.05), {}, ("verify_mfma", "lse_merge")),
     ("verify q4, one split", lambda: W.make_case(1209, [200, 4], q_len=4, block_size=7, interleave=True),
      {"num_splits": 1}, ("verify_mfma", "splits=1")),
+    ("verify q2, splits", lambda: W.make_case(1211, [20000, 20, 0], q_len=2, block_size=784, interleave=True,
+                                              boost_frac=0.05), {}, ("verify_rows", "lse_merge")),
 ]
 
 
