@@ -477,9 +477,11 @@ def measure(args, dev, hip, emit_cpu=True):
         else:
             cpu = cpu_baseline(case, varlen, args.window, kv_bytes, args.cpu_seconds)
 
-    kernel = ("verify_split_kernel (prefill blocks)" if prefill else
-              "verify_split_kernel" if (case.q_len > 1 or varlen is not None) else
-              "decode_mfma_kernel" if args.kv_dtype == "fp8" else "decode_split_kernel")
+    # The split kernel of the variant that ran (the library's run-time marker).
+    kernel = ("verify_split_kernel (prefill blocks)" if variant.startswith("prefill_mfma") else
+              "verify_split_kernel" if variant.startswith(("verify_mfma", "varlen_mfma")) else
+              "decode_mfma_kernel" if variant.startswith(("decode_mfma", "verify_rows", "varlen_rows")) else
+              "decode_split_kernel")
     timing_src = ("HIP events that the library records on its stream right around the split kernel "
                   "(hipExtLaunchKernel), averaged over the K launches after the timed regions")
     if prefill:   # a dense contraction: priced against the bf16 MFMA peak
