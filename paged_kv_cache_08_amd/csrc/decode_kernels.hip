@@ -44,6 +44,7 @@ __global__ __launch_bounds__(64 * MW) void lse_merge_kernel(DecodeArgs a) {
   constexpr int kPerWave = 64 / MW;   // accumulator loads in flight per thread per pass
   constexpr int kPass = MW * kPerWave;
   constexpr bool kAhead = AHEAD;
+  static_assert(MW == 4 || MW == 8, "the final sum over the waves is written out for 4 or 8 waves");
   __shared__ float sm_w[MW][kMergeSplitsLds];
   __shared__ float part[MW][64];
   const int cb = blockIdx.z, h = blockIdx.y;
@@ -151,6 +152,7 @@ __global__ __launch_bounds__(64 * MW) void lse_merge_kernel(DecodeArgs a) {
 template <int MW, bool AHEAD>
 __global__ __launch_bounds__(64 * MW) void lse_merge_row_kernel(DecodeArgs a) {
   constexpr int D = 256;
+  static_assert(MW == 4, "the final sum over the waves is written out for 4 waves");
   constexpr int kPerWave = 64 / MW;   // accumulator loads in flight per thread per pass
   constexpr int kPass = MW * kPerWave;
   __shared__ float sm_w[MW][kMergeSplitsLds];
@@ -238,15 +240,10 @@ __global__ __launch_bounds__(64 * MW) void lse_merge_row_kernel(DecodeArgs a) {
   part[wave][lane] = num;
   __syncthreads();
   if (wave == 0) {
-    float4 t = part[0][lane];
-#pragma unroll
-    for (int w = 1; w < MW; ++w) {
-      const float4 u = part[w][lane];
-      t.x += u.x;
-      t.y += u.y;
-      t.z += u.z;
-      t.w += u.w;
-    }
+    // Pairwise over the 4 waves, as lse_merge_kernel<D, 4> adds them.
+    const float4 u0 = part[0][lane], u1 = part[1][lane], u2 = part[2][lane], u3 = part[3][lane];
+    const float4 t = make_float4((u0.x + u1.x) + (u2.x + u3.x), (u0.y + u1.y) + (u2.y + u3.y),
+                                 (u0.z + u1.z) + (u2.z + u3.z), (u0.w + u1.w) + (u2.w + u3.w));
     const float4 o = M == -INFINITY ? make_float4(0.f, 0.f, 0.f, 0.f)
                                     : make_float4(t.x * inv_den, t.y * inv_den, t.z * inv_den, t.w * inv_den);
     store_out4(a, prow * D + 4 * lane, o);

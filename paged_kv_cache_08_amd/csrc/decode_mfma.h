@@ -55,6 +55,13 @@
 //     the waves to a common max and adds them in a fixed order, and writes the
 //     split's partial (max, sum, accumulator), or the normalised output when
 //     the sequence has a single split.
+//   * MR (several query rows per sequence; "Qwen3.8 auf MI350P betreiben",
+//     Lektion 3: one K/V walk for all verify rows, each with its own causal
+//     bound): up to 32 rows per KV head (G heads x n rows, head-major: row f
+//     is head f / n at position f % n) in two 16-row tiles that share every
+//     K and V operand read. A score counts only when its token is at most the
+//     row's position L - n + i (and within the row's window); the epilogue
+//     merges the waves one tile at a time. bf16 and FP8 caches, head_dim 256.
 // Every reduction order depends only on logical token indices and the split
 // plan, never on block_size or physical page ids.
 #pragma once
@@ -156,22 +163,6 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(DecodeArgs a
   const int grp = lane >> 4, ln = lane & 15;
   const int G = a.hq / a.hkv;
   const int64_t out_row0 = (int64_t(b) * a.hq + int64_t(g) * G) * D;   // q_len == 1
-  // MR: the sequence's query rows [row_base, row_base + n_rows); row f of the
-  // KV head is head f / n_rows at position f % n_rows.
-  int n_rows = 1, row_base = b;
-  if constexpr (MR) {
-    const QRows qr = seq_q_rows(a, b);
-    if (qr.n <= 0) {   // no rows, or inconsistent cu_seqlens_q
-      if (!qr.ok && s == 0 && g == 0 && tid == 0 && a.err) atomicOr(a.err, 2u);
-      return;
-    }
-    n_rows = qr.n;
-    row_base = qr.base;
-  }
-  const int R = G * n_rows;   // rows of this KV head
-  auto prow_of = [&](int f) {
-    return (int64_t(row_base) + f % n_rows) * a.hq + int64_t(g) * G + f / n_rows;
-  };
 
   // Stand-in rows as element offsets from the cache bases (all 16-byte aligned).
   const int64_t kstand =
@@ -195,6 +186,23 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_mfma_kernel(DecodeArgs a
       e_tok[r] = table_entry(a, b, t);
     }
   }
+  // MR: the sequence's query rows [row_base, row_base + n_rows); row f of the
+  // KV head is head f / n_rows at position f % n_rows. (Read after the loads
+  // above are issued: they do not depend on the rows.)
+  int n_rows = 1, row_base = b;
+  if constexpr (MR) {
+    const QRows qr = seq_q_rows(a, b);
+    if (qr.n <= 0) {   // no rows, or inconsistent cu_seqlens_q
+      if (!qr.ok && s == 0 && g == 0 && tid == 0 && a.err) atomicOr(a.err, 2u);
+      return;
+    }
+    n_rows = qr.n;
+    row_base = qr.base;
+  }
+  const int R = G * n_rows;   // rows of this KV head
+  auto prow_of = [&](int f) {
+    return (int64_t(row_base) + f % n_rows) * a.hq + int64_t(g) * G + f / n_rows;
+  };
   const SplitSpan sp = split_span_len(a, L_in, s, n_rows);
   flag_clamped(a, sp, s == 0 && g == 0 && tid == 0);
   if (sp.begin >= sp.L) {
