@@ -148,3 +148,24 @@ def test_varlen_rows_invalid_table_entry_is_skipped_and_flagged():
     drop[32:48] = True
     assert_matches_oracle(got[3:], ref_without_tokens(case, 1, q[3:], [0, 1, 2, 3], drop),
                           "sequence 1 without page 2")
+
+
+@pytest.mark.parametrize("hq,hkv,ql,ctx", [(32, 4, 4, 20000), (32, 2, 2, 40000), (8, 4, 16, 20000)])
+def test_rows_32_rows_per_kv_head(hq, hkv, ql, ctx):
+    # G x rows = 32: both 16-row tiles full (8 heads x 4 rows, 16 x 2, 2 x 16);
+    # contexts long enough for splits of more than 256 tokens.
+    log(f"case: verify {hq}/{hkv}/256, q_len {ql}, context {ctx}, page 784")
+    case = W.make_case(1320 + hq + ql, [ctx], q_len=ql, num_q_heads=hq, num_kv_heads=hkv, block_size=784,
+                       boost_frac=0.05)
+    got = run_gpu(case)
+    ran("verify_rows")
+    assert_matches_oracle(got, oracle_out(case), f"rows {hq}/{hkv} q{ql}")
+
+
+@pytest.mark.parametrize("splits", [40, 60])
+def test_rows_forced_splits(splits):
+    log(f"case: verify q_len 3, lengths [20000, 700, 3], {splits} forced splits")
+    case = W.make_case(1330 + splits, [20000, 700, 3], q_len=3, block_size=784, interleave=True, boost_frac=0.05)
+    got = run_gpu(case, num_splits=splits)
+    ran("verify_rows")
+    assert_matches_oracle(got, oracle_out(case), f"rows S={splits}")
