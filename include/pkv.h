@@ -64,8 +64,10 @@ typedef struct pkv_decode_params {
   int32_t q_len;             /* new query rows per sequence, 1..16 (1 = decode; prefill: up to 2^24) */
   int32_t num_q_heads;       /* Hq */
   int32_t num_kv_heads;      /* Hkv; Hq % Hkv == 0; (Hq / Hkv) * q_len <= 128. q_len 1 with
-                                Hq / Hkv <= 8 runs on the decode kernel, everything else on
-                                the MFMA kernel */
+                                Hq / Hkv <= 8 runs on the decode kernel; several rows with
+                                (Hq / Hkv) * q_len <= 32, D 256 and splits of more than 256
+                                tokens on the few-row MFMA kernel; everything else on the
+                                tiled MFMA kernel */
   int32_t head_dim;          /* D: 128 or 256 */
   int32_t block_size;        /* tokens per physical page, any value >= 1 (e.g. 16, 784, 832) */
   int32_t max_pages_per_seq; /* row stride of block_table, in entries */
