@@ -574,7 +574,7 @@ def ladder(args, dev, hip):
         rec, ok = measure(a, dev, hip, emit_cpu=False)
         ok_all &= ok
         row = {"ladder_row": True, "context": ctx, "block_size": bs, "us_per_step": rec["us_per_step"],
-               "gbs": rec["value"], "pct_hbm_peak": rec["pct_hbm_peak"],
+               "graph_us_per_step": rec["graph_us_per_step"], "gbs": rec["value"], "pct_hbm_peak": rec["pct_hbm_peak"],
                "kernel_us_avg": rec["roofline"]["kernel_us_avg"], "variant": rec["config"]["variant"],
                "parity_ok": ok, "max_abs_err": rec["parity"].get("max_abs_err"),
                "input_sha256": rec["identity"]["input_sha256"]}
@@ -584,6 +584,14 @@ def ladder(args, dev, hip):
     L = np.array([f[0] for f in fit], dtype=np.float64)
     t = np.array([f[1] for f in fit], dtype=np.float64)
     b, a0 = np.polyfit(L, t, 1)
+    # The same fit over HIP-graph replays of the same steps (no host launch
+    # cost per call), when the rows measured them.
+    fit_graph = None
+    tg = [r["graph_us_per_step"] for r in rows if r["block_size"] == 784]
+    if all(x is not None for x in tg):
+        bg, ag = np.polyfit(L, np.array(tg, dtype=np.float64), 1)
+        fit_graph = {"a_us": round(float(ag), 3), "b_ns_per_token": round(float(bg) * 1e3, 4),
+                     "points": [[int(x), float(y)] for x, y in zip(L, tg)]}
     t32 = {r["block_size"]: r["us_per_step"] for r in rows if r["context"] == 32768}
     spread = (max(t32.values()) - min(t32.values())) / min(t32.values())
     summary = {
@@ -592,6 +600,7 @@ def ladder(args, dev, hip):
                 "points": [[int(x), float(y)] for x, y in fit],
                 "b_16_layers_us_per_token": round(16 * float(b), 6),
                 "pages_context_us_per_token": {"hybrid_dual_radeon": 4.840, "dense_8b_dual_radeon": 0.118}},
+        "fit_graph_replay": fit_graph,
         "page_sizes_at_32k_us": {str(k): v for k, v in t32.items()},
         "page_size_spread_pct": round(100.0 * spread, 2),
         "no_cliff": bool(spread <= 0.05),
