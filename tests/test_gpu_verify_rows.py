@@ -169,3 +169,18 @@ def test_rows_forced_splits(splits):
     got = run_gpu(case, num_splits=splits)
     ran("verify_rows")
     assert_matches_oracle(got, oracle_out(case), f"rows S={splits}")
+
+
+def test_varlen_rows_window_fp8():
+    # Eight sequences, so that the plan over their windows gives splits of more than 256 tokens.
+    lens = [20000, 9000, 3000, 2500, 15000, 4000, 7000, 2100]
+    rows = [2, 4, 1, 3, 0, 4, 2, 1]
+    log(f"case: varlen rows {rows}, FP8 K/V, window 2048, lengths {lens}, page 784")
+    case = W.make_case(1340, lens, q_len=4, block_size=784, interleave=True, boost_frac=0.05,
+                       kv_dtype="fp8_e4m3")
+    q, cu = W.pack_varlen(case, rows)
+    got, _ = run_gpu_varlen(case, q, cu, window=2048)
+    ran("varlen_rows")
+    ref = O.paged_attention_varlen_ref(q, cu, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                                       case.block_size, case.scale, window=2048, **H.oracle_kv(case))
+    assert_matches_oracle(got, ref, "varlen rows window fp8")
